@@ -1,0 +1,243 @@
+"""fp64 definitions of the ops (test infrastructure; see the package docstring).
+
+Notation: T tokens, d hidden, D head_dim, F ffn, V vocabulary, H lm-head input width.
+Inputs may be numpy arrays or CPU torch tensors of any float dtype; they are widened
+to float64 exactly before any arithmetic.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    if hasattr(a, "detach"):  # torch tensor: widen exactly (bf16/fp32 -> fp64)
+        import torch
+        return a.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def _i64(a) -> np.ndarray:
+    if hasattr(a, "detach"):
+        return a.detach().to("cpu").numpy().astype(np.int64)
+    return np.asarray(a, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm — [FastLLM] 三 技术架构, "Transformer Block 结构" (normalization:
+# LayerNorm / RMSNorm) and 训练配置示例 (normalization type rms_norm, epsilon 1e-5);
+# [LF] "当前已实现的 kernels" (npu_fused_rmsnorm); [HFK] "Liger" (fused RMSNorm).
+# Reading: eps inside the root; y = x * r * w with no (1+w) offset, no bias and no
+# mean subtraction.
+# ---------------------------------------------------------------------------
+def rmsnorm_fwd(x, w, eps):
+    """y[t,j] = x[t,j] * r[t] * w[j],  r[t] = 1/sqrt(mean_j x[t,j]^2 + eps).
+
+    Returns (y [T,d], rstd [T])."""
+    x = _f64(x)
+    w = _f64(w)
+    ms = np.mean(x * x, axis=-1)
+    rstd = 1.0 / np.sqrt(ms + eps)
+    y = x * rstd[..., None] * w
+    return y, rstd
+
+
+def rmsnorm_bwd(dy, x, w, eps):
+    """Gradients of y = rmsnorm_fwd(x, w, eps) for upstream dy.
+
+    With g = w*dy and r as above, differentiating y_j = x_j r w_j, where
+    dr/dx_k = -r^3 x_k / d, gives
+        dx[t,k] = r g_k - r^3 x_k * (1/d) sum_j g_j x_j
+        dw[j]   = sum_t dy[t,j] x[t,j] r[t]
+    Returns (dx [T,d], dw [d])."""
+    dy = _f64(dy)
+    x = _f64(x)
+    w = _f64(w)
+    d = x.shape[-1]
+    _, r = rmsnorm_fwd(x, w, eps)
+    g = dy * w
+    c = np.sum(g * x, axis=-1) / d
+    dx = r[..., None] * g - (r ** 3 * c)[..., None] * x
+    dw = np.sum(dy * x * r[..., None], axis=tuple(range(x.ndim - 1)))
+    return dx, dw
+
+
+# ---------------------------------------------------------------------------
+# RoPE — [FastLLM] 三 技术架构, "Transformer Block 结构" (attention + RoPE) and
+# 训练配置示例 (rotary type default, theta; heads / head_groups / head_size);
+# [LF] npu_fused_rope; [HFK] "Liger" (rope).
+# Readings: half-split pairing (element i pairs with i + D/2, the layout of the
+# HF-format checkpoints these pages load); frequencies theta^(-2i/D) over the full
+# head dim; no scaling variants; the angle pos*freq is formed in fp64.
+# ---------------------------------------------------------------------------
+def rope_angles(pos, D, theta):
+    """a[t,i] = pos[t] * theta^(-2i/D) for i in [0, D/2)."""
+    pos = _i64(pos).astype(np.float64)
+    i = np.arange(D // 2, dtype=np.float64)
+    freq = np.power(float(theta), -2.0 * i / D)
+    return pos[:, None] * freq[None, :]
+
+
+def _rotate(x, a):
+    # x [T, heads, D], a [T, D/2]: rotate each pair (x_i, x_{i+D/2}) by angle a_i.
+    D = x.shape[-1]
+    h = D // 2
+    c = np.cos(a)[:, None, :]
+    s = np.sin(a)[:, None, :]
+    lo, hi = x[..., :h], x[..., h:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def rope_fwd(q, k, pos, theta):
+    """Rotate every Q head and every K head of token t by the angles of pos[t].
+
+    q [T,Hq,D], k [T,Hkv,D] -> (q', k').  GQA grouping does not enter the rotation."""
+    q = _f64(q)
+    k = _f64(k)
+    a = rope_angles(pos, q.shape[-1], theta)
+    return _rotate(q, a), _rotate(k, a)
+
+
+def rope_bwd(dq, dk, pos, theta):
+    """Transpose of rope_fwd: rotate the gradients by the negated angles."""
+    dq = _f64(dq)
+    dk = _f64(dk)
+    a = rope_angles(pos, dq.shape[-1], theta)
+    return _rotate(dq, -a), _rotate(dk, -a)
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU — [FastLLM] 三 技术架构, "Transformer Block 结构" (gated MLP with SiLU) and
+# 训练配置示例 (mlp gated: true, activation: silu); [LF] npu_fused_swiglu;
+# [HFK] "Liger" (swiglu).  Reading: h = silu(gate) * up, silu(x) = x * sigmoid(x).
+# ---------------------------------------------------------------------------
+def _sigmoid(x):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def silu(x):
+    x = _f64(x)
+    return x * _sigmoid(x)
+
+
+def swiglu_fwd(gate, up):
+    """h = gate * sigmoid(gate) * up, elementwise."""
+    g = _f64(gate)
+    u = _f64(up)
+    return g * _sigmoid(g) * u
+
+
+def swiglu_bwd(dh, gate, up):
+    """d/dg [g s(g) u] = u (s + g s (1 - s)) = u s (1 + g (1 - s));  d/du = g s(g).
+
+    Returns (dgate, dup)."""
+    dh = _f64(dh)
+    g = _f64(gate)
+    u = _f64(up)
+    s = _sigmoid(g)
+    dg = dh * u * s * (1.0 + g * (1.0 - s))
+    du = dh * g * s
+    return dg, du
+
+
+# ---------------------------------------------------------------------------
+# Cross-entropy with ignore_index and z-loss — [FastLLM] 三 技术架构, "损失函数体系"
+# (Cross-Entropy; Z-Loss "prevents over-confidence"), and the Triton kernel list of
+# 整体框架结构 (entropy_loss.py, z_loss.py); [HFK] "Liger" (cross_entropy).
+# Readings: mean over non-ignored rows (N = number of valid targets); z-loss is
+# c_z * mean_valid(lse^2) added to the loss; a target outside [0, V) that is not
+# ignore_index is counted as bad and treated as ignored; N = 0 gives loss 0 and
+# all-zero gradients; ignored rows get exactly zero gradient.
+# ---------------------------------------------------------------------------
+def _valid_mask(tg, V, ignore_index):
+    inr = (tg >= 0) & (tg < V)
+    valid = inr & (tg != ignore_index)
+    bad = (~inr) & (tg != ignore_index)
+    return valid, bad
+
+
+def xent_rows(z, tg, valid, n_valid, z_loss, dloss):
+    """Per-row pieces for rows z [R,V] (fp64) with targets tg [R] and valid mask.
+
+    logsumexp in the plain two-pass form: m = max_j z_j, lse = m + log sum_j exp(z_j - m).
+      loss_t = lse - z[t, y_t] + c_z * lse^2
+      dz[t]  = (dloss / N) * (softmax(z_t) * (1 + 2 c_z lse) - onehot(y_t))
+    Rows with valid=False get loss 0 (excluded) and dz = 0.
+    Returns (loss_rows [R], zterm_rows [R], lse [R], dz [R,V])."""
+    R, V = z.shape
+    m = np.max(z, axis=1)
+    lse = m + np.log(np.sum(np.exp(z - m[:, None]), axis=1))
+    yt = np.where(valid, tg, 0)
+    zy = z[np.arange(R), yt]
+    zterm = z_loss * lse * lse
+    loss_rows = np.where(valid, lse - zy + zterm, 0.0)
+    zterm = np.where(valid, zterm, 0.0)
+    dz = np.zeros_like(z)
+    if n_valid > 0:
+        scale = dloss / n_valid
+        p = np.exp(z - lse[:, None])
+        g = p * (1.0 + 2.0 * z_loss * lse)[:, None]
+        g[np.arange(R), yt] -= 1.0
+        dz = np.where(valid[:, None], scale * g, 0.0)
+    return loss_rows, zterm, lse, dz
+
+
+def xent_fwd_bwd(logits, targets, ignore_index=-100, z_loss=0.0, dloss=1.0):
+    """Mean cross-entropy (+ z-loss) over valid rows, and its logit gradient.
+
+    Returns dict(loss, z_loss, n_valid, n_bad, lse [T], dlogits [T,V])."""
+    z = _f64(logits)
+    tg = _i64(targets)
+    T, V = z.shape
+    valid, bad = _valid_mask(tg, V, ignore_index)
+    n = int(valid.sum())
+    loss_rows, zterm, lse, dz = xent_rows(z, tg, valid, n, z_loss, dloss)
+    loss = float(loss_rows.sum() / n) if n else 0.0
+    zl = float(zterm.sum() / n) if n else 0.0
+    return dict(loss=loss, z_loss=zl, n_valid=n, n_bad=int(bad.sum()), lse=lse,
+                dlogits=dz)
+
+
+# ---------------------------------------------------------------------------
+# Fused linear cross-entropy — [HFK] "Liger" (fused_linear_cross_entropy: the lm-head
+# projection and the loss fused so that large vocabularies stay feasible in memory).
+# Definition: the composition xent(H W^T) with dH = dZ W and dW = dZ^T H, where dZ
+# is the cross-entropy gradient above.  Reading: no bias, softcap or temperature.
+# The optional row chunking below only bounds host memory; rows are independent, so
+# it does not change the result beyond fp64 summation order.
+# ---------------------------------------------------------------------------
+def flce_fwd_bwd(hidden, weight, targets, ignore_index=-100, z_loss=0.0, dloss=1.0,
+                 chunk=None, dh_rows=None, dw_rows=None):
+    """Returns dict(loss, z_loss, n_valid, n_bad, dhidden, dweight).
+
+    dh_rows / dw_rows: optional index arrays; when given only those rows of dH
+    ([len, H]) and of dW ([len, H]) are formed (for sampled checks at large sizes)."""
+    Hm = _f64(hidden)
+    W = _f64(weight)
+    tg = _i64(targets)
+    T = Hm.shape[0]
+    V = W.shape[0]
+    valid, bad = _valid_mask(tg, V, ignore_index)
+    n = int(valid.sum())
+    chunk = T if chunk is None else int(chunk)
+    want_dh = np.arange(T) if dh_rows is None else np.asarray(dh_rows)
+    want_dw = None if dw_rows is None else np.asarray(dw_rows)
+    dH = np.zeros((len(want_dh), Hm.shape[1]))
+    dW = np.zeros((V if want_dw is None else len(want_dw), Hm.shape[1]))
+    loss_sum = 0.0
+    z_sum = 0.0
+    pos_in_dh = {int(r): i for i, r in enumerate(want_dh)}
+    for c0 in range(0, T, chunk):
+        c1 = min(T, c0 + chunk)
+        Z = Hm[c0:c1] @ W.T
+        lr, zt, _, dZ = xent_rows(Z, tg[c0:c1], valid[c0:c1], n, z_loss, dloss)
+        loss_sum += lr.sum()
+        z_sum += zt.sum()
+        rows = [r for r in range(c0, c1) if r in pos_in_dh]
+        if rows:
+            dH[[pos_in_dh[r] for r in rows]] = dZ[np.array(rows) - c0] @ W
+        dZ_sel = dZ if want_dw is None else dZ[:, want_dw]
+        dW += dZ_sel.T @ Hm[c0:c1]
+    return dict(loss=float(loss_sum / n) if n else 0.0,
+                z_loss=float(z_sum / n) if n else 0.0,
+                n_valid=n, n_bad=int(bad.sum()), dhidden=dH, dweight=dW)
