@@ -1,0 +1,437 @@
+// RMSNorm forward and backward for gfx950.
+//
+// Definition ("Fast-LLM: 高效大语言模型训练框架", 三 技术架构: Transformer Block 结构
+// lists RMSNorm as a block normalisation; 训练配置示例 gives type rms_norm with an
+// epsilon; the Liger section of "Kernels（自定义内核）" fuses it into one kernel):
+//   r[t] = 1/sqrt(mean_j x[t,j]^2 + eps),  y[t,j] = x[t,j] r[t] w[j]
+//   dx = r (w*dy) - r^3 x mean_j(w_j dy_j x_j),  dw[j] = sum_t dy[t,j] x[t,j] r[t]
+//
+// Fast path (16-byte aligned rows whose length is a multiple of the vector): the
+// forward gives one wave64 per row and holds the row in registers between the sum of
+// squares and the write, so x is read from HBM exactly once.  The backward gives each
+// row RW waves (RW grows with d so a lane holds at most 16 elements per operand); every
+// lane owns a fixed set of columns and accumulates their dw contribution in registers
+// across all the rows its workgroup visits.  The waves of a workgroup are folded
+// through LDS in a fixed order into one fp32 partial row per workgroup (at most 256
+// workgroups, so the partials stay a few MB), and a second small kernel sums the
+// partial rows in a fixed order.  Any other shape takes a workgroup-per-row path that
+// reads the row twice (the second read from L2).
+#include <type_traits>
+
+#include "fo_common.hpp"
+
+namespace fo {
+namespace {
+
+constexpr int kFwdWaves = 4;     // rows (waves) per workgroup, forward
+constexpr int kBwdWaves = 16;    // waves per workgroup, backward
+constexpr int kMaxPartials = 256;  // dw partial rows (workgroups of the backward)
+constexpr int kGenericThreads = 256;
+
+// ----------------------------------------------------------------- forward, fast
+template <typename T, int NV>
+__global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
+    int64_t T_, int nvec, int d, const T* __restrict__ x, int64_t ldx,
+    const T* __restrict__ w, float eps, T* y, int64_t ldy, float* __restrict__ rstd) {
+  constexpr int VEC = Vec<T>::N;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * kFwdWaves + (threadIdx.x / kWave);
+  if (row >= T_) return;
+  const T* xr = x + row * ldx;
+  Pack<T> xv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = lane + i * kWave;
+    if (v < nvec) xv[i] = load_pack(xr + (int64_t)v * VEC);
+    else xv[i].raw = u32x4{0, 0, 0, 0};
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      const float f = to_f32(xv[i].v[j]);
+      ss = fmaf(f, f, ss);
+    }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  T* yr = y + row * ldy;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = lane + i * kWave;
+    if (v < nvec) {
+      const Pack<T> wv = load_pack_cached(w + (int64_t)v * VEC);
+      Pack<T> o;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) o.v[j] = from_f32<T>(to_f32(xv[i].v[j]) * r * to_f32(wv.v[j]));
+      store_pack(yr + (int64_t)v * VEC, o);
+    }
+  }
+  if (rstd != nullptr && lane == 0) rstd[row] = r;
+}
+
+// Workgroup sum with a fixed combination order; every thread gets the total.
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) sh[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) t += sh[i];
+  return t;
+}
+
+// -------------------------------------------------------------- forward, generic
+template <typename T>
+__global__ __launch_bounds__(kGenericThreads) void rmsnorm_fwd_block(
+    int64_t T_, int64_t d, const T* x, int64_t ldx, const T* __restrict__ w, float eps,
+    T* y, int64_t ldy, float* __restrict__ rstd) {
+  __shared__ float sh[kGenericThreads / kWave];
+  const int64_t row = blockIdx.x;
+  const T* xr = x + row * ldx;
+  float ss = 0.f;
+  for (int64_t j = threadIdx.x; j < d; j += kGenericThreads) {
+    const float f = to_f32(xr[j]);
+    ss = fmaf(f, f, ss);
+  }
+  ss = block_sum<kGenericThreads>(ss, sh);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  T* yr = y + row * ldy;
+  for (int64_t j = threadIdx.x; j < d; j += kGenericThreads)
+    yr[j] = from_f32<T>(to_f32(xr[j]) * r * to_f32(w[j]));
+  if (rstd != nullptr && threadIdx.x == 0) rstd[row] = r;
+}
+
+// ----------------------------------------------------------------- backward, fast
+// A workgroup of kBwdWaves waves works on kBwdWaves/RW rows at a time, RW waves per
+// row; lane (w, l) of a row owns the vectors (w*64 + l) + i*RW*64, i < NV, and keeps
+// its columns' dw contribution in registers across all rows the workgroup visits.
+// The per-row dot products are combined across the RW waves through LDS (every wave
+// runs the same number of row rounds, so the barriers match).  At the end the waves'
+// column partials are folded through LDS in a fixed order into one fp32 partial row
+// per workgroup: partial[blockIdx.x, :].
+template <typename T, int NV, int RW>
+__global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
+    int64_t T_, int nvec, int d, const T* dy, int64_t lddy, const T* x, int64_t ldx,
+    const T* __restrict__ w, const float* __restrict__ rstd, float eps, T* dx,
+    int64_t lddx, float* __restrict__ partial) {
+  constexpr int VEC = Vec<T>::N;
+  constexpr int RG = kBwdWaves / RW;  // rows in flight per workgroup
+  extern __shared__ float fold[];     // [d]
+  __shared__ float xdot[kBwdWaves], xss[kBwdWaves];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int rg = wave / RW, wr = wave % RW;
+  const int vbase = wr * kWave + lane;
+  Pack<T> wv[NV];
+  float acc[NV][VEC];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = vbase + i * RW * kWave;
+    if (v < nvec) wv[i] = load_pack_cached(w + (int64_t)v * VEC);
+    else wv[i].raw = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) acc[i][j] = 0.f;
+  }
+  const float inv_d = 1.0f / (float)d;
+  const int64_t stride = (int64_t)gridDim.x * RG;
+  const int64_t rounds = ceil_div(T_ - (int64_t)blockIdx.x * RG, stride);
+  for (int64_t rd = 0; rd < rounds; ++rd) {
+    const int64_t row = (int64_t)blockIdx.x * RG + rg + rd * stride;
+    const bool live = row < T_;
+    Pack<T> gv[NV], xv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = vbase + i * RW * kWave;
+      if (live && v < nvec) {
+        gv[i] = load_pack(dy + row * lddy + (int64_t)v * VEC);
+        xv[i] = load_pack(x + row * ldx + (int64_t)v * VEC);
+      } else {
+        gv[i].raw = u32x4{0, 0, 0, 0};
+        xv[i].raw = u32x4{0, 0, 0, 0};
+      }
+    }
+    float dot = 0.f, ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        const float xf = to_f32(xv[i].v[j]);
+        dot = fmaf(to_f32(wv[i].v[j]) * to_f32(gv[i].v[j]), xf, dot);
+        ss = fmaf(xf, xf, ss);
+      }
+    dot = wave_sum(dot);
+    ss = wave_sum(ss);
+    if constexpr (RW > 1) {
+      if (lane == 0) { xdot[wave] = dot; xss[wave] = ss; }
+      __syncthreads();
+      dot = 0.f;
+      ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < RW; ++k) { dot += xdot[rg * RW + k]; ss += xss[rg * RW + k]; }
+      __syncthreads();  // slots are rewritten next round
+    }
+    if (!live) continue;
+    const float r = rstd != nullptr ? rstd[row] : 1.0f / sqrtf(ss * inv_d + eps);
+    const float k = r * r * r * (dot * inv_d);
+    T* dxr = dx + row * lddx;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = vbase + i * RW * kWave;
+      if (v < nvec) {
+        Pack<T> o;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+          const float xf = to_f32(xv[i].v[j]);
+          const float gf = to_f32(gv[i].v[j]);
+          o.v[j] = from_f32<T>(r * (to_f32(wv[i].v[j]) * gf) - k * xf);
+          acc[i][j] = fmaf(gf * xf, r, acc[i][j]);
+        }
+        store_pack(dxr + (int64_t)v * VEC, o);
+      }
+    }
+  }
+  // fold the row groups' column partials in order 0,1,2,... (RW waves of a group own
+  // disjoint columns, so they write their slots in the same step)
+  for (int s = 0; s < RG; ++s) {
+    if (rg == s) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int v = vbase + i * RW * kWave;
+        if (v < nvec) {
+#pragma unroll
+          for (int j = 0; j < VEC; ++j) {
+            float* p = &fold[v * VEC + j];
+            *p = (s == 0) ? acc[i][j] : (*p + acc[i][j]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  float* out = partial + (int64_t)blockIdx.x * d;
+  for (int j = threadIdx.x; j < d; j += blockDim.x) out[j] = fold[j];
+}
+
+// -------------------------------------------------------------- backward, generic
+// One workgroup per row: dx, and r[t] saved for the dw pass.
+template <typename T>
+__global__ __launch_bounds__(kGenericThreads) void rmsnorm_bwd_dx_block(
+    int64_t T_, int64_t d, const T* dy, int64_t lddy, const T* x, int64_t ldx,
+    const T* __restrict__ w, const float* __restrict__ rstd, float eps, T* dx,
+    int64_t lddx, float* __restrict__ r_out) {
+  __shared__ float sh[kGenericThreads / kWave];
+  const int64_t row = blockIdx.x;
+  const T* dyr = dy + row * lddy;
+  const T* xr = x + row * ldx;
+  float dot = 0.f, ss = 0.f;
+  for (int64_t j = threadIdx.x; j < d; j += kGenericThreads) {
+    const float xf = to_f32(xr[j]);
+    dot = fmaf(to_f32(w[j]) * to_f32(dyr[j]), xf, dot);
+    ss = fmaf(xf, xf, ss);
+  }
+  dot = block_sum<kGenericThreads>(dot, sh);
+  float r;
+  if (rstd != nullptr) {
+    r = rstd[row];
+  } else {
+    ss = block_sum<kGenericThreads>(ss, sh);
+    r = 1.0f / sqrtf(ss / (float)d + eps);
+  }
+  const float k = r * r * r * (dot / (float)d);
+  T* dxr = dx + row * lddx;
+  // dx may alias dy: every element is read (above) by the thread that writes it, and
+  // the block_sum barriers separate all reads of the dot product from these writes.
+  for (int64_t j = threadIdx.x; j < d; j += kGenericThreads) {
+    const float xf = to_f32(xr[j]);
+    dxr[j] = from_f32<T>(r * (to_f32(w[j]) * to_f32(dyr[j])) - k * xf);
+  }
+  if (threadIdx.x == 0) r_out[row] = r;
+}
+
+// dw partial rows of the generic path: workgroup (g, column block) sums its row range.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_dw_partial_block(
+    int64_t T_, int64_t d, const T* dy, int64_t lddy, const T* x, int64_t ldx,
+    const float* __restrict__ r, int64_t rows_per_group, float* __restrict__ partial) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t g = blockIdx.y;
+  if (j >= d) return;
+  const int64_t r0 = g * rows_per_group;
+  const int64_t r1 = (r0 + rows_per_group < T_) ? r0 + rows_per_group : T_;
+  float acc = 0.f;
+  for (int64_t t = r0; t < r1; ++t)
+    acc = fmaf(to_f32(dy[t * lddy + j]) * to_f32(x[t * ldx + j]), r[t], acc);
+  partial[g * d + j] = acc;
+}
+
+// dw[j] = sum_g partial[g, j] in the order g = 0,1,...: 4 row phases per column, then
+// the 4 phase sums in order.
+__global__ __launch_bounds__(256) void rmsnorm_dw_reduce(int64_t G, int64_t d,
+                                                        const float* __restrict__ partial,
+                                                        float* __restrict__ dw) {
+  __shared__ float sh[4][64];
+  const int c = threadIdx.x & 63;
+  const int ph = threadIdx.x >> 6;
+  const int64_t j = (int64_t)blockIdx.x * 64 + c;
+  const int64_t per = (G + 3) / 4;
+  const int64_t g0 = ph * per;
+  const int64_t g1 = (g0 + per < G) ? g0 + per : G;
+  float acc = 0.f;
+  if (j < d)
+    for (int64_t g = g0; g < g1; ++g) acc += partial[g * d + j];
+  sh[ph][c] = acc;
+  __syncthreads();
+  if (ph == 0 && j < d) dw[j] = ((sh[0][c] + sh[1][c]) + sh[2][c]) + sh[3][c];
+}
+
+__global__ void fill_f32(float* p, int64_t n, float v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// ------------------------------------------------------------------ dispatch
+template <typename T>
+bool vector_ok(int64_t d, const void* a, int64_t lda, const void* b, int64_t ldb,
+               const void* c, int64_t ldc, const void* w) {
+  constexpr int VEC = Vec<T>::N;
+  return d % VEC == 0 && lda % VEC == 0 && ldb % VEC == 0 && ldc % VEC == 0 &&
+         aligned16(a) && aligned16(b) && aligned16(c) && aligned16(w) &&
+         d <= 16 * kWave * VEC;
+}
+
+template <typename T>
+int nv_for(int64_t d) {
+  const int64_t nvec = d / Vec<T>::N;
+  const int64_t per = ceil_div(nvec, kWave);
+  return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
+}
+
+template <typename T>
+int fwd_impl(int64_t T_, int64_t d, const void* x, int64_t ldx, const void* w, float eps,
+             void* y, int64_t ldy, float* rstd, hipStream_t st) {
+  const T* xp = static_cast<const T*>(x);
+  const T* wp = static_cast<const T*>(w);
+  T* yp = static_cast<T*>(y);
+  if (vector_ok<T>(d, x, ldx, y, ldy, x, ldx, w)) {
+    const int nvec = (int)(d / Vec<T>::N);
+    const dim3 grid((unsigned)ceil_div(T_, kFwdWaves));
+    const dim3 block(kFwdWaves * kWave);
+    switch (nv_for<T>(d)) {
+      case 1: rmsnorm_fwd_wave<T, 1><<<grid, block, 0, st>>>(T_, nvec, (int)d, xp, ldx, wp, eps, yp, ldy, rstd); break;
+      case 2: rmsnorm_fwd_wave<T, 2><<<grid, block, 0, st>>>(T_, nvec, (int)d, xp, ldx, wp, eps, yp, ldy, rstd); break;
+      case 4: rmsnorm_fwd_wave<T, 4><<<grid, block, 0, st>>>(T_, nvec, (int)d, xp, ldx, wp, eps, yp, ldy, rstd); break;
+      case 8: rmsnorm_fwd_wave<T, 8><<<grid, block, 0, st>>>(T_, nvec, (int)d, xp, ldx, wp, eps, yp, ldy, rstd); break;
+      default: rmsnorm_fwd_wave<T, 16><<<grid, block, 0, st>>>(T_, nvec, (int)d, xp, ldx, wp, eps, yp, ldy, rstd); break;
+    }
+  } else {
+    rmsnorm_fwd_block<T><<<dim3((unsigned)T_), dim3(kGenericThreads), 0, st>>>(
+        T_, d, xp, ldx, wp, eps, yp, ldy, rstd);
+  }
+  return launch_status();
+}
+
+// Upper bound of the dw partial rows of either backward path (workspace sizing).
+int64_t bwd_groups(int64_t T_) { return T_ < kMaxPartials ? T_ : kMaxPartials; }
+
+template <typename T>
+int bwd_impl(int64_t T_, int64_t d, const void* dy, int64_t lddy, const void* x,
+             int64_t ldx, const void* w, const float* rstd, float eps, void* dx,
+             int64_t lddx, float* dw, void* ws, hipStream_t st) {
+  const T* dyp = static_cast<const T*>(dy);
+  const T* xp = static_cast<const T*>(x);
+  const T* wp = static_cast<const T*>(w);
+  T* dxp = static_cast<T*>(dx);
+  float* partial = static_cast<float*>(ws);
+  int64_t G;
+  if (vector_ok<T>(d, dy, lddy, x, ldx, dx, lddx, w)) {
+    const int nvec = (int)(d / Vec<T>::N);
+    // fewest waves per row that keep each lane at <= 16 elements per operand
+    constexpr int kMaxNV = 16 / Vec<T>::N;
+    int rw = 1;
+    while (rw < kBwdWaves && ceil_div(nvec, (int64_t)rw * kWave) > kMaxNV) rw *= 2;
+    const int64_t per = ceil_div(nvec, (int64_t)rw * kWave);
+    const int nv = per <= 1 ? 1 : per <= 2 ? 2 : 4;
+    const int64_t rows_in_flight = kBwdWaves / rw;
+    G = ceil_div(T_, rows_in_flight);
+    if (G > kMaxPartials) G = kMaxPartials;
+    const dim3 grid((unsigned)G), block(kBwdWaves * kWave);
+    const size_t lds = (size_t)d * sizeof(float);
+    auto go = [&](auto nv_c, auto rw_c) {
+      rmsnorm_bwd_wave<T, decltype(nv_c)::value, decltype(rw_c)::value><<<grid, block, lds, st>>>(
+          T_, nvec, (int)d, dyp, lddy, xp, ldx, wp, rstd, eps, dxp, lddx, partial);
+    };
+    auto go_rw = [&](auto rw_c) {
+      if (nv == 1) go(std::integral_constant<int, 1>{}, rw_c);
+      else if (nv == 2 || kMaxNV == 2) go(std::integral_constant<int, 2>{}, rw_c);
+      else go(std::integral_constant<int, kMaxNV>{}, rw_c);
+    };
+    switch (rw) {
+      case 1: go_rw(std::integral_constant<int, 1>{}); break;
+      case 2: go_rw(std::integral_constant<int, 2>{}); break;
+      case 4: go_rw(std::integral_constant<int, 4>{}); break;
+      case 8: go_rw(std::integral_constant<int, 8>{}); break;
+      default: go_rw(std::integral_constant<int, 16>{}); break;
+    }
+  } else {
+    // r[t] after the partials in the workspace
+    G = bwd_groups(T_);
+    float* r = partial + align_up((size_t)G * (size_t)d, 64);
+    rmsnorm_bwd_dx_block<T><<<dim3((unsigned)T_), dim3(kGenericThreads), 0, st>>>(
+        T_, d, dyp, lddy, xp, ldx, wp, rstd, eps, dxp, lddx, r);
+    const int64_t rows_per_group = ceil_div(T_, G);
+    G = ceil_div(T_, rows_per_group);
+    rmsnorm_dw_partial_block<T><<<dim3((unsigned)ceil_div(d, 256), (unsigned)G), dim3(256), 0, st>>>(
+        T_, d, dyp, lddy, xp, ldx, r, rows_per_group, partial);
+  }
+  rmsnorm_dw_reduce<<<dim3((unsigned)ceil_div(d, 64)), dim3(256), 0, st>>>(G, d, partial, dw);
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace fo
+
+using namespace fo;
+
+extern "C" size_t fo_rmsnorm_bwd_workspace(int64_t T, int64_t d) {
+  if (T < 0 || d < 1) return 0;
+  const int64_t G = T > 0 ? bwd_groups(T) : 1;
+  return (align_up((size_t)G * (size_t)d, 64) + (size_t)T) * sizeof(float) + 256;
+}
+
+extern "C" int fo_rmsnorm_fwd(int dtype, int64_t T, int64_t d, const void* x, int64_t ldx,
+                              const void* w, float eps, void* y, int64_t ldy, float* rstd,
+                              void* stream) {
+  if (dtype != FO_F32 && dtype != FO_BF16) return FO_ERR_DTYPE;
+  if (T < 0 || d < 1 || T > INT32_MAX) return FO_ERR_SHAPE;
+  if (ldx < d || ldy < d) return FO_ERR_STRIDE;
+  if (T == 0) return FO_OK;
+  if (!x || !w || !y) return FO_ERR_NULL;
+  hipStream_t st = as_stream(stream);
+  return dtype == FO_F32 ? fwd_impl<float>(T, d, x, ldx, w, eps, y, ldy, rstd, st)
+                         : fwd_impl<bf16>(T, d, x, ldx, w, eps, y, ldy, rstd, st);
+}
+
+extern "C" int fo_rmsnorm_bwd(int dtype, int64_t T, int64_t d, const void* dy, int64_t lddy,
+                              const void* x, int64_t ldx, const void* w, const float* rstd,
+                              float eps, void* dx, int64_t lddx, float* dw, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (dtype != FO_F32 && dtype != FO_BF16) return FO_ERR_DTYPE;
+  if (T < 0 || d < 1 || T > INT32_MAX) return FO_ERR_SHAPE;
+  if (lddy < d || ldx < d || lddx < d) return FO_ERR_STRIDE;
+  if (!dw) return FO_ERR_NULL;
+  hipStream_t st = as_stream(stream);
+  if (T == 0) {
+    fill_f32<<<dim3((unsigned)ceil_div(d, 256)), dim3(256), 0, st>>>(dw, d, 0.f);
+    return launch_status();
+  }
+  if (!dy || !x || !w || !dx) return FO_ERR_NULL;
+  if (!ws || ws_bytes < fo_rmsnorm_bwd_workspace(T, d)) return FO_ERR_WORKSPACE;
+  return dtype == FO_F32
+             ? bwd_impl<float>(T, d, dy, lddy, x, ldx, w, rstd, eps, dx, lddx, dw, ws, st)
+             : bwd_impl<bf16>(T, d, dy, lddy, x, ldx, w, rstd, eps, dx, lddx, dw, ws, st);
+}

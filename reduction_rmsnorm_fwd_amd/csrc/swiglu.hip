@@ -1,0 +1,228 @@
+// SwiGLU forward and backward for gfx950.
+//
+// Definition ("Fast-LLM: 高效大语言模型训练框架", 三 技术架构: gated MLP with SiLU in the
+// Transformer Block 结构 table, and mlp gated: true / activation: silu in 训练配置示例;
+// fused op in "LLaMA-Factory Kernels 系统" and in the Liger section of
+// "Kernels（自定义内核）"):
+//   h = silu(g) u,  silu(g) = g s(g),  s(g) = 1/(1+exp(-g))
+//   dg = dh u s (1 + g (1 - s)),  du = dh g s
+// Purely elementwise and HBM-bound: each element of every operand is read once and
+// each output written once with 16-byte vector accesses, the gate and up reads of an
+// element issued together so one pass produces the output.  Rows may have their own
+// strides (halves of a [T, 2F] tensor work); fully contiguous operands are walked as
+// one flat row.
+#include "fo_common.hpp"
+
+namespace fo {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 2;  // vectors per thread per operand
+
+__device__ __forceinline__ float sigmoid_f(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+// Index space: rows x nvr vectors (VEC elements each); nb column blocks per row.
+template <typename T, int VEC>
+__global__ __launch_bounds__(kThreads) void swiglu_fwd_k(int64_t nvr, int64_t nb,
+                                                         const T* g, int64_t ldg, const T* u,
+                                                         int64_t ldu, T* h, int64_t ldh) {
+  const int64_t row = blockIdx.x / nb;
+  const int64_t cb = blockIdx.x - row * nb;
+  const T* gr = g + row * ldg;
+  const T* ur = u + row * ldu;
+  T* hr = h + row * ldh;
+  const int64_t v0 = cb * (kThreads * kUnroll) + threadIdx.x;
+  if constexpr (VEC > 1) {
+    Pack<T> gv[kUnroll], uv[kUnroll];
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const int64_t v = v0 + i * kThreads;
+      if (v < nvr) {
+        gv[i] = load_pack(gr + v * VEC);
+        uv[i] = load_pack(ur + v * VEC);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const int64_t v = v0 + i * kThreads;
+      if (v < nvr) {
+        Pack<T> o;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+          const float gf = to_f32(gv[i].v[j]);
+          o.v[j] = from_f32<T>(gf * sigmoid_f(gf) * to_f32(uv[i].v[j]));
+        }
+        store_pack(hr + v * VEC, o);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const int64_t v = v0 + i * kThreads;
+      if (v < nvr) {
+        const float gf = to_f32(gr[v]);
+        hr[v] = from_f32<T>(gf * sigmoid_f(gf) * to_f32(ur[v]));
+      }
+    }
+  }
+}
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t nvr, int64_t nb,
+                                                         const T* dh, int64_t lddh,
+                                                         const T* g, int64_t ldg, const T* u,
+                                                         int64_t ldu, T* dg, int64_t lddg,
+                                                         T* du, int64_t lddu) {
+  const int64_t row = blockIdx.x / nb;
+  const int64_t cb = blockIdx.x - row * nb;
+  const T* dhr = dh + row * lddh;
+  const T* gr = g + row * ldg;
+  const T* ur = u + row * ldu;
+  T* dgr = dg + row * lddg;
+  T* dur = du + row * lddu;
+  const int64_t v0 = cb * (kThreads * kUnroll) + threadIdx.x;
+  if constexpr (VEC > 1) {
+    Pack<T> hv[kUnroll], gv[kUnroll], uv[kUnroll];
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const int64_t v = v0 + i * kThreads;
+      if (v < nvr) {
+        hv[i] = load_pack(dhr + v * VEC);
+        gv[i] = load_pack(gr + v * VEC);
+        uv[i] = load_pack(ur + v * VEC);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const int64_t v = v0 + i * kThreads;
+      if (v < nvr) {
+        Pack<T> og, ou;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+          const float gf = to_f32(gv[i].v[j]);
+          const float uf = to_f32(uv[i].v[j]);
+          const float hf = to_f32(hv[i].v[j]);
+          const float s = sigmoid_f(gf);
+          og.v[j] = from_f32<T>(hf * uf * s * fmaf(gf, 1.0f - s, 1.0f));
+          ou.v[j] = from_f32<T>(hf * gf * s);
+        }
+        store_pack(dgr + v * VEC, og);
+        store_pack(dur + v * VEC, ou);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const int64_t v = v0 + i * kThreads;
+      if (v < nvr) {
+        const float gf = to_f32(gr[v]), uf = to_f32(ur[v]), hf = to_f32(dhr[v]);
+        const float s = sigmoid_f(gf);
+        dgr[v] = from_f32<T>(hf * uf * s * fmaf(gf, 1.0f - s, 1.0f));
+        dur[v] = from_f32<T>(hf * gf * s);
+      }
+    }
+  }
+}
+
+// Launch geometry: rows x vectors-per-row; one flat row when every operand is a
+// single contiguous [T*F] run.
+struct Geo {
+  int64_t rows, nvr, nb;
+  bool vec;
+};
+
+template <typename T>
+Geo plan(int64_t T_, int64_t F, int n, const void* const* ptr, const int64_t* ld) {
+  constexpr int VEC = Vec<T>::N;
+  bool contiguous = true, aligned = true, ld_ok = true;
+  for (int i = 0; i < n; ++i) {
+    contiguous = contiguous && ld[i] == F;
+    aligned = aligned && aligned16(ptr[i]);
+    ld_ok = ld_ok && ld[i] % VEC == 0;
+  }
+  Geo g;
+  const int64_t per_row = contiguous ? T_ * F : F;
+  g.rows = contiguous ? 1 : T_;
+  g.vec = aligned && per_row % VEC == 0 && (contiguous || ld_ok);
+  g.nvr = g.vec ? per_row / VEC : per_row;
+  g.nb = ceil_div(g.nvr, kThreads * kUnroll);
+  return g;
+}
+
+template <typename T>
+int fwd_impl(int64_t T_, int64_t F, const void* g, int64_t ldg, const void* u, int64_t ldu,
+             void* h, int64_t ldh, hipStream_t st) {
+  const void* p[3] = {g, u, h};
+  const int64_t l[3] = {ldg, ldu, ldh};
+  const Geo geo = plan<T>(T_, F, 3, p, l);
+  const dim3 grid((unsigned)(geo.rows * geo.nb)), block(kThreads);
+  const T* gp = static_cast<const T*>(g);
+  const T* up = static_cast<const T*>(u);
+  T* hp = static_cast<T*>(h);
+  if (geo.vec)
+    swiglu_fwd_k<T, Vec<T>::N><<<grid, block, 0, st>>>(geo.nvr, geo.nb, gp, ldg, up, ldu, hp, ldh);
+  else
+    swiglu_fwd_k<T, 1><<<grid, block, 0, st>>>(geo.nvr, geo.nb, gp, ldg, up, ldu, hp, ldh);
+  return launch_status();
+}
+
+template <typename T>
+int bwd_impl(int64_t T_, int64_t F, const void* dh, int64_t lddh, const void* g, int64_t ldg,
+             const void* u, int64_t ldu, void* dg, int64_t lddg, void* du, int64_t lddu,
+             hipStream_t st) {
+  const void* p[5] = {dh, g, u, dg, du};
+  const int64_t l[5] = {lddh, ldg, ldu, lddg, lddu};
+  const Geo geo = plan<T>(T_, F, 5, p, l);
+  const dim3 grid((unsigned)(geo.rows * geo.nb)), block(kThreads);
+  const T* dhp = static_cast<const T*>(dh);
+  const T* gp = static_cast<const T*>(g);
+  const T* up = static_cast<const T*>(u);
+  T* dgp = static_cast<T*>(dg);
+  T* dup = static_cast<T*>(du);
+  if (geo.vec)
+    swiglu_bwd_k<T, Vec<T>::N><<<grid, block, 0, st>>>(geo.nvr, geo.nb, dhp, lddh, gp, ldg, up,
+                                                       ldu, dgp, lddg, dup, lddu);
+  else
+    swiglu_bwd_k<T, 1><<<grid, block, 0, st>>>(geo.nvr, geo.nb, dhp, lddh, gp, ldg, up, ldu,
+                                               dgp, lddg, dup, lddu);
+  return launch_status();
+}
+
+bool grid_fits(int64_t T_, int64_t F) {
+  // rows * column blocks must fit a 1-D grid
+  return T_ * ceil_div(F, kThreads * kUnroll) < (int64_t)UINT32_MAX &&
+         ceil_div(T_ * F, kThreads * kUnroll) < (int64_t)UINT32_MAX;
+}
+
+}  // namespace
+}  // namespace fo
+
+using namespace fo;
+
+extern "C" int fo_swiglu_fwd(int dtype, int64_t T, int64_t F, const void* gate, int64_t ldg,
+                             const void* up, int64_t ldu, void* h, int64_t ldh, void* stream) {
+  if (dtype != FO_F32 && dtype != FO_BF16) return FO_ERR_DTYPE;
+  if (T < 0 || F < 1 || !grid_fits(T, F)) return FO_ERR_SHAPE;
+  if (ldg < F || ldu < F || ldh < F) return FO_ERR_STRIDE;
+  if (T == 0) return FO_OK;
+  if (!gate || !up || !h) return FO_ERR_NULL;
+  hipStream_t st = as_stream(stream);
+  return dtype == FO_F32 ? fwd_impl<float>(T, F, gate, ldg, up, ldu, h, ldh, st)
+                         : fwd_impl<bf16>(T, F, gate, ldg, up, ldu, h, ldh, st);
+}
+
+extern "C" int fo_swiglu_bwd(int dtype, int64_t T, int64_t F, const void* dh, int64_t lddh,
+                             const void* gate, int64_t ldg, const void* up, int64_t ldu,
+                             void* dgate, int64_t lddg, void* dup, int64_t lddu, void* stream) {
+  if (dtype != FO_F32 && dtype != FO_BF16) return FO_ERR_DTYPE;
+  if (T < 0 || F < 1 || !grid_fits(T, F)) return FO_ERR_SHAPE;
+  if (lddh < F || ldg < F || ldu < F || lddg < F || lddu < F) return FO_ERR_STRIDE;
+  if (T == 0) return FO_OK;
+  if (!dh || !gate || !up || !dgate || !dup) return FO_ERR_NULL;
+  hipStream_t st = as_stream(stream);
+  return dtype == FO_F32
+             ? bwd_impl<float>(T, F, dh, lddh, gate, ldg, up, ldu, dgate, lddg, dup, lddu, st)
+             : bwd_impl<bf16>(T, F, dh, lddh, gate, ldg, up, ldu, dgate, lddg, dup, lddu, st);
+}

@@ -1,0 +1,317 @@
+// Cross-entropy row kernels (forward + backward in one sweep), shared by the
+// cross-entropy entry point and the fused linear cross-entropy chunk loop.
+//
+// Definition ("Fast-LLM: 高效大语言模型训练框架", 三 技术架构, 损失函数体系: cross-entropy
+// and a z-loss regulariser against over-confidence; the Triton kernel list of 整体框架结构
+// names entropy_loss and z_loss; the Liger section of "Kernels（自定义内核）" fuses
+// CrossEntropy).  For a valid row t with target y:
+//   lse = log sum_j exp(z_j),  loss_t = lse - z_y + c lse^2,
+//   dz_j = (dloss/N) (softmax_j (1 + 2 c lse) - [j == y])
+// Invalid rows (ignore_index or a target outside [0,V)) contribute no loss and get an
+// all +0.0 gradient row.  N, the number of valid rows, is counted by a first tiny
+// kernel so that the row kernel can scale the gradient in the same sweep.
+//
+// Row kernel, register-resident form: one workgroup per row; every thread loads its
+// NV 16-byte vectors of the row into registers, folding each into a running
+// (max, sum of exp) pair as it arrives (online logsumexp); the pairs are merged across
+// the workgroup in a fixed order; the gradient is then formed from the registers and
+// written.  The row is read from HBM once.  Rows too long for the registers (or not
+// vector-aligned) take the streaming form, which makes the same online pass and then
+// reads the row a second time for the gradient.
+#pragma once
+
+#include "fo_common.hpp"
+
+namespace fo {
+namespace xent {
+namespace {  // internal linkage: each including source file gets its own copy
+
+struct Counters {
+  long long n_valid;
+  int n_bad;
+  int pad;
+};
+
+__device__ __forceinline__ bool row_valid(long long y, long long V, long long ignore) {
+  return y != ignore && y >= 0 && y < V;
+}
+
+template <typename T> __device__ __forceinline__ float ex(float x);
+// fp32 inputs keep the accurate exponential (fp32 parity is checked at 1e-5);
+// bf16 inputs use the hardware exp2 path.
+template <> __device__ __forceinline__ float ex<float>(float x) { return expf(x); }
+template <> __device__ __forceinline__ float ex<bf16>(float x) { return __expf(x); }
+
+// Count valid and bad targets of rows [0, T).  One workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void count_targets(int64_t T_, int64_t V,
+                                                      const int64_t* __restrict__ tg,
+                                                      int64_t ignore, Counters* cnt) {
+  __shared__ long long sv[16], sb[16];
+  long long nv = 0, nb = 0;
+  for (int64_t t = threadIdx.x; t < T_; t += 1024) {
+    const long long y = tg[t];
+    nv += row_valid(y, V, ignore);
+    nb += (y != ignore) && (y < 0 || y >= V);
+  }
+  nv = wave_sum_i64(nv);
+  nb = wave_sum_i64(nb);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) { sv[w] = nv; sb[w] = nb; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long a = 0, b = 0;
+    for (int i = 0; i < 16; ++i) { a += sv[i]; b += sb[i]; }
+    cnt->n_valid = a;
+    cnt->n_bad = (int)b;
+    cnt->pad = 0;
+  }
+}
+
+// Fixed-order merge of the per-wave (m, s) pairs: every thread gets the same lse.
+template <int NT>
+__device__ __forceinline__ float block_lse(float m, float s, float* shm, float* shs) {
+  wave_lse(m, s);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) { shm[w] = m; shs[w] = s; }
+  __syncthreads();
+  float M = shm[0], S = shs[0];
+#pragma unroll
+  for (int i = 1; i < NT / kWave; ++i) lse_merge(M, S, shm[i], shs[i]);
+  return M + __logf(S);
+}
+
+// Writes one all-zero gradient row.
+template <typename Tout, int VEC, int NT>
+__device__ __forceinline__ void zero_row(Tout* dr, int64_t nvec) {
+  if constexpr (VEC > 1) {
+    Pack<Tout> z;
+    z.raw = u32x4{0, 0, 0, 0};
+    for (int64_t v = threadIdx.x; v < nvec; v += NT) store_pack(dr + v * VEC, z);
+  } else {
+    for (int64_t v = threadIdx.x; v < nvec; v += NT) dr[v] = from_f32<Tout>(0.f);
+  }
+}
+
+struct RowArgs {
+  int64_t T, V;
+  int64_t ldz, ldd;
+  int64_t ignore;
+  float zc, dloss;
+  const int64_t* tg;
+  const Counters* cnt;
+  float* row_loss;  // [T] loss_t (0 for invalid rows)
+  float* row_z;     // [T] c lse^2 (0 for invalid rows)
+};
+
+// Register-resident row kernel.  Requires V % VEC == 0, aligned rows, nvec <= NT*NV.
+template <typename Tin, typename Tout, int NV, int NT>
+__global__ __launch_bounds__(NT) void row_reg(RowArgs a, const Tin* z, Tout* dz) {
+  constexpr int VEC = Vec<Tin>::N;
+  static_assert(Vec<Tout>::N == VEC || Vec<Tout>::N == 2 * VEC, "vector widths");
+  __shared__ float shm[NT / kWave], shs[NT / kWave];
+  __shared__ float sh_zy;
+  const int64_t row = blockIdx.x;
+  const long long y = a.tg[row];
+  const int64_t nvec = a.V / VEC;
+  if (!row_valid(y, a.V, a.ignore)) {
+    if (dz != nullptr) {
+      Tout* dr = dz + row * a.ldd;
+      if constexpr (Vec<Tout>::N == VEC) zero_row<Tout, VEC, NT>(dr, nvec);
+      else for (int64_t e = threadIdx.x; e < a.V; e += NT) dr[e] = from_f32<Tout>(0.f);
+    }
+    if (threadIdx.x == 0) { a.row_loss[row] = 0.f; a.row_z[row] = 0.f; }
+    return;
+  }
+  const Tin* zr = z + row * a.ldz;
+  if (threadIdx.x == 0) sh_zy = to_f32(zr[y]);  // read before any gradient write
+  Pack<Tin> xv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t v = threadIdx.x + (int64_t)i * NT;
+    if (v < nvec) xv[i] = load_pack(zr + v * VEC);
+  }
+  float m = -INFINITY, s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t v = threadIdx.x + (int64_t)i * NT;
+    if (v < nvec) {
+      float vm = to_f32(xv[i].v[0]);
+#pragma unroll
+      for (int j = 1; j < VEC; ++j) vm = fmaxf(vm, to_f32(xv[i].v[j]));
+      if (vm > m) { s *= ex<Tin>(m - vm); m = vm; }
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) s += ex<Tin>(to_f32(xv[i].v[j]) - m);
+    }
+  }
+  const float lse = block_lse<NT>(m, s, shm, shs);
+  if (threadIdx.x == 0) {
+    const float zt = a.zc * lse * lse;
+    a.row_loss[row] = (lse - sh_zy) + zt;
+    a.row_z[row] = zt;
+  }
+  if (dz == nullptr) return;
+  const float scale = a.dloss / (float)a.cnt->n_valid;
+  const float coef = scale * fmaf(2.f * a.zc, lse, 1.f);
+  Tout* dr = dz + row * a.ldd;
+  // Keep the row in its packed 16-byte form between the passes (re-widen it below)
+  // instead of letting the compiler hold widened fp32 copies: half the registers.
+#pragma unroll
+  for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(xv[i].raw));
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t v = threadIdx.x + (int64_t)i * NT;
+    if (v < nvec) {
+      float g[VEC];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        g[j] = coef * ex<Tin>(to_f32(xv[i].v[j]) - lse);
+        if (v * VEC + j == y) g[j] -= scale;
+      }
+      if constexpr (Vec<Tout>::N == VEC) {
+        Pack<Tout> o;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) o.v[j] = from_f32<Tout>(g[j]);
+        store_pack(dr + v * VEC, o);
+      } else {
+        // fp32 in, bf16 out: VEC outputs fill half a 16-byte vector
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        union { u32x2 raw; Tout e[VEC]; } o;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) o.e[j] = from_f32<Tout>(g[j]);
+        __builtin_nontemporal_store(o.raw, reinterpret_cast<u32x2*>(dr + v * VEC));
+      }
+    }
+  }
+}
+
+// Streaming row kernel: any V, any alignment (VEC = 1) or aligned vectors (VEC > 1).
+// The second read of the row is a cached load (the row was just read, it is usually
+// still in L2 or the Infinity Cache).
+template <typename Tin, typename Tout, int VEC, int NT>
+__global__ __launch_bounds__(NT) void row_stream(RowArgs a, const Tin* z, Tout* dz) {
+  __shared__ float shm[NT / kWave], shs[NT / kWave];
+  __shared__ float sh_zy;
+  const int64_t row = blockIdx.x;
+  const long long y = a.tg[row];
+  if (!row_valid(y, a.V, a.ignore)) {
+    if (dz != nullptr) {
+      Tout* dr = dz + row * a.ldd;
+      for (int64_t e = threadIdx.x; e < a.V; e += NT) dr[e] = from_f32<Tout>(0.f);
+    }
+    if (threadIdx.x == 0) { a.row_loss[row] = 0.f; a.row_z[row] = 0.f; }
+    return;
+  }
+  const Tin* zr = z + row * a.ldz;
+  const int64_t nvec = a.V / VEC;  // VEC divides V on this path
+  if (threadIdx.x == 0) sh_zy = to_f32(zr[y]);
+  float m = -INFINITY, s = 0.f;
+  for (int64_t v = threadIdx.x; v < nvec; v += NT) {
+    float x[VEC];
+    if constexpr (VEC > 1) {
+      const Pack<Tin> p = load_pack_cached(zr + v * VEC);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) x[j] = to_f32(p.v[j]);
+    } else {
+      x[0] = to_f32(zr[v]);
+    }
+    float vm = x[0];
+#pragma unroll
+    for (int j = 1; j < VEC; ++j) vm = fmaxf(vm, x[j]);
+    if (vm > m) { s *= ex<Tin>(m - vm); m = vm; }
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) s += ex<Tin>(x[j] - m);
+  }
+  const float lse = block_lse<NT>(m, s, shm, shs);
+  if (threadIdx.x == 0) {
+    const float zt = a.zc * lse * lse;
+    a.row_loss[row] = (lse - sh_zy) + zt;
+    a.row_z[row] = zt;
+  }
+  if (dz == nullptr) return;
+  // In place (dz == z): every element below is read by the thread that then
+  // overwrites it, and the barrier in block_lse separates all first-pass reads.
+  const float scale = a.dloss / (float)a.cnt->n_valid;
+  const float coef = scale * fmaf(2.f * a.zc, lse, 1.f);
+  Tout* dr = dz + row * a.ldd;
+  for (int64_t v = threadIdx.x; v < nvec; v += NT) {
+    float x[VEC];
+    if constexpr (VEC > 1) {
+      const Pack<Tin> p = load_pack(zr + v * VEC);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) x[j] = to_f32(p.v[j]);
+    } else {
+      x[0] = to_f32(zr[v]);
+    }
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      float g = coef * ex<Tin>(x[j] - lse);
+      if (v * VEC + j == y) g -= scale;
+      dr[v * VEC + j] = from_f32<Tout>(g);
+    }
+  }
+}
+
+// loss = sum_t row_loss / N, z_loss = sum_t row_z / N (fp64, fixed order); also
+// publishes n_valid and the bad-target count.
+__global__ __launch_bounds__(1024) void finalize(int64_t T_, const float* __restrict__ row_loss,
+                                                 const float* __restrict__ row_z,
+                                                 const Counters* __restrict__ cnt, float* loss,
+                                                 float* z_loss, int64_t* n_valid,
+                                                 int32_t* status) {
+  __shared__ double s1[16], s2[16];
+  double a = 0.0, b = 0.0;
+  for (int64_t t = threadIdx.x; t < T_; t += 1024) {
+    a += (double)row_loss[t];
+    b += (double)row_z[t];
+  }
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) { s1[w] = a; s2[w] = b; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double A = 0.0, B = 0.0;
+    for (int i = 0; i < 16; ++i) { A += s1[i]; B += s2[i]; }
+    const long long n = cnt->n_valid;
+    *loss = n > 0 ? (float)(A / (double)n) : 0.f;
+    if (z_loss) *z_loss = n > 0 ? (float)(B / (double)n) : 0.f;
+    if (n_valid) *n_valid = n;
+    if (status) *status = cnt->n_bad;
+  }
+}
+
+// Chooses and launches the row kernel for rows [0, a.T) of z/dz.
+template <typename Tin, typename Tout>
+hipError_t launch_rows(const RowArgs& a, const Tin* z, Tout* dz, hipStream_t st) {
+  constexpr int VEC = Vec<Tin>::N;
+  const bool vec = a.V % VEC == 0 && a.ldz % VEC == 0 && aligned16(z) &&
+                   (dz == nullptr || (a.ldd % VEC == 0 && aligned16(dz)));
+  const dim3 grid((unsigned)a.T);
+  if (vec) {
+    const int64_t nvec = a.V / VEC;
+    if (nvec <= 256 * 4) {
+      const int64_t per = ceil_div(nvec, 256);
+      if (per <= 1) row_reg<Tin, Tout, 1, 256><<<grid, 256, 0, st>>>(a, z, dz);
+      else if (per <= 2) row_reg<Tin, Tout, 2, 256><<<grid, 256, 0, st>>>(a, z, dz);
+      else row_reg<Tin, Tout, 4, 256><<<grid, 256, 0, st>>>(a, z, dz);
+      return hipGetLastError();
+    }
+    const int64_t per = ceil_div(nvec, 1024);
+    switch (per) {
+      case 1: row_reg<Tin, Tout, 1, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      case 2: row_reg<Tin, Tout, 2, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      case 3: case 4: row_reg<Tin, Tout, 4, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      case 5: case 6: case 7: case 8: row_reg<Tin, Tout, 8, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      case 9: case 10: case 11: case 12: row_reg<Tin, Tout, 12, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      case 13: case 14: case 15: case 16: row_reg<Tin, Tout, 16, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      default: row_stream<Tin, Tout, VEC, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
+    }
+  } else {
+    row_stream<Tin, Tout, 1, 1024><<<grid, 1024, 0, st>>>(a, z, dz);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace xent
+}  // namespace fo

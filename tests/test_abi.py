@@ -1,0 +1,136 @@
+"""The C ABI library: it loads, exports every function include/fo.h declares, and its
+host-side argument checks return the documented statuses before any launch.  No GPU:
+only calls that must fail validation (or query sizes) are made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import reduction_rmsnorm_fwd_amd as fo
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fo.h")
+
+OK, NULL, SHAPE, DTYPE, STRIDE, WS, DEVICE, HIP = range(8)
+F32, BF16 = 0, 1
+P = ctypes.c_void_p(0x1000)  # a non-NULL pointer that is never dereferenced
+N = None
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fo_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fo.LIB_PATH):
+        pytest.fail("libfo.so is not built (run python -m reduction_rmsnorm_fwd_amd.build)")
+    return fo.load_library()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = declared()
+    assert len(names) == 14, names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in fo.SIGNATURES, f"binding lacks {n}"
+    assert set(fo.SIGNATURES) == set(names)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.fo_abi_version() == 1
+    for s in range(8):
+        assert lib.fo_status_str(s).decode().startswith("FO_")
+    assert b"unknown" in lib.fo_status_str(99)
+
+
+def test_no_device_here(lib):
+    # this container has no GPU: the device check must say so, not crash
+    assert lib.fo_device_supported(0) == DEVICE
+    assert lib.fo_device_supported(-1) == DEVICE
+
+
+def test_rmsnorm_validation(lib):
+    f = lib.fo_rmsnorm_fwd
+    assert f(7, 4, 8, P, 8, P, 1e-5, P, 8, N, N) == DTYPE
+    assert f(F32, -1, 8, P, 8, P, 1e-5, P, 8, N, N) == SHAPE
+    assert f(F32, 4, 0, P, 8, P, 1e-5, P, 8, N, N) == SHAPE
+    assert f(F32, 4, 8, P, 7, P, 1e-5, P, 8, N, N) == STRIDE
+    assert f(F32, 4, 8, P, 8, P, 1e-5, P, 4, N, N) == STRIDE
+    assert f(BF16, 4, 8, N, 8, P, 1e-5, P, 8, N, N) == NULL
+    assert f(BF16, 4, 8, P, 8, N, 1e-5, P, 8, N, N) == NULL
+    assert f(BF16, 0, 8, N, 8, N, 1e-5, N, 8, N, N) == OK  # empty: nothing to do
+    b = lib.fo_rmsnorm_bwd
+    ws = lib.fo_rmsnorm_bwd_workspace(100, 64)
+    assert ws >= 64 * 4 * min(100, 256)
+    assert lib.fo_rmsnorm_bwd_workspace(-1, 64) == 0
+    assert b(BF16, 100, 64, P, 64, P, 64, P, N, 1e-5, P, 64, N, P, ws, N) == NULL  # dw
+    assert b(BF16, 100, 64, P, 64, P, 64, P, N, 1e-5, P, 64, P, P, ws - 1, N) == WS
+    assert b(BF16, 100, 64, P, 64, P, 64, P, N, 1e-5, P, 64, P, N, ws, N) == WS
+    assert b(BF16, 100, 64, P, 63, P, 64, P, N, 1e-5, P, 64, P, P, ws, N) == STRIDE
+    assert b(BF16, 100, 64, N, 64, P, 64, P, N, 1e-5, P, 64, P, P, ws, N) == NULL
+
+
+def test_rope_validation(lib):
+    f = lib.fo_rope_fwd
+    assert f(BF16, 8, 4, 2, 7, P, 28, P, 14, P, 1e4, N) == SHAPE       # odd head_dim
+    assert f(BF16, 8, 6, 4, 8, P, 48, P, 32, P, 1e4, N) == SHAPE       # 6 % 4 != 0
+    assert f(BF16, 8, 4, 2, 1024, P, 4096, P, 2048, P, 1e4, N) == SHAPE  # head_dim > 512
+    assert f(BF16, 8, 4, 2, 8, P, 32, P, 16, P, 0.0, N) == SHAPE       # theta <= 0
+    assert f(BF16, 8, 4, 2, 8, P, 31, P, 16, P, 1e4, N) == STRIDE
+    assert f(BF16, 8, 4, 2, 8, P, 32, P, 15, P, 1e4, N) == STRIDE
+    assert f(BF16, 8, 4, 2, 8, P, 32, P, 16, N, 1e4, N) == NULL        # positions
+    assert f(BF16, 8, 4, 0, 8, P, 32, P, 16, P, 1e4, N) == SHAPE
+    assert lib.fo_rope_bwd(5, 8, 4, 2, 8, P, 32, P, 16, P, 1e4, N) == DTYPE
+
+
+def test_swiglu_validation(lib):
+    f = lib.fo_swiglu_fwd
+    assert f(BF16, 4, 0, P, 8, P, 8, P, 8, N) == SHAPE
+    assert f(BF16, 4, 8, P, 7, P, 8, P, 8, N) == STRIDE
+    assert f(BF16, 4, 8, P, 8, N, 8, P, 8, N) == NULL
+    assert f(BF16, 0, 8, N, 8, N, 8, N, 8, N) == OK
+    b = lib.fo_swiglu_bwd
+    assert b(BF16, 4, 8, P, 8, P, 8, P, 8, P, 8, P, 7, N) == STRIDE
+    assert b(BF16, 4, 8, P, 8, P, 8, P, 8, N, 8, P, 8, N) == NULL
+    assert b(2, 4, 8, P, 8, P, 8, P, 8, P, 8, P, 8, N) == DTYPE
+
+
+def test_xent_validation(lib):
+    f = lib.fo_xent_fwd_bwd
+    ws = lib.fo_xent_workspace(16, 100)
+    assert ws >= 2 * 16 * 4
+    assert f(BF16, 16, 100, P, 100, P, -100, 0.0, 1.0, P, 100, N, N, N, N, P, ws, N) == NULL
+    assert f(BF16, 16, 100, P, 99, P, -100, 0.0, 1.0, P, 100, P, N, N, N, P, ws, N) == STRIDE
+    assert f(BF16, 16, 100, P, 100, P, -100, 0.0, 1.0, P, 99, P, N, N, N, P, ws, N) == STRIDE
+    assert f(BF16, 16, 100, P, 100, P, -100, 0.0, 1.0, P, 100, P, N, N, N, P, ws - 1, N) == WS
+    assert f(BF16, 16, 0, P, 100, P, -100, 0.0, 1.0, P, 100, P, N, N, N, P, ws, N) == SHAPE
+    assert f(BF16, 16, 100, N, 100, P, -100, 0.0, 1.0, P, 100, P, N, N, N, P, ws, N) == NULL
+    assert f(3, 16, 100, P, 100, P, -100, 0.0, 1.0, P, 100, P, N, N, N, P, ws, N) == DTYPE
+
+
+def test_flce_validation(lib):
+    f = lib.fo_flce_fwd_bwd
+    ws = lib.fo_flce_workspace(64, 32, 100, 0, F32)
+    assert ws > 32 * 100 * 2  # at least the transposed weight
+    assert lib.fo_flce_workspace(64, 32, 100, 0, BF16) >= ws + 100 * 32 * 4
+    args = [BF16, 64, 32, 100, P, P, P, -100, 1e-4, 1.0, P, P, F32, P, N, N, N, 0, P, ws, N]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return f(*a)
+
+    assert call(a0=F32) == DTYPE                 # bf16 only
+    assert call(a12=5) == DTYPE                  # dweight dtype
+    assert call(a2=12) == SHAPE                  # H % 8
+    assert call(a3=0) == SHAPE
+    assert call(a13=N) == NULL                   # loss
+    assert call(a5=N) == NULL                    # weight
+    assert call(a4=ctypes.c_void_p(0x1002)) == STRIDE   # misaligned hidden
+    assert call(a19=ws - 1) == WS
+    assert call(a17=-1) == SHAPE

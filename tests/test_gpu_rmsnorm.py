@@ -1,0 +1,124 @@
+"""GPU parity of fo_rmsnorm_fwd / fo_rmsnorm_bwd against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from reduction_rmsnorm_fwd_amd import synth
+from tolerance import check
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run(fo, x, w, dy, eps, use_rstd=True):
+    xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
+    y, rstd = fo.fo_rmsnorm_fwd(xg, wg, eps)
+    dx, dw = fo.fo_rmsnorm_bwd(dyg, xg, wg, rstd if use_rstd else None, eps)
+    torch.cuda.synchronize()
+    return y.cpu(), rstd.cpu(), dx.cpu(), dw.cpu()
+
+
+def compare(x, w, dy, eps, dt, got, rows=None):
+    y, rstd, dx, dw = got
+    ry, rr = oracle.rmsnorm_fwd(x, w, eps)
+    rdx, rdw = oracle.rmsnorm_bwd(dy, x, w, eps)
+    sel = slice(None) if rows is None else rows
+    check(y[sel], ry[sel], dt, "y", single_rounding=True)
+    check(rstd[sel], rr[sel], "f32", "rstd")
+    check(dx[sel], rdx[sel], dt, "dx", single_rounding=True)
+    # dw is an fp32 output: the products of exact inputs summed in fp32
+    check(dw, rdw, "f32", "dw")
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+@pytest.mark.parametrize("T", [1, 67])
+def test_configs_small(gpu, cid, T):
+    cfg = synth.scaled(synth.CONFIGS[cid], T)
+    i = synth.rmsnorm_inputs(cfg)
+    got = run(gpu, i["x"], i["w"], i["dy"], cfg.eps)
+    compare(i["x"], i["w"], i["dy"], cfg.eps, cfg.dtype, got)
+    got2 = run(gpu, i["x"], i["w"], i["dy"], cfg.eps, use_rstd=False)
+    compare(i["x"], i["w"], i["dy"], cfg.eps, cfg.dtype, got2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [13, 1000, 4097, 8, 12288])
+def test_unaligned_and_wide_rows(gpu, dtype, d):
+    cfg = synth.Config(0, "odd", dtype, T=37, d=d, n_q=1, n_kv=1, head_dim=2, F=1, V=2,
+                       eps=1e-5, theta=1e4, logit_std=1, z_loss=0, ignore_frac=0,
+                       packed=False, doc_lengths=(37,), seed=11)
+    i = synth.rmsnorm_inputs(cfg)
+    got = run(gpu, i["x"], i["w"], i["dy"], cfg.eps)
+    compare(i["x"], i["w"], i["dy"], cfg.eps, dtype, got)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_strided_and_misaligned_rows(gpu, dtype):
+    td = synth.torch_dtype(dtype)
+    T, d, ld = 50, 256, 264  # ld > d and a multiple of the vector: strided fast path
+    g = torch.Generator().manual_seed(3)
+    base = torch.randn(T, ld, generator=g).to(td)
+    w = (1 + 0.1 * torch.randn(d, generator=g)).to(td)
+    dy = torch.randn(T, d, generator=g).to(td)
+    for off in (0, 1):  # off=1: base pointer not 16-byte aligned
+        xs = base[:, off:off + d]
+        xg = base.to(DEV)[:, off:off + d]
+        y, rstd = gpu.fo_rmsnorm_fwd(xg, w.to(DEV), 1e-6)
+        dx, dw = gpu.fo_rmsnorm_bwd(dy.to(DEV), xg, w.to(DEV), rstd, 1e-6)
+        torch.cuda.synchronize()
+        compare(xs, w, dy, 1e-6, dtype, (y.cpu(), rstd.cpu(), dx.cpu(), dw.cpu()))
+
+
+def test_in_place_forward_and_backward(gpu):
+    cfg = synth.scaled(synth.CONFIGS[3], 40)
+    i = synth.rmsnorm_inputs(cfg)
+    xg, wg = i["x"].to(DEV), i["w"].to(DEV)
+    ref_y, _ = gpu.fo_rmsnorm_fwd(xg, wg, cfg.eps)
+    x2 = xg.clone()
+    gpu.fo_rmsnorm_fwd(x2, wg, cfg.eps, y=x2, want_rstd=False)
+    dyg = i["dy"].to(DEV)
+    ref_dx, ref_dw = gpu.fo_rmsnorm_bwd(dyg, xg, wg, None, cfg.eps)
+    dy2 = dyg.clone()
+    _, dw2 = gpu.fo_rmsnorm_bwd(dy2, xg, wg, None, cfg.eps, dx=dy2)
+    torch.cuda.synchronize()
+    assert torch.equal(x2, ref_y) and torch.equal(dy2, ref_dx) and torch.equal(dw2, ref_dw)
+
+
+def test_empty_batch_zeroes_dw(gpu):
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(64, dtype=torch.bfloat16, device=DEV)
+    dw = torch.full((64,), 7.0, device=DEV)
+    gpu.fo_rmsnorm_bwd(x, x, w, None, 1e-5, dx=x, dw=dw)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0)
+
+
+def test_deterministic(gpu):
+    cfg = synth.scaled(synth.CONFIGS[4], 3000)
+    i = synth.rmsnorm_inputs(cfg)
+    a = run(gpu, i["x"], i["w"], i["dy"], cfg.eps)
+    b = run(gpu, i["x"], i["w"], i["dy"], cfg.eps)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4])
+def test_full_size_sampled(gpu, cid):
+    cfg = synth.CONFIGS[cid]
+    i = synth.rmsnorm_inputs(cfg)
+    got = run(gpu, i["x"], i["w"], i["dy"], cfg.eps)
+    rows = np.unique(np.concatenate([[0, 1, cfg.T - 1],
+                                     np.random.default_rng(cid).integers(0, cfg.T, 29)]))
+    y, rstd, dx, dw = got
+    x, w, dy = i["x"][rows], i["w"], i["dy"][rows]
+    ry, rr = oracle.rmsnorm_fwd(x, w, cfg.eps)
+    rdx, _ = oracle.rmsnorm_bwd(dy, x, w, cfg.eps)
+    check(y[rows], ry, cfg.dtype, "y", single_rounding=True)
+    check(rstd[rows], rr, "f32", "rstd")
+    check(dx[rows], rdx, cfg.dtype, "dx", single_rounding=True)
+    # dw needs every row: oracle over all T in row blocks
+    rdw = np.zeros(cfg.d)
+    for r0 in range(0, cfg.T, 2048):
+        rdw += oracle.rmsnorm_bwd(i["dy"][r0:r0 + 2048], i["x"][r0:r0 + 2048], w, cfg.eps)[1]
+    check(dw, rdw, "f32", "dw")

@@ -1,0 +1,133 @@
+"""GPU parity of fo_rope_fwd / fo_rope_bwd against the fp64 oracle, and the bit-exact
+position-reset properties."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from reduction_rmsnorm_fwd_amd import synth
+from tolerance import check
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def gpu_rope(fo, q, k, pos, theta, bwd=False):
+    qg, kg, pg = q.to(DEV).clone(), k.to(DEV).clone(), pos.to(DEV)
+    (fo.fo_rope_bwd if bwd else fo.fo_rope_fwd)(qg, kg, pg, theta)
+    torch.cuda.synchronize()
+    return qg.cpu(), kg.cpu()
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+@pytest.mark.parametrize("T", [1, 131])
+def test_configs_small(gpu, cid, T):
+    cfg = synth.CONFIGS[cid]
+    i = synth.rope_inputs(synth.scaled(cfg, T) if not cfg.packed else cfg)
+    sl = slice(0, T)
+    q, k, dq, dk = i["q"][sl], i["k"][sl], i["dq"][sl], i["dk"][sl]
+    pos = i["pos"][sl]
+    if cid == 3:
+        pos = pos + 7000  # large positions stress the angle precision
+    gq, gk = gpu_rope(gpu, q, k, pos, cfg.theta)
+    rq, rk = oracle.rope_fwd(q, k, pos, cfg.theta)
+    check(gq, rq, cfg.dtype, "q", single_rounding=True)
+    check(gk, rk, cfg.dtype, "k", single_rounding=True)
+    bq, bk = gpu_rope(gpu, dq, dk, pos, cfg.theta, bwd=True)
+    oq, ok = oracle.rope_bwd(dq, dk, pos, cfg.theta)
+    check(bq, oq, cfg.dtype, "dq", single_rounding=True)
+    check(bk, ok, cfg.dtype, "dk", single_rounding=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_long_positions_fp32_precision(gpu, dtype):
+    # positions up to 16383 and beyond: an fp32 angle would be off by ~1e-3 rad here
+    T, D = 64, 128
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn(T, 4, D, generator=g).to(synth.torch_dtype(dtype))
+    k = torch.randn(T, 2, D, generator=g).to(synth.torch_dtype(dtype))
+    pos = torch.from_numpy(np.linspace(0, 16383, T).astype(np.int64) + np.arange(T) % 3)
+    pos[-1] = 1_000_000
+    for theta in (1e4, 5e5, 1e6):
+        gq, gk = gpu_rope(gpu, q, k, pos, theta)
+        rq, rk = oracle.rope_fwd(q, k, pos, theta)
+        check(gq, rq, dtype, "q", single_rounding=True)
+        check(gk, rk, dtype, "k", single_rounding=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scalar_path_odd_pairs_and_strides(gpu, dtype):
+    # head_dim 10 (5 pairs: not a whole vector), token strides with padding
+    T, hq, hk, D = 33, 6, 3, 10
+    g = torch.Generator().manual_seed(6)
+    td = synth.torch_dtype(dtype)
+    qb = torch.randn(T, hq * D + 3, generator=g).to(td)
+    kb = torch.randn(T, hk * D + 5, generator=g).to(td)
+    q = qb[:, :hq * D].unflatten(1, (hq, D))
+    k = kb[:, :hk * D].unflatten(1, (hk, D))
+    pos = torch.arange(T, dtype=torch.int64) * 37
+    qg, kg = qb.to(DEV), kb.to(DEV)
+    gq = qg[:, :hq * D].unflatten(1, (hq, D))
+    gk = kg[:, :hk * D].unflatten(1, (hk, D))
+    gpu.fo_rope_fwd(gq, gk, pos.to(DEV), 1e4)
+    torch.cuda.synchronize()
+    rq, rk = oracle.rope_fwd(q, k, pos, 1e4)
+    check(gq.cpu(), rq, dtype, "q", single_rounding=True)
+    check(gk.cpu(), rk, dtype, "k", single_rounding=True)
+    # padding columns untouched
+    assert torch.equal(qg[:, hq * D:].cpu(), qb[:, hq * D:])
+    assert torch.equal(kg[:, hk * D:].cpu(), kb[:, hk * D:])
+
+
+def test_position_zero_is_bit_exact_identity(gpu):
+    cfg = synth.CONFIGS[4]
+    i = synth.rope_inputs(cfg)
+    q, k, pos = i["q"][:2000], i["k"][:2000], i["pos"][:2000]
+    q[0, 0, 0] = -0.0  # signed zero must survive too
+    gq, gk = gpu_rope(gpu, q, k, pos, cfg.theta)
+    z = (pos == 0).nonzero().flatten()
+    assert len(z) >= 2
+    for t in z.tolist():
+        assert torch.equal(gq[t].view(torch.int16), q[t].view(torch.int16))
+        assert torch.equal(gk[t].view(torch.int16), k[t].view(torch.int16))
+
+
+def test_packed_equals_separate_documents_bit_exact(gpu):
+    cfg = synth.CONFIGS[4]
+    i = synth.rope_inputs(cfg)
+    T = 6000
+    q, k, pos = i["q"][:T], i["k"][:T], i["pos"][:T]
+    gq, gk = gpu_rope(gpu, q, k, pos, cfg.theta)
+    starts = (pos == 0).nonzero().flatten().tolist() + [T]
+    assert len(starts) > 3
+    for a, b in zip(starts[:-1], starts[1:]):
+        sq, sk = gpu_rope(gpu, q[a:b], k[a:b], torch.arange(b - a), cfg.theta)
+        assert torch.equal(sq, gq[a:b]) and torch.equal(sk, gk[a:b]), (a, b)
+
+
+def test_fwd_then_bwd_round_trip(gpu):
+    cfg = synth.CONFIGS[3]
+    i = synth.rope_inputs(synth.scaled(cfg, 256))
+    q = i["q"].float()
+    k = i["k"].float()
+    pos = i["pos"] * 29
+    fq, fk = gpu_rope(gpu, q, k, pos, cfg.theta)
+    bq, bk = gpu_rope(gpu, fq, fk, pos, cfg.theta, bwd=True)
+    assert torch.max(torch.abs(bq - q)) < 5e-6 and torch.max(torch.abs(bk - k)) < 5e-6
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4])
+def test_full_size_sampled(gpu, cid):
+    cfg = synth.CONFIGS[cid]
+    i = synth.rope_inputs(cfg)
+    gq, gk = gpu_rope(gpu, i["q"], i["k"], i["pos"], cfg.theta)
+    bq, bk = gpu_rope(gpu, i["dq"], i["dk"], i["pos"], cfg.theta, bwd=True)
+    rows = np.unique(np.concatenate([[0, cfg.T - 1],
+                                     np.random.default_rng(cid).integers(0, cfg.T, 30)]))
+    p = i["pos"][rows]
+    rq, rk = oracle.rope_fwd(i["q"][rows], i["k"][rows], p, cfg.theta)
+    check(gq[rows], rq, cfg.dtype, "q", single_rounding=True)
+    check(gk[rows], rk, cfg.dtype, "k", single_rounding=True)
+    oq, ok = oracle.rope_bwd(i["dq"][rows], i["dk"][rows], p, cfg.theta)
+    check(bq[rows], oq, cfg.dtype, "dq", single_rounding=True)
+    check(bk[rows], ok, cfg.dtype, "dk", single_rounding=True)
