@@ -1,0 +1,328 @@
+"""Benchmark of the fused per-token training ops on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input, with
+every input already resident in HBM:
+  RMSNorm fwd + bwd, RoPE fwd + bwd on Q/K, SwiGLU fwd + bwd, cross-entropy fwd+bwd
+  (with z-loss) at the Llama-3-8B layer shapes (T 8192, d 4096, 32 Q / 8 KV heads of
+  128, ffn 14336, vocab 128256), and the fused linear cross-entropy of the lm head
+  of the same model (H [8192, 4096], W [128256, 4096], 10% ignored targets, z-loss).
+`value` is whole-step throughput in tokens/s (8192 tokens per step).  Per op it
+reports the time inside the step and in isolation (caches flushed before each call),
+the algorithmic bytes (or flops) and the fraction of the MI355X roofline.  The fp64
+CPU oracle is timed on a bounded sample of the same step as the baseline.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HBM GB/s & % of peak per fused op (fwd+bwd); xent/FLCE tokens/s"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
+FLUSH_BYTES = 1 << 30        # written between isolated calls: beyond L2 and the 256 MB MALL
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--iso-reps", type=int, default=10, help="isolated calls per op")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-isolated", action="store_true")
+    p.add_argument("--only", default="", help="comma list of ops to run (profiling)")
+    return p.parse_args()
+
+
+class Workload:
+    """Device-resident inputs/outputs of one step and the per-op callables."""
+
+    def __init__(self, fo, synth, torch, only=()):
+        self.fo, self.torch = fo, torch
+        dev = "cuda"
+        c3, c5 = synth.CONFIGS[3], synth.CONFIGS[5]
+        self.c3, self.c5 = c3, c5
+        T, d = c3.T, c3.d
+        self.T = T
+        r = synth.rmsnorm_inputs(c3)
+        self.x, self.w, self.dy = (r[k].to(dev) for k in ("x", "w", "dy"))
+        self.y = torch.empty_like(self.x)
+        self.dx = torch.empty_like(self.x)
+        self.rstd = torch.empty(T, dtype=torch.float32, device=dev)
+        self.dw = torch.empty(d, dtype=torch.float32, device=dev)
+        self.rms_ws = torch.empty(fo.fo_rmsnorm_bwd_workspace(T, d), dtype=torch.uint8, device=dev)
+        ro = synth.rope_inputs(c3)
+        self.q, self.k, self.dq, self.dk = (ro[k].to(dev) for k in ("q", "k", "dq", "dk"))
+        self.pos = ro["pos"].to(dev)
+        s = synth.swiglu_inputs(c3)
+        self.g, self.u, self.dh = (s[k].to(dev) for k in ("gate", "up", "dh"))
+        self.h = torch.empty_like(self.g)
+        self.dg = torch.empty_like(self.g)
+        self.du = torch.empty_like(self.g)
+        xe = synth.xent_inputs(c3)
+        self.logits, self.tg = xe["logits"].to(dev), xe["targets"].to(dev)
+        self.dlogits = torch.empty_like(self.logits)
+        self.xent_ws = torch.empty(fo.fo_xent_workspace(T, c3.V), dtype=torch.uint8, device=dev)
+        self.xo = fo._scalars(dev)
+        fl = synth.flce_inputs(c5)
+        self.H, self.W, self.ftg = (fl[k].to(dev) for k in ("hidden", "weight", "targets"))
+        self.dH = torch.empty_like(self.H)
+        self.dW = torch.empty(self.W.shape, dtype=torch.float32, device=dev)
+        self.flce_ws = torch.empty(fo.fo_flce_workspace(c5.T, c5.flce_H, c5.V, 0, fo.FO_F32),
+                                   dtype=torch.uint8, device=dev)
+        self.fo_out = fo._scalars(dev)
+        self.n_valid_x = int((xe["targets"] != synth.IGNORE_INDEX).sum())
+        self.n_valid_f = int((fl["targets"] != synth.IGNORE_INDEX).sum())
+        del r, ro, s, xe, fl
+        self.ops = self._ops()
+        if only:
+            self.ops = [o for o in self.ops if o[0] in only]
+
+    def _ops(self):
+        fo, c3, c5 = self.fo, self.c3, self.c5
+        T, d, b = c3.T, c3.d, 2
+        heads = c3.n_q + c3.n_kv
+        D, F, V = c3.head_dim, c3.F, c3.V
+        n_ign = T - self.n_valid_x
+        H5, V5 = c5.flce_H, c5.V
+        # algorithmic bytes (what each op must move at least) and flops
+        by = {
+            "rmsnorm_fwd": 2 * T * d * b + d * b + 4 * T,
+            "rmsnorm_bwd": 3 * T * d * b + d * b + 4 * T + 4 * d,
+            "rope_fwd": 2 * T * heads * D * b + 8 * T,
+            "rope_bwd": 2 * T * heads * D * b + 8 * T,
+            "swiglu_fwd": 3 * T * F * b,
+            "swiglu_bwd": 5 * T * F * b,
+            "xent_fwd_bwd": (2 * self.n_valid_x + n_ign) * V * b + 8 * T,
+        }
+        flce_flops = 6 * self.n_valid_f * H5 * V5
+        return [
+            ("rmsnorm_fwd", lambda: fo.fo_rmsnorm_fwd(self.x, self.w, c3.eps, y=self.y, rstd=self.rstd),
+             by["rmsnorm_fwd"], "hbm"),
+            ("rmsnorm_bwd", lambda: fo.fo_rmsnorm_bwd(self.dy, self.x, self.w, self.rstd, c3.eps,
+                                                      dx=self.dx, dw=self.dw, ws=self.rms_ws),
+             by["rmsnorm_bwd"], "hbm"),
+            ("rope_fwd", lambda: fo.fo_rope_fwd(self.q, self.k, self.pos, c3.theta),
+             by["rope_fwd"], "hbm"),
+            ("rope_bwd", lambda: fo.fo_rope_bwd(self.dq, self.dk, self.pos, c3.theta),
+             by["rope_bwd"], "hbm"),
+            ("swiglu_fwd", lambda: fo.fo_swiglu_fwd(self.g, self.u, h=self.h), by["swiglu_fwd"], "hbm"),
+            ("swiglu_bwd", lambda: fo.fo_swiglu_bwd(self.dh, self.g, self.u, dgate=self.dg, dup=self.du),
+             by["swiglu_bwd"], "hbm"),
+            ("xent_fwd_bwd", lambda: fo.fo_xent_fwd_bwd(self.logits, self.tg, -100, c3.z_loss, 1.0,
+                                                        dlogits=self.dlogits, ws=self.xent_ws,
+                                                        out=self.xo),
+             by["xent_fwd_bwd"], "hbm"),
+            ("flce_fwd_bwd", lambda: fo.fo_flce_fwd_bwd(self.H, self.W, self.ftg, -100, c5.z_loss, 1.0,
+                                                        dhidden=self.dH, dweight=self.dW,
+                                                        ws=self.flce_ws, out=self.fo_out),
+             flce_flops, "mfma"),
+        ]
+
+
+def gpu_bench(args):
+    import torch
+    import reduction_rmsnorm_fwd_amd as fo
+    from reduction_rmsnorm_fwd_amd import synth
+
+    torch.cuda.set_device(0)
+    fo.load()
+    only = tuple(s for s in args.only.split(",") if s)
+    t0 = time.time()
+    wl = Workload(fo, synth, torch, only)
+    print(f"# inputs resident in HBM after {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        for i, (_, fn, _, _) in enumerate(wl.ops):
+            if evs is not None:
+                evs[i][0].record(stream)
+            fn()
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+
+    nops = len(wl.ops)
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(nops)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    in_step = [[evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]
+               for i in range(nops)]
+    print(f"# timed {args.steps} steps in {wall:.3f}s", file=sys.stderr, flush=True)
+
+    iso = [None] * nops
+    if not args.no_isolated:
+        scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        for i, (name, fn, _, _) in enumerate(wl.ops):
+            ts = []
+            for _ in range(args.iso_reps):
+                scratch.fill_(1.0)  # evict L2 and the Infinity Cache
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                b.synchronize()
+                ts.append(a.elapsed_time(b))
+            iso[i] = ts
+        del scratch
+        print("# isolated timings done", file=sys.stderr, flush=True)
+
+    def med(v):
+        v = sorted(v)
+        return v[len(v) // 2]
+
+    per_op = {}
+    for i, (name, _, work, bound) in enumerate(wl.ops):
+        ms = sum(in_step[i]) / len(in_step[i])
+        e = {"ms_in_step": round(ms, 4)}
+        if iso[i] is not None:
+            e["ms_isolated_median"] = round(med(iso[i]), 4)
+            e["ms_isolated_p10_p90"] = [round(sorted(iso[i])[len(iso[i]) // 10], 4),
+                                        round(sorted(iso[i])[(9 * len(iso[i])) // 10], 4)]
+        t_ref = e.get("ms_isolated_median", ms)
+        if bound == "hbm":
+            e["algorithmic_MB"] = round(work / 1e6, 3)
+            e["GBps"] = round(work / (t_ref * 1e-3) / 1e9, 1)
+            e["frac_hbm_peak"] = round(work / (t_ref * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            e["GBps_in_step"] = round(work / (ms * 1e-3) / 1e9, 1)
+        else:
+            e["algorithmic_TFLOP"] = round(work / 1e12, 4)
+            e["TFLOPs"] = round(work / (t_ref * 1e-3) / 1e12, 1)
+            e["frac_bf16_peak"] = round(work / (t_ref * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+            e["tokens_per_s"] = round(wl.T / (t_ref * 1e-3), 1)
+        if name == "xent_fwd_bwd":
+            e["tokens_per_s"] = round(wl.T / (t_ref * 1e-3), 1)
+        per_op[name] = e
+
+    ms_step = wall / args.steps * 1e3
+    out = {
+        "metric": METRIC,
+        "value": round(wl.T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3-8b-shaped per-token ops fwd+bwd + lm-head fused linear cross-entropy",
+            "tokens_per_step": wl.T,
+            "layer_ops": "T 8192, d 4096, 32 Q / 8 KV heads x 128, ffn 14336, eps 1e-5, "
+                         "rope theta 5e5, vocab 128256, logits N(0,3^2), z-loss 1e-4",
+            "lm_head": "H [8192,4096] N(0,1), W [128256,4096] N(0,0.02^2), 10% ignore_index, "
+                       "z-loss 1e-4, dW fp32",
+            "parallelism": "single GPU",
+        },
+        "per_op": per_op,
+    }
+    # dominant op of the step: the fused linear cross-entropy (MFMA-bound)
+    if "flce_fwd_bwd" in per_op:
+        i = [o[0] for o in wl.ops].index("flce_fwd_bwd")
+        ms = sum(in_step[i]) / len(in_step[i])
+        work = wl.ops[i][2]
+        ach = work / (ms * 1e-3) / 1e12
+        out["roofline"] = {
+            "kernel": "fo_flce_fwd_bwd (per call: gemm_nt x3 per 2048-token chunk, cross-entropy "
+                      "row kernel, transposes)",
+            "bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "ms_per_launch": round(ms, 4),
+        }
+    return out, wl
+
+
+def cpu_baseline():
+    """The fp64 oracle, as it stands, on a bounded sample of the same step: 128 of the
+    8192 tokens for every layer op and 32 tokens for the lm head; times are scaled up
+    linearly in tokens (every op is per-token) to the step's 8192 tokens."""
+    import numpy as np
+    import torch
+    import oracle
+    from reduction_rmsnorm_fwd_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = os.cpu_count() or 1
+    c3, c5 = synth.CONFIGS[3], synth.CONFIGS[5]
+    n_layer, n_head = 128, 32
+    s3 = synth.scaled(c3, n_layer)
+    t = {}
+    r = synth.rmsnorm_inputs(s3)
+    a = time.perf_counter()
+    oracle.rmsnorm_fwd(r["x"], r["w"], c3.eps)
+    oracle.rmsnorm_bwd(r["dy"], r["x"], r["w"], c3.eps)
+    t["rmsnorm"] = time.perf_counter() - a
+    ro = synth.rope_inputs(s3)
+    a = time.perf_counter()
+    oracle.rope_fwd(ro["q"], ro["k"], ro["pos"], c3.theta)
+    oracle.rope_bwd(ro["dq"], ro["dk"], ro["pos"], c3.theta)
+    t["rope"] = time.perf_counter() - a
+    s = synth.swiglu_inputs(s3)
+    a = time.perf_counter()
+    oracle.swiglu_fwd(s["gate"], s["up"])
+    oracle.swiglu_bwd(s["dh"], s["gate"], s["up"])
+    t["swiglu"] = time.perf_counter() - a
+    xe = synth.xent_inputs(s3)
+    a = time.perf_counter()
+    oracle.xent_fwd_bwd(xe["logits"], xe["targets"], -100, c3.z_loss, 1.0)
+    t["xent"] = time.perf_counter() - a
+    fl = synth.flce_inputs(c5)  # the full weight; a token sample of the hidden states
+    h = fl["hidden"][:n_head]
+    tg = fl["targets"][:n_head]
+    a = time.perf_counter()
+    oracle.flce_fwd_bwd(h, fl["weight"], tg, -100, c5.z_loss, 1.0)
+    t["flce"] = time.perf_counter() - a
+    T = c3.T
+    est = (t["rmsnorm"] + t["rope"] + t["swiglu"] + t["xent"]) * T / n_layer + t["flce"] * T / n_head
+    return {
+        "value": round(T / est, 3), "unit": "tokens/s", "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle on {n_layer} of 8192 tokens for RMSNorm/RoPE/SwiGLU/xent "
+                  f"and {n_head} tokens for the lm-head FLCE (full 128256x4096 weight), scaled "
+                  f"linearly to one 8192-token step; elementwise numpy runs on 1 thread, the "
+                  f"FLCE matmuls on {blas_threads} BLAS threads",
+        "seconds_measured": round(sum(t.values()), 2),
+        "est_seconds_per_step": round(est, 2),
+        "per_op_seconds_sample": {k: round(v, 3) for k, v in t.items()},
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only; the library has no "
+                                   "multi-GPU path (see the sharding paragraph of the design "
+                                   "notes). Run with --gpus 1."}))
+        sys.exit(2)
+    out, wl = gpu_bench(args)
+    del wl
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

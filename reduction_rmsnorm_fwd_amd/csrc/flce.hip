@@ -108,7 +108,7 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
       g.B = W; g.ldb = H;
       g.C = Z; g.ldc = L.ldz;
       g.M = cl; g.N = V; g.K = H;
-      FO_HIP(gemm::launch<gemm::kStoreF32>(g, st));
+      FO_HIP((gemm::launch_cfg<256, 256, 64, 4, 2, gemm::kStoreF32>(g, st)));
       // 2. loss rows and dZ
       xent::RowArgs r;
       r.T = cl; r.V = V; r.ldz = L.ldz; r.ldd = L.Vpad; r.ignore = ignore; r.zc = zc;
@@ -123,7 +123,7 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
         h.B = Wt; h.ldb = L.Vpad;
         h.C = dH + c0 * H; h.ldc = H;
         h.M = cl; h.N = H; h.K = L.Vpad;
-        FO_HIP(gemm::launch<gemm::kStoreBF16>(h, st));
+        FO_HIP((gemm::launch_cfg<128, 128, 64, 2, 2, gemm::kStoreBF16>(h, st)));
       }
       // 4. dW contribution
       if (dW != nullptr) {
@@ -134,8 +134,8 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
         w.B = Hct; w.ldb = L.Cpad;
         w.C = dW32; w.ldc = H;
         w.M = V; w.N = H; w.K = clp;
-        if (c0 == 0) FO_HIP(gemm::launch<gemm::kStoreF32>(w, st));
-        else FO_HIP(gemm::launch<gemm::kAccumF32>(w, st));
+        if (c0 == 0) FO_HIP((gemm::launch_cfg<256, 256, 64, 4, 2, gemm::kStoreF32>(w, st)));
+        else FO_HIP((gemm::launch_cfg<256, 256, 64, 4, 2, gemm::kAccumF32>(w, st)));
       }
     }
   } else if (dW != nullptr) {

@@ -63,17 +63,19 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t nbl, int64_t tm, in
   on = r / gm;
 }
 
-template <int BM, int BN, int BK, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void gemm_nt(Args a) {
+// WGM x WGN waves; wave tile (BM/WGM) x (BN/WGN) as FM x FN blocks of 32x32.
+template <int BM, int BN, int BK, int WGM, int WGN, int MODE>
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_nt(Args a) {
+  constexpr int NT = WGM * WGN * 64;
   constexpr int PAD = 8;
   constexpr int LDS_ROW = BK + PAD;                 // elements
-  constexpr int WM = BM / 2, WN = BN / 2;           // wave tile
+  constexpr int WM = BM / WGM, WN = BN / WGN;       // wave tile
   constexpr int FM = WM / 32, FN = WN / 32;         // 32x32 blocks per wave
   constexpr int VPR = BK / 8;                       // 16-byte vectors per row slice
-  constexpr int A_LD = BM * VPR / kThreads;         // vectors per thread per slice
-  constexpr int B_LD = BN * VPR / kThreads;
-  static_assert(BM * VPR % kThreads == 0 && BN * VPR % kThreads == 0, "tile/threads");
-  static_assert(BK % 16 == 0, "BK");
+  constexpr int A_LD = BM * VPR / NT;               // vectors per thread per slice
+  constexpr int B_LD = BN * VPR / NT;
+  static_assert(BM * VPR % NT == 0 && BN * VPR % NT == 0, "tile/threads");
+  static_assert(BK % 16 == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
 
   __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDS_ROW];
   __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * LDS_ROW];
@@ -86,14 +88,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_nt(Args a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   // global -> register staging
   u32x4 ra[A_LD], rb[B_LD];
   auto load_slice = [&](int64_t k0) {
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-      const int idx = tid + i * kThreads;
+      const int idx = tid + i * NT;
       const int r = idx / VPR, c = (idx % VPR) * 8;
       const int64_t gm = m0 + r, gk = k0 + c;
       if (gm < a.M && gk < a.K)
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_nt(Args a) {
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      const int idx = tid + i * kThreads;
+      const int idx = tid + i * NT;
       const int r = idx / VPR, c = (idx % VPR) * 8;
       const int64_t gn = n0 + r, gk = k0 + c;
       if (gn < a.N && gk < a.K)
@@ -115,13 +117,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_nt(Args a) {
   auto store_slice = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-      const int idx = tid + i * kThreads;
+      const int idx = tid + i * NT;
       const int r = idx / VPR, c = (idx % VPR) * 8;
       *reinterpret_cast<u32x4*>(&As[buf][r * LDS_ROW + c]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      const int idx = tid + i * kThreads;
+      const int idx = tid + i * NT;
       const int r = idx / VPR, c = (idx % VPR) * 8;
       *reinterpret_cast<u32x4*>(&Bs[buf][r * LDS_ROW + c]) = rb[i];
     }
@@ -188,13 +190,17 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_nt(Args a) {
     }
 }
 
-template <int MODE>
-hipError_t launch(const Args& a, hipStream_t st) {
-  constexpr int BM = 128, BN = 128, BK = 64;
+template <int BM, int BN, int BK, int WGM, int WGN, int MODE>
+hipError_t launch_cfg(const Args& a, hipStream_t st) {
   const int64_t tiles = ceil_div(a.M, BM) * ceil_div(a.N, BN);
   if (tiles == 0) return hipSuccess;
-  gemm_nt<BM, BN, BK, MODE><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(a);
+  gemm_nt<BM, BN, BK, WGM, WGN, MODE><<<dim3((unsigned)tiles), dim3(WGM * WGN * 64), 0, st>>>(a);
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch(const Args& a, hipStream_t st) {
+  return launch_cfg<128, 128, 64, 2, 2, MODE>(a, st);
 }
 
 // dst[c, r] = src[r, c] for r < R, c < Cn; dst[c, r] = 0 for R <= r < Rpad.
