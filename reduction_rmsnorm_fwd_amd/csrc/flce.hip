@@ -26,7 +26,9 @@ constexpr int64_t kAutoChunk = 2048;
 
 struct Layout {
   int64_t C, Cpad, Vpad, ldz;
-  size_t off_cnt, off_loss, off_z, off_wt, off_zbuf, off_dz, off_dzt, off_hct, off_dw, total;
+  gemm::SplitPlan dh_split;  // split-K of the dH product (a full chunk)
+  size_t off_cnt, off_loss, off_z, off_wt, off_zbuf, off_dz, off_dzt, off_hct, off_dw,
+      off_part, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
@@ -48,6 +50,8 @@ Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
   L.off_dzt = take((size_t)V * L.Cpad * 2);
   L.off_hct = take((size_t)H * L.Cpad * 2);
   L.off_dw = take(dw_dtype == FO_BF16 ? (size_t)V * H * 4 : 0);
+  L.dh_split = gemm::split_plan(C, H, L.Vpad);
+  L.off_part = take(L.dh_split.splits > 1 ? (size_t)L.dh_split.splits * C * H * 4 : 0);
   L.total = o;
   return L;
 }
@@ -108,7 +112,7 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
       g.B = W; g.ldb = H;
       g.C = Z; g.ldc = L.ldz;
       g.M = cl; g.N = V; g.K = H;
-      FO_HIP((gemm::launch_cfg<256, 256, 64, 4, 2, gemm::kStoreF32>(g, st)));
+      FO_HIP(gemm::run<gemm::kStoreF32>(g, gemm::kWide, st));
       // 2. loss rows and dZ
       xent::RowArgs r;
       r.T = cl; r.V = V; r.ldz = L.ldz; r.ldd = L.Vpad; r.ignore = ignore; r.zc = zc;
@@ -116,14 +120,25 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
       r.row_z = row_z + c0;
       const bool need_grad = dH != nullptr || dW != nullptr;
       FO_HIP(xent::launch_rows<float, bf16>(r, Z, need_grad ? dZ : nullptr, st));
-      // 3. dH rows of the chunk
+      // 3. dH rows of the chunk (split over the vocabulary when a chunk's 256x256 tiles
+      //    cannot fill the chip; the fp32 partials are summed in a fixed order)
       if (dH != nullptr) {
         gemm::Args h;
         h.A = dZ; h.lda = L.Vpad;
         h.B = Wt; h.ldb = L.Vpad;
-        h.C = dH + c0 * H; h.ldc = H;
         h.M = cl; h.N = H; h.K = L.Vpad;
-        FO_HIP((gemm::launch_cfg<128, 128, 64, 2, 2, gemm::kStoreBF16>(h, st)));
+        const gemm::SplitPlan sp = gemm::split_plan(cl, H, L.Vpad);
+        if (sp.splits > 1 && sp.splits <= L.dh_split.splits) {
+          float* part = reinterpret_cast<float*>(ws + L.off_part);
+          h.C = part; h.ldc = H;
+          h.k_split = sp.k_split; h.c_split = cl * H;
+          FO_HIP(gemm::run<gemm::kStoreF32>(h, gemm::kWide, st));
+          gemm::reduce_splits_bf16<<<2048, 256, 0, st>>>(part, sp.splits, cl * H, H, dH + c0 * H, H);
+          FO_HIP(hipGetLastError());
+        } else {
+          h.C = dH + c0 * H; h.ldc = H;
+          FO_HIP(gemm::run<gemm::kStoreBF16>(h, gemm::kNarrow, st));
+        }
       }
       // 4. dW contribution
       if (dW != nullptr) {
@@ -134,8 +149,8 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
         w.B = Hct; w.ldb = L.Cpad;
         w.C = dW32; w.ldc = H;
         w.M = V; w.N = H; w.K = clp;
-        if (c0 == 0) FO_HIP((gemm::launch_cfg<256, 256, 64, 4, 2, gemm::kStoreF32>(w, st)));
-        else FO_HIP((gemm::launch_cfg<256, 256, 64, 4, 2, gemm::kAccumF32>(w, st)));
+        if (c0 == 0) FO_HIP(gemm::run<gemm::kStoreF32>(w, gemm::kWide, st));
+        else FO_HIP(gemm::run<gemm::kAccumF32>(w, gemm::kWide, st));
       }
     }
   } else if (dW != nullptr) {
