@@ -45,11 +45,28 @@ struct Args {
   // writes its fp32 partial at C + y*c_split (elements); k_split = 0: no split
   int64_t k_split = 0;
   int64_t c_split = 0;
+  // device-side extent: when dev_count is set, the effective M (dev_dim 1) or K
+  // (dev_dim 2) is clamp(*dev_count - count_base, 0, M or K), K rounded up to 64 (the
+  // operands hold zeros up to that point).  The grid stays sized for the static M;
+  // workgroups whose tile starts past the effective M return at once.
+  const long long* dev_count = nullptr;
+  int64_t count_base = 0;
+  int dev_dim = 0;
 };
 
 // The K slice of this workgroup row (split-K), applied to a copy of the arguments.
 __device__ __forceinline__ Args split_args(const Args& in) {
   Args a = in;
+  if (in.dev_count != nullptr) {
+    int64_t e = *in.dev_count - in.count_base;
+    if (e < 0) e = 0;
+    if (in.dev_dim == 1) {
+      a.M = e < in.M ? e : in.M;
+    } else {
+      e = (e + 63) / 64 * 64;
+      a.K = e < in.K ? e : in.K;
+    }
+  }
   if (in.k_split > 0) {
     const int64_t kb = (int64_t)blockIdx.y * in.k_split;
     a.A += kb;
@@ -98,10 +115,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_nt(Args a_in) {
   __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDS_ROW];
   __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * LDS_ROW];
 
-  const int64_t tm_n = ceil_div(a.M, BM), tn_n = ceil_div(a.N, BN);
+  const int64_t tm_n = ceil_div(a_in.M, BM), tn_n = ceil_div(a_in.N, BN);
   int64_t tm, tn;
   tile_of(blockIdx.x, (int64_t)gridDim.x, tm_n, tn_n, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
+  if (m0 >= a.M) return;  // past a device-side row count
+  if (MODE == kAccumF32 && a.K == 0) return;  // nothing to add
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -235,6 +254,39 @@ __device__ __forceinline__ void wait_vm(int n) {
   }
 }
 
+// Accumulator start values: zero, or (accumulate mode) the current C tile, loaded
+// straight into the accumulator registers before the K loop.  All loads are
+// independent, so they are in flight together with the first K slices' DMA.
+template <int MODE, int BM, int BN, int WM, int WN, int FM, int FN>
+__device__ __forceinline__ void init_tile(const Args& a, f32x16 (&acc)[FM][FN], int64_t m0,
+                                          int64_t n0, int wm, int wn, int fr, int fh) {
+  if constexpr (MODE != kAccumF32) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  } else {
+    const bool full = m0 + BM <= a.M && n0 + BN <= a.N;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t n = n0 + wn * WN + j * 32 + fr;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t mb = m0 + wm * WM + i * 32 + 8 * g + 4 * fh;
+          const float* p = static_cast<const float*>(a.C) + mb * a.ldc + n;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[i][j][4 * g + q] =
+                (full || (mb + q < a.M && n < a.N)) ? p[q * a.ldc] : 0.f;
+        }
+      }
+  }
+}
+
 // Epilogue: accumulator register r of block (i, j) holds C[8(r/4) + 4 fh + r%4][fr]
 // of the block.  Each group of 4 registers is 4 consecutive rows of one column, so a
 // row pointer is formed once per group; whole tiles skip the bounds tests.
@@ -259,10 +311,7 @@ __device__ __forceinline__ void store_tile(const Args& a, f32x16 (&acc)[FM][FN],
           float* p = static_cast<float*>(a.C) + mb * a.ldc + n;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            if (full || (mb + q < a.M && n < a.N)) {
-              if constexpr (MODE == kAccumF32) p[q * a.ldc] += acc[i][j][4 * g + q];
-              else p[q * a.ldc] = acc[i][j][4 * g + q];
-            }
+            if (full || (mb + q < a.M && n < a.N)) p[q * a.ldc] = acc[i][j][4 * g + q];
         }
       }
     }
@@ -286,10 +335,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_nt_dma(Args a_in) {
   __shared__ __attribute__((aligned(1024))) bf16 sA1[BM * BK], sB1[BN * BK];
   __shared__ __attribute__((aligned(1024))) bf16 sA2[ST == 3 ? BM * BK : 8], sB2[ST == 3 ? BN * BK : 8];
 
-  const int64_t tm_n = ceil_div(a.M, BM), tn_n = ceil_div(a.N, BN);
+  const int64_t tm_n = ceil_div(a_in.M, BM), tn_n = ceil_div(a_in.N, BN);
   int64_t tm, tn;
   tile_of(blockIdx.x, (int64_t)gridDim.x, tm_n, tn_n, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
+  if (m0 >= a.M) return;  // past a device-side row count
+  if (MODE == kAccumF32 && a.K == 0) return;  // nothing to add
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -339,13 +390,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_nt_dma(Args a_in) {
   };
 
   f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
   const int fr = lane & 31;
   const int fh = lane >> 5;
   // Every fragment row this lane reads is fr plus a multiple of 32, and
@@ -389,6 +433,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_nt_dma(Args a_in) {
       compute(cA, cB);
     };
     dma(sA0, sB0, 0);
+    init_tile<MODE, BM, BN, WM, WN, FM, FN>(a, acc, m0, n0, wm, wn, fr, fh);
     int64_t kt = 0;
     for (; kt + 2 <= nk; kt += 2) {
       step(sA0, sB0, sA1, sB1, kt);
@@ -404,6 +449,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_nt_dma(Args a_in) {
     };
     dma(sA0, sB0, 0);
     if (nk > 1) dma(sA1, sB1, BK);
+    init_tile<MODE, BM, BN, WM, WN, FM, FN>(a, acc, m0, n0, wm, wn, fr, fh);
     int64_t kt = 0;
     for (; kt + 3 <= nk; kt += 3) {
       step(sA0, sB0, sA2, sB2, kt);
@@ -477,11 +523,20 @@ inline SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
 }
 
 // out[m, n] = bf16(sum_s part[s, m, n]) summed in the order s = 0, 1, ...
+// (dev_rows: only rows m < *dev_rows - rows_base exist.)
 __global__ __launch_bounds__(256) void reduce_splits_bf16(const float* __restrict__ part,
                                                           int64_t splits, int64_t MN,
                                                           int64_t N, bf16* __restrict__ out,
-                                                          int64_t ldo) {
-  for (int64_t e4 = (int64_t)blockIdx.x * 256 + threadIdx.x; e4 * 4 < MN;
+                                                          int64_t ldo,
+                                                          const long long* dev_rows,
+                                                          int64_t rows_base) {
+  int64_t len = MN;  // elements to reduce; MN stays the stride between partials
+  if (dev_rows != nullptr) {
+    int64_t eff = *dev_rows - rows_base;
+    eff = eff < 0 ? 0 : eff;
+    if (eff * N < len) len = eff * N;
+  }
+  for (int64_t e4 = (int64_t)blockIdx.x * 256 + threadIdx.x; e4 * 4 < len;
        e4 += (int64_t)gridDim.x * 256) {
     const int64_t e = e4 * 4;
     float v[4] = {0.f, 0.f, 0.f, 0.f};

@@ -67,6 +67,56 @@ __global__ __launch_bounds__(1024) void count_targets(int64_t T_, int64_t V,
   }
 }
 
+// Valid rows in order: idx[j] = the j-th valid row, pos_of[t] = its j (or -1),
+// tg_valid[j] = its target; also the counters.  One workgroup of 1024 threads walks T
+// in blocks with a ballot/popcount prefix scan (deterministic).
+__global__ __launch_bounds__(1024) void compact_targets(int64_t T_, int64_t V,
+                                                        const int64_t* __restrict__ tg,
+                                                        int64_t ignore, Counters* cnt,
+                                                        int* __restrict__ idx,
+                                                        int* __restrict__ pos_of,
+                                                        int64_t* __restrict__ tg_valid) {
+  __shared__ int wsum[16];
+  __shared__ long long sb[16];
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  long long base = 0, nb = 0;
+  for (int64_t b0 = 0; b0 < T_; b0 += 1024) {
+    const int64_t t = b0 + threadIdx.x;
+    const long long y = t < T_ ? tg[t] : ignore;
+    const bool v = t < T_ && row_valid(y, V, ignore);
+    nb += (t < T_) && (y != ignore) && (y < 0 || y >= V);
+    const unsigned long long bal = __ballot(v);
+    const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[w] = __popcll(bal);
+    __syncthreads();
+    int off = 0, tot = 0;
+    for (int i = 0; i < 16; ++i) {
+      off += (i < w) ? wsum[i] : 0;
+      tot += wsum[i];
+    }
+    if (t < T_) {
+      const int p = v ? (int)(base + off + pre) : -1;
+      pos_of[t] = p;
+      if (v) {
+        idx[p] = (int)t;
+        tg_valid[p] = y;
+      }
+    }
+    base += tot;
+    __syncthreads();  // wsum is rewritten next block
+  }
+  nb = wave_sum_i64(nb);
+  if (lane == 0) sb[w] = nb;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long b = 0;
+    for (int i = 0; i < 16; ++i) b += sb[i];
+    cnt->n_valid = base;
+    cnt->n_bad = (int)b;
+    cnt->pad = 0;
+  }
+}
+
 // Fixed-order merge of the per-wave (m, s) pairs: every thread gets the same lse.
 template <int NT>
 __device__ __forceinline__ float block_lse(float m, float s, float* shm, float* shs) {
@@ -101,7 +151,26 @@ struct RowArgs {
   const Counters* cnt;
   float* row_loss;  // [T] loss_t (0 for invalid rows)
   float* row_z;     // [T] c lse^2 (0 for invalid rows)
+  // Compacted rows (fused linear cross-entropy): only rows < *dev_rows - rows_base
+  // exist; the ones after that up to the next multiple of 64 get a zero gradient row
+  // (they are K padding of the next contraction), the rest are left alone.
+  const long long* dev_rows = nullptr;
+  int64_t rows_base = 0;
 };
+
+// true if this row is past a device-side row count (and handled here)
+template <typename Tout>
+__device__ __forceinline__ bool beyond_rows(const RowArgs& a, int64_t row, Tout* dz, int nt) {
+  if (a.dev_rows == nullptr) return false;
+  int64_t eff = *a.dev_rows - a.rows_base;
+  eff = eff < 0 ? 0 : (eff > a.T ? a.T : eff);
+  if (row < eff) return false;
+  if (dz != nullptr && row < (eff + 63) / 64 * 64) {
+    Tout* dr = dz + row * a.ldd;
+    for (int64_t e = threadIdx.x; e < a.V; e += nt) dr[e] = from_f32<Tout>(0.f);
+  }
+  return true;
+}
 
 // Register-resident row kernel.  Requires V % VEC == 0, aligned rows, nvec <= NT*NV.
 template <typename Tin, typename Tout, int NV, int NT>
@@ -111,6 +180,7 @@ __global__ __launch_bounds__(NT) void row_reg(RowArgs a, const Tin* z, Tout* dz)
   __shared__ float shm[NT / kWave], shs[NT / kWave];
   __shared__ float sh_zy;
   const int64_t row = blockIdx.x;
+  if (beyond_rows(a, row, dz, NT)) return;
   const long long y = a.tg[row];
   const int64_t nvec = a.V / VEC;
   if (!row_valid(y, a.V, a.ignore)) {
@@ -192,6 +262,7 @@ __global__ __launch_bounds__(NT) void row_stream(RowArgs a, const Tin* z, Tout* 
   __shared__ float shm[NT / kWave], shs[NT / kWave];
   __shared__ float sh_zy;
   const int64_t row = blockIdx.x;
+  if (beyond_rows(a, row, dz, NT)) return;
   const long long y = a.tg[row];
   if (!row_valid(y, a.V, a.ignore)) {
     if (dz != nullptr) {
@@ -253,13 +324,15 @@ __global__ __launch_bounds__(NT) void row_stream(RowArgs a, const Tin* z, Tout* 
 
 // loss = sum_t row_loss / N, z_loss = sum_t row_z / N (fp64, fixed order); also
 // publishes n_valid and the bad-target count.
+// compacted: the per-row arrays hold the valid rows first; only those are summed.
 __global__ __launch_bounds__(1024) void finalize(int64_t T_, const float* __restrict__ row_loss,
                                                  const float* __restrict__ row_z,
                                                  const Counters* __restrict__ cnt, float* loss,
                                                  float* z_loss, int64_t* n_valid,
-                                                 int32_t* status) {
+                                                 int32_t* status, int compacted = 0) {
   __shared__ double s1[16], s2[16];
   double a = 0.0, b = 0.0;
+  if (compacted && cnt->n_valid < T_) T_ = cnt->n_valid;
   for (int64_t t = threadIdx.x; t < T_; t += 1024) {
     a += (double)row_loss[t];
     b += (double)row_z[t];
