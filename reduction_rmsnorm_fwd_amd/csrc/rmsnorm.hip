@@ -56,6 +56,10 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
   T* yr = y + row * ldy;
+  // re-widen from the packed row instead of holding fp32 copies: fewer VGPRs, more
+  // waves per SIMD
+#pragma unroll
+  for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(xv[i].raw));
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int v = lane + i * kWave;
@@ -139,21 +143,29 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
   const float inv_d = 1.0f / (float)d;
   const int64_t stride = (int64_t)gridDim.x * RG;
   const int64_t rounds = ceil_div(T_ - (int64_t)blockIdx.x * RG, stride);
-  for (int64_t rd = 0; rd < rounds; ++rd) {
+  // The next round's rows are loaded before the current round is reduced, so a
+  // round's cross-wave barrier never leaves the memory pipe empty.
+  Pack<T> gv[NV], xv[NV], gn[NV], xn[NV];
+  auto load_round = [&](int64_t rd, Pack<T>* g, Pack<T>* xx) {
     const int64_t row = (int64_t)blockIdx.x * RG + rg + rd * stride;
-    const bool live = row < T_;
-    Pack<T> gv[NV], xv[NV];
+    const bool live = rd < rounds && row < T_;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int v = vbase + i * RW * kWave;
       if (live && v < nvec) {
-        gv[i] = load_pack(dy + row * lddy + (int64_t)v * VEC);
-        xv[i] = load_pack(x + row * ldx + (int64_t)v * VEC);
+        g[i] = load_pack(dy + row * lddy + (int64_t)v * VEC);
+        xx[i] = load_pack(x + row * ldx + (int64_t)v * VEC);
       } else {
-        gv[i].raw = u32x4{0, 0, 0, 0};
-        xv[i].raw = u32x4{0, 0, 0, 0};
+        g[i].raw = u32x4{0, 0, 0, 0};
+        xx[i].raw = u32x4{0, 0, 0, 0};
       }
     }
+  };
+  load_round(0, gv, xv);
+  for (int64_t rd = 0; rd < rounds; ++rd) {
+    const int64_t row = (int64_t)blockIdx.x * RG + rg + rd * stride;
+    const bool live = row < T_;
+    load_round(rd + 1, gn, xn);
     float dot = 0.f, ss = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
@@ -165,6 +177,9 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
       }
     dot = wave_sum(dot);
     ss = wave_sum(ss);
+    // keep the operands packed across the reduction (re-widened below)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(gv[i].raw), "+v"(xv[i].raw), "+v"(wv[i].raw));
     if constexpr (RW > 1) {
       if (lane == 0) { xdot[wave] = dot; xss[wave] = ss; }
       __syncthreads();
@@ -174,24 +189,30 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
       for (int k = 0; k < RW; ++k) { dot += xdot[rg * RW + k]; ss += xss[rg * RW + k]; }
       __syncthreads();  // slots are rewritten next round
     }
-    if (!live) continue;
-    const float r = rstd != nullptr ? rstd[row] : 1.0f / sqrtf(ss * inv_d + eps);
-    const float k = r * r * r * (dot * inv_d);
-    T* dxr = dx + row * lddx;
+    if (live) {
+      const float r = rstd != nullptr ? rstd[row] : 1.0f / sqrtf(ss * inv_d + eps);
+      const float k = r * r * r * (dot * inv_d);
+      T* dxr = dx + row * lddx;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int v = vbase + i * RW * kWave;
+        if (v < nvec) {
+          Pack<T> o;
+#pragma unroll
+          for (int j = 0; j < VEC; ++j) {
+            const float xf = to_f32(xv[i].v[j]);
+            const float gf = to_f32(gv[i].v[j]);
+            o.v[j] = from_f32<T>(r * (to_f32(wv[i].v[j]) * gf) - k * xf);
+            acc[i][j] = fmaf(gf * xf, r, acc[i][j]);
+          }
+          store_pack(dxr + (int64_t)v * VEC, o);
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int v = vbase + i * RW * kWave;
-      if (v < nvec) {
-        Pack<T> o;
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-          const float xf = to_f32(xv[i].v[j]);
-          const float gf = to_f32(gv[i].v[j]);
-          o.v[j] = from_f32<T>(r * (to_f32(wv[i].v[j]) * gf) - k * xf);
-          acc[i][j] = fmaf(gf * xf, r, acc[i][j]);
-        }
-        store_pack(dxr + (int64_t)v * VEC, o);
-      }
+      gv[i] = gn[i];
+      xv[i] = xn[i];
     }
   }
   // fold the row groups' column partials in order 0,1,2,... (RW waves of a group own
@@ -268,16 +289,16 @@ __global__ __launch_bounds__(256) void rmsnorm_dw_partial_block(
   partial[g * d + j] = acc;
 }
 
-// dw[j] = sum_g partial[g, j] in the order g = 0,1,...: 4 row phases per column, then
-// the 4 phase sums in order.
-__global__ __launch_bounds__(256) void rmsnorm_dw_reduce(int64_t G, int64_t d,
-                                                        const float* __restrict__ partial,
-                                                        float* __restrict__ dw) {
-  __shared__ float sh[4][64];
+// dw[j] = sum_g partial[g, j]: 16 row phases per column (phase p sums its rows in
+// order), then the 16 phase sums in order p = 0..15.  A workgroup covers 64 columns.
+__global__ __launch_bounds__(1024) void rmsnorm_dw_reduce(int64_t G, int64_t d,
+                                                         const float* __restrict__ partial,
+                                                         float* __restrict__ dw) {
+  __shared__ float sh[16][64];
   const int c = threadIdx.x & 63;
   const int ph = threadIdx.x >> 6;
   const int64_t j = (int64_t)blockIdx.x * 64 + c;
-  const int64_t per = (G + 3) / 4;
+  const int64_t per = (G + 15) / 16;
   const int64_t g0 = ph * per;
   const int64_t g1 = (g0 + per < G) ? g0 + per : G;
   float acc = 0.f;
@@ -285,7 +306,12 @@ __global__ __launch_bounds__(256) void rmsnorm_dw_reduce(int64_t G, int64_t d,
     for (int64_t g = g0; g < g1; ++g) acc += partial[g * d + j];
   sh[ph][c] = acc;
   __syncthreads();
-  if (ph == 0 && j < d) dw[j] = ((sh[0][c] + sh[1][c]) + sh[2][c]) + sh[3][c];
+  if (ph == 0 && j < d) {
+    float t = sh[0][c];
+#pragma unroll
+    for (int p = 1; p < 16; ++p) t += sh[p][c];
+    dw[j] = t;
+  }
 }
 
 __global__ void fill_f32(float* p, int64_t n, float v) {
@@ -388,7 +414,7 @@ int bwd_impl(int64_t T_, int64_t d, const void* dy, int64_t lddy, const void* x,
     rmsnorm_dw_partial_block<T><<<dim3((unsigned)ceil_div(d, 256), (unsigned)G), dim3(256), 0, st>>>(
         T_, d, dyp, lddy, xp, ldx, r, rows_per_group, partial);
   }
-  rmsnorm_dw_reduce<<<dim3((unsigned)ceil_div(d, 64)), dim3(256), 0, st>>>(G, d, partial, dw);
+  rmsnorm_dw_reduce<<<dim3((unsigned)ceil_div(d, 64)), dim3(1024), 0, st>>>(G, d, partial, dw);
   return launch_status();
 }
 

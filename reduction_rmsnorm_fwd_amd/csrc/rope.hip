@@ -7,7 +7,7 @@
 //   a[t,i] = pos[t] * theta^(-2i/D),  (x_i, x_{i+D/2}) <- R(a) (x_i, x_{i+D/2})
 // The backward applies R(-a).
 //
-// A workgroup owns kTok consecutive tokens.  It first computes cos/sin of every
+// A workgroup owns a few consecutive tokens.  It first computes cos/sin of every
 // (token, pair) once into LDS: the angle is the fp64 product of the position and the
 // host-computed fp64 frequency, range-reduced against 2*pi in fp64, and only the
 // reduced angle (|r| <= pi) is rounded to fp32 for sincosf.  That keeps the angle
@@ -23,8 +23,9 @@ namespace fo {
 namespace {
 
 constexpr int kMaxHeadDim = 512;
-constexpr int kTok = 4;          // tokens per workgroup
+constexpr int kMaxTok = 8;       // tokens per workgroup, at most
 constexpr int kThreads = 256;
+constexpr int kMaxU = 4;         // (low, high) vector pairs per thread, at most
 
 struct Freqs {
   double f[kMaxHeadDim / 2];  // theta^(-2i/D), fp64, computed on the host
@@ -41,16 +42,19 @@ __device__ __forceinline__ void rope_cs(double a, float& c, float& s) {
   sincosf((float)r, &s, &c);
 }
 
-// VEC elements per access (16-byte vectors, or 1 for the scalar path)
+// VEC elements per access (16-byte vectors, or 1 for the scalar path).  A workgroup
+// owns `tok` consecutive tokens (chosen by the host so that each thread has at most
+// kMaxU units); every thread first issues the loads of all its units, then rotates and
+// stores them, so up to 2*kMaxU 16-byte loads per thread are in flight.
 template <typename T, int VEC>
 __global__ __launch_bounds__(kThreads) void rope_kernel(
-    int64_t T_, int nq, int nkv, int D, T* q, int64_t ldq, T* k, int64_t ldk,
+    int64_t T_, int nq, int nkv, int D, int tok, T* q, int64_t ldq, T* k, int64_t ldk,
     const int64_t* __restrict__ pos, Freqs fr, float sgn) {
-  __shared__ float cs[kTok][kMaxHeadDim / 2][2];
-  __shared__ int ident[kTok];
+  __shared__ float cs[kMaxTok][kMaxHeadDim / 2][2];
+  __shared__ int ident[kMaxTok];
   const int P = D / 2;
-  const int64_t t0 = (int64_t)blockIdx.x * kTok;
-  const int ntok = (T_ - t0 < kTok) ? (int)(T_ - t0) : kTok;
+  const int64_t t0 = (int64_t)blockIdx.x * tok;
+  const int ntok = (T_ - t0 < tok) ? (int)(T_ - t0) : tok;
   if (threadIdx.x < ntok) ident[threadIdx.x] = pos[t0 + threadIdx.x] == 0;
   for (int u = threadIdx.x; u < ntok * P; u += kThreads) {
     const int tl = u / P, i = u - tl * P;
@@ -61,39 +65,57 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(
     cs[tl][i][1] = sgn * s;
   }
   __syncthreads();
-  const int PV = P / VEC;             // vectors per half head
-  const int heads = nq + nkv;
-  const int per_tok = heads * PV;
-  for (int u = threadIdx.x; u < ntok * per_tok; u += kThreads) {
-    const int tl = u / per_tok;
-    const int rem = u - tl * per_tok;
-    const int h = rem / PV;
-    const int pv = rem - h * PV;
-    if (ident[tl]) continue;
-    const int64_t t = t0 + tl;
-    T* base = (h < nq) ? q + t * ldq + (int64_t)h * D : k + t * ldk + (int64_t)(h - nq) * D;
-    T* lo = base + pv * VEC;
-    T* hi = lo + P;
-    float c[VEC], s[VEC];
+  const int PV = P / VEC;  // vectors per half head
+  const int per_tok = (nq + nkv) * PV;
+  const int nunits = ntok * per_tok;
+  for (int ub = 0; ub < nunits; ub += kThreads * kMaxU) {
+    T* lo[kMaxU];
+    Pack<T> a[kMaxU], b[kMaxU];
+    int tlu[kMaxU], pvu[kMaxU];
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      c[j] = cs[tl][pv * VEC + j][0];
-      s[j] = cs[tl][pv * VEC + j][1];
+    for (int m = 0; m < kMaxU; ++m) {
+      const int u = ub + threadIdx.x + m * kThreads;
+      lo[m] = nullptr;
+      if (u < nunits) {
+        const int tl = u / per_tok;
+        const int rem = u - tl * per_tok;
+        const int h = rem / PV;
+        const int pv = rem - h * PV;
+        if (!ident[tl]) {
+          const int64_t t = t0 + tl;
+          T* base = (h < nq) ? q + t * ldq + (int64_t)h * D : k + t * ldk + (int64_t)(h - nq) * D;
+          lo[m] = base + pv * VEC;
+          tlu[m] = tl;
+          pvu[m] = pv;
+          if constexpr (VEC > 1) {
+            a[m] = load_pack(lo[m]);
+            b[m] = load_pack(lo[m] + P);
+          } else {
+            a[m].v[0] = lo[m][0];
+            b[m].v[0] = lo[m][P];
+          }
+        }
+      }
     }
-    if constexpr (VEC > 1) {
-      Pack<T> a = load_pack(lo), b = load_pack(hi), oa, ob;
+#pragma unroll
+    for (int m = 0; m < kMaxU; ++m) {
+      if (lo[m] == nullptr) continue;
+      Pack<T> oa, ob;
 #pragma unroll
       for (int j = 0; j < VEC; ++j) {
-        const float x1 = to_f32(a.v[j]), x2 = to_f32(b.v[j]);
-        oa.v[j] = from_f32<T>(fmaf(x1, c[j], -x2 * s[j]));
-        ob.v[j] = from_f32<T>(fmaf(x2, c[j], x1 * s[j]));
+        const float c = cs[tlu[m]][pvu[m] * VEC + j][0];
+        const float sn = cs[tlu[m]][pvu[m] * VEC + j][1];
+        const float x1 = to_f32(a[m].v[j]), x2 = to_f32(b[m].v[j]);
+        oa.v[j] = from_f32<T>(fmaf(x1, c, -x2 * sn));
+        ob.v[j] = from_f32<T>(fmaf(x2, c, x1 * sn));
       }
-      store_pack(lo, oa);
-      store_pack(hi, ob);
-    } else {
-      const float x1 = to_f32(lo[0]), x2 = to_f32(hi[0]);
-      lo[0] = from_f32<T>(fmaf(x1, c[0], -x2 * s[0]));
-      hi[0] = from_f32<T>(fmaf(x2, c[0], x1 * s[0]));
+      if constexpr (VEC > 1) {
+        store_pack(lo[m], oa);
+        store_pack(lo[m] + P, ob);
+      } else {
+        lo[m][0] = oa.v[0];
+        lo[m][P] = ob.v[0];
+      }
     }
   }
 }
@@ -106,12 +128,17 @@ int rope_impl(int64_t T_, int nq, int nkv, int D, void* q, int64_t ldq, void* k,
   constexpr int VEC = Vec<T>::N;
   const bool vec = (D / 2) % VEC == 0 && ldq % VEC == 0 && ldk % VEC == 0 && aligned16(q) &&
                    aligned16(k);
-  const dim3 grid((unsigned)ceil_div(T_, kTok)), block(kThreads);
+  const int per_tok = (nq + nkv) * ((D / 2) / (vec ? VEC : 1));
+  // tokens per workgroup: as many as fit kMaxU units per thread (at least one token;
+  // a token wider than that takes several passes of the unit loop below)
+  int tok = (kThreads * kMaxU) / per_tok;
+  tok = tok < 1 ? 1 : (tok > kMaxTok ? kMaxTok : tok);
+  const dim3 grid((unsigned)ceil_div(T_, tok)), block(kThreads);
   if (vec)
-    rope_kernel<T, VEC><<<grid, block, 0, st>>>(T_, nq, nkv, D, static_cast<T*>(q), ldq,
+    rope_kernel<T, VEC><<<grid, block, 0, st>>>(T_, nq, nkv, D, tok, static_cast<T*>(q), ldq,
                                                 static_cast<T*>(k), ldk, pos, fr, sgn);
   else
-    rope_kernel<T, 1><<<grid, block, 0, st>>>(T_, nq, nkv, D, static_cast<T*>(q), ldq,
+    rope_kernel<T, 1><<<grid, block, 0, st>>>(T_, nq, nkv, D, tok, static_cast<T*>(q), ldq,
                                               static_cast<T*>(k), ldk, pos, fr, sgn);
   return launch_status();
 }

@@ -17,7 +17,7 @@ namespace fo {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 2;  // vectors per thread per operand
+constexpr int kUnroll = 4;  // vectors per thread per operand
 
 __device__ __forceinline__ float sigmoid_f(float g) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-g));

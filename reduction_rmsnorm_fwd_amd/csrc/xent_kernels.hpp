@@ -227,15 +227,19 @@ __global__ __launch_bounds__(NT) void row_reg(RowArgs a, const Tin* z, Tout* dz)
   // instead of letting the compiler hold widened fp32 copies: half the registers.
 #pragma unroll
   for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(xv[i].raw));
+  const int64_t yv = y / VEC;          // the vector holding the target
+  const int yj = (int)(y - yv * VEC);  // and its element
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int64_t v = threadIdx.x + (int64_t)i * NT;
     if (v < nvec) {
       float g[VEC];
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        g[j] = coef * ex<Tin>(to_f32(xv[i].v[j]) - lse);
-        if (v * VEC + j == y) g[j] -= scale;
+      for (int j = 0; j < VEC; ++j) g[j] = coef * ex<Tin>(to_f32(xv[i].v[j]) - lse);
+      if (v == yv) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+          if (j == yj) g[j] -= scale;
       }
       if constexpr (Vec<Tout>::N == VEC) {
         Pack<Tout> o;
