@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-isolated", action="store_true")
     p.add_argument("--only", default="", help="comma list of ops to run (profiling)")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="first run one plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
 
 
@@ -135,6 +137,18 @@ def gpu_bench(args):
 
     torch.cuda.set_device(0)
     fo.load()
+    if args.calib_copy:
+        # a plain copy of known size: 1 GiB read + 1 GiB written, for scaling the
+        # FETCH_SIZE / WRITE_SIZE counters of the ops
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        evict = torch.empty(1 << 29, dtype=torch.float32, device="cuda")
+        evict.fill_(0.0)  # 2 GiB written after src: src is read cold from HBM below
+        torch.cuda.synchronize()
+        # device-to-device memcpy: the runtime's plain blit kernel
+        dst.untyped_storage().copy_(src.untyped_storage())
+        torch.cuda.synchronize()
+        del src, dst, evict
     only = tuple(s for s in args.only.split(",") if s)
     t0 = time.time()
     wl = Workload(fo, synth, torch, only)

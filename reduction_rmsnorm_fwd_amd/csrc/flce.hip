@@ -8,8 +8,10 @@
 // The full [T, V] logits never exist: tokens go through in chunks of C rows, and per
 // chunk
 //   1. Z_c = H_c W^T            bf16 MFMA, fp32 out, into a [C, V] fp32 buffer
-//   2. row kernel on Z_c        loss rows + dZ_c (bf16), scaled by dloss/N with N
-//                               counted once over all T targets up front
+//   2. CE over Z_c's rows       the logits product also leaves each row's online
+//                               logsumexp partials, so one read of Z_c gives the loss
+//                               rows and dZ_c (bf16), scaled by dloss/N with N counted
+//                               once over all T targets up front
 //   3. dH_c = dZ_c (W^T)^T      bf16 MFMA (W^T made once per call), bf16 out
 //   4. dW (+)= dZ_c^T H_c       bf16 MFMA on transposed copies of dZ_c and H_c, fp32
 //                               accumulation across chunks in dW (or a workspace
@@ -29,9 +31,12 @@ constexpr int64_t kAutoChunk = 2048;
 
 struct Layout {
   int64_t C, Cpad, Vpad, ldz;
+  bool pair;      // dW over two chunks per product
+  int64_t nparts;  // logsumexp partials per logits row
+  int64_t Kbuf;   // row length of the transposed dW operands
   gemm::SplitPlan dh_split;  // split-K of the dH product (a full chunk)
   size_t off_cnt, off_loss, off_z, off_wt, off_zbuf, off_dz, off_dzt, off_hct, off_dw,
-      off_part, off_idx, off_pos, off_tgv, off_hv, off_dhv, total;
+      off_part, off_stats, off_idx, off_pos, off_tgv, off_hv, off_dhv, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
@@ -50,12 +55,18 @@ Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
   L.off_wt = take((size_t)H * L.Vpad * 2);
   L.off_zbuf = take((size_t)C * L.ldz * 4);
   L.off_dz = take((size_t)C * L.Vpad * 2);
-  L.off_dzt = take((size_t)V * L.Cpad * 2);
-  L.off_hct = take((size_t)H * L.Cpad * 2);
+  // dW products take two chunks at a time (K = 2C) when C is a multiple of 64, so
+  // the fp32 dW is read and rewritten half as often
+  L.pair = C % 64 == 0 && T > C;
+  L.Kbuf = L.pair ? 2 * C : L.Cpad;
+  L.off_dzt = take((size_t)V * L.Kbuf * 2);
+  L.off_hct = take((size_t)H * L.Kbuf * 2);
   L.off_dw = take(dw_dtype == FO_BF16 ? (size_t)V * H * 4 : 0);
   L.dh_split = gemm::split_plan(C, H, L.Vpad);
   L.off_part = take(L.dh_split.splits > 1 ? (size_t)L.dh_split.splits * C * H * 4 : 0);
   const size_t Tn = (size_t)(T > 0 ? T : 1);
+  L.nparts = ceil_div(V, gemm::kStatsCols);
+  L.off_stats = take((size_t)C * L.nparts * 8);
   L.off_idx = take(Tn * 4);
   L.off_pos = take(Tn * 4);
   L.off_tgv = take(Tn * 8);
@@ -110,6 +121,71 @@ __global__ __launch_bounds__(256) void scatter_rows(const bf16* __restrict__ dHv
         p >= 0 ? *reinterpret_cast<const u32x4*>(src + v * 8) : u32x4{0, 0, 0, 0};
 }
 
+// Cross-entropy of one chunk of logits Z (fp32, rows of stride ldz) whose per-row
+// online-logsumexp partials were produced by the logits product: merge the row's
+// partials (fixed order) into lse, write the row's loss, then one pass over the row
+// writes dZ = (dloss/N)(softmax (1 + 2 c lse) - onehot) in bf16.  Rows past the
+// chunk's valid count get zero dZ rows up to the next multiple of 64 (K padding of
+// the dW product).  One 256-thread workgroup per row.
+constexpr int kApplyThreads = 256;
+__global__ __launch_bounds__(kApplyThreads) void ce_apply(
+    const float* __restrict__ Z, int64_t ldz, const float2* __restrict__ stats, int64_t nparts,
+    const int64_t* __restrict__ tg, const xent::Counters* __restrict__ cnt, int64_t rows_base,
+    int64_t rows, int64_t V, float zc, float dloss, bf16* __restrict__ dZ, int64_t ldd,
+    float* __restrict__ row_loss, float* __restrict__ row_z) {
+  __shared__ float shm[kApplyThreads / kWave], shs[kApplyThreads / kWave];
+  const int64_t row = blockIdx.x;
+  int64_t eff = cnt->n_valid - rows_base;
+  eff = eff < 0 ? 0 : (eff > rows ? rows : eff);
+  if (row >= eff) {
+    if (dZ != nullptr && row < (eff + 63) / 64 * 64) {
+      bf16* dr = dZ + row * ldd;
+      for (int64_t e = threadIdx.x; e < V; e += kApplyThreads) dr[e] = from_f32<bf16>(0.f);
+    }
+    return;
+  }
+  float m = -INFINITY, s = 0.f;
+  const float2* sp = stats + row * nparts;
+  for (int64_t p = threadIdx.x; p < nparts; p += kApplyThreads) {
+    const float2 q = sp[p];
+    lse_merge(m, s, q.x, q.y);
+  }
+  const float lse = xent::block_lse<kApplyThreads>(m, s, shm, shs);
+  const float* zr = Z + row * ldz;
+  const long long y = tg[row];
+  if (threadIdx.x == 0) {
+    const float zt = zc * lse * lse;
+    row_loss[row] = (lse - zr[y]) + zt;
+    row_z[row] = zt;
+  }
+  if (dZ == nullptr) return;
+  const float scale = dloss / (float)cnt->n_valid;
+  const float coef = scale * fmaf(2.f * zc, lse, 1.f);
+  bf16* dr = dZ + row * ldd;
+  if (V % 4 == 0) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    for (int64_t v = threadIdx.x; v < V / 4; v += kApplyThreads) {
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      const f32x4 z4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(zr) + v);
+      const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
+      union { u32x2 raw; bf16 e[4]; } o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float g = coef * __expf(zz[j] - lse);
+        if (v * 4 + j == y) g -= scale;
+        o.e[j] = from_f32<bf16>(g);
+      }
+      *reinterpret_cast<u32x2*>(dr + v * 4) = o.raw;
+    }
+  } else {
+    for (int64_t v = threadIdx.x; v < V; v += kApplyThreads) {
+      float g = coef * __expf(zr[v] - lse);
+      if (v == y) g -= scale;
+      dr[v] = from_f32<bf16>(g);
+    }
+  }
+}
+
 #define FO_HIP(...)                                \
   do {                                             \
     if ((__VA_ARGS__) != hipSuccess) return FO_ERR_HIP; \
@@ -133,6 +209,7 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
   int64_t* tgv = reinterpret_cast<int64_t*>(ws + L.off_tgv);
   bf16* Hv = reinterpret_cast<bf16*>(ws + L.off_hv);
   bf16* dHv = reinterpret_cast<bf16*>(ws + L.off_dhv);
+  float2* stats = reinterpret_cast<float2*>(ws + L.off_stats);
   float* dW32 = dw_dtype == FO_BF16 ? reinterpret_cast<float*>(ws + L.off_dw)
                                     : static_cast<float*>(dW);
 
@@ -157,13 +234,13 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
       g.C = Z; g.ldc = L.ldz;
       g.M = cl; g.N = V; g.K = H;
       g.dev_count = nv; g.count_base = c0; g.dev_dim = 1;
-      FO_HIP(gemm::run<gemm::kStoreF32>(g, gemm::kWide, st));
-      // 2. loss rows and dZ
-      xent::RowArgs r;
-      r.T = cl; r.V = V; r.ldz = L.ldz; r.ldd = L.Vpad; r.ignore = ignore; r.zc = zc;
-      r.dloss = dloss; r.tg = tgv + c0; r.cnt = cnt; r.row_loss = row_loss + c0;
-      r.row_z = row_z + c0; r.dev_rows = nv; r.rows_base = c0;
-      FO_HIP(xent::launch_rows<float, bf16>(r, Z, need_grad ? dZ : nullptr, st));
+      g.stats = stats; g.stats_ld = L.nparts;
+      FO_HIP(gemm::run<gemm::kStoreF32Stats>(g, gemm::kWide, st));
+      // 2. loss rows and dZ from the row partials: one read of the logits
+      ce_apply<<<(unsigned)cl, kApplyThreads, 0, st>>>(
+          Z, L.ldz, stats, L.nparts, tgv + c0, cnt, c0, cl, V, zc, dloss,
+          need_grad ? dZ : nullptr, L.Vpad, row_loss + c0, row_z + c0);
+      FO_HIP(hipGetLastError());
       // 3. dH rows of the chunk (split over the vocabulary when a chunk's 256x256 tiles
       //    cannot fill the chip; the fp32 partials are summed in a fixed order)
       if (dH != nullptr) {
@@ -186,19 +263,26 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
           FO_HIP(gemm::run<gemm::kStoreBF16>(h, gemm::kNarrow, st));
         }
       }
-      // 4. dW contribution: K = the chunk's valid rows, rounded up to 64 (the rows
-      //    after the valid ones are zero in both transposed operands)
+      // 4. dW contribution.  The chunk's transposed operands go to slot 0 or 1 of the
+      //    K dimension; the product runs once both slots are filled (or at the end),
+      //    with K = the valid rows since the pair's start rounded up to 64 (the rows
+      //    after the valid ones are zero in both transposed operands).
       if (dW != nullptr) {
-        FO_HIP(gemm::transpose(dZ, L.Vpad, dZt, L.Cpad, cl, V, clp, st));
-        FO_HIP(gemm::transpose(Hv + c0 * H, H, Hct, L.Cpad, cl, H, clp, st));
-        gemm::Args w;
-        w.A = dZt; w.lda = L.Cpad;
-        w.B = Hct; w.ldb = L.Cpad;
-        w.C = dW32; w.ldc = H;
-        w.M = V; w.N = H; w.K = clp;
-        w.dev_count = nv; w.count_base = c0; w.dev_dim = 2;
-        if (c0 == 0) FO_HIP(gemm::run<gemm::kStoreF32>(w, gemm::kWide, st));
-        else FO_HIP(gemm::run<gemm::kAccumF32>(w, gemm::kWide, st));
+        const int64_t slot = L.pair ? (c0 / L.C) % 2 : 0;
+        const int64_t koff = slot * L.C;
+        FO_HIP(gemm::transpose(dZ, L.Vpad, dZt + koff, L.Kbuf, cl, V, clp, st));
+        FO_HIP(gemm::transpose(Hv + c0 * H, H, Hct + koff, L.Kbuf, cl, H, clp, st));
+        if (!L.pair || slot == 1 || c0 + L.C >= T) {
+          const int64_t base = c0 - koff;
+          gemm::Args w;
+          w.A = dZt; w.lda = L.Kbuf;
+          w.B = Hct; w.ldb = L.Kbuf;
+          w.C = dW32; w.ldc = H;
+          w.M = V; w.N = H; w.K = koff + clp;
+          w.dev_count = nv; w.count_base = base; w.dev_dim = 2;
+          if (base == 0) FO_HIP(gemm::run<gemm::kStoreF32>(w, gemm::kWide, st));
+          else FO_HIP(gemm::run<gemm::kAccumF32>(w, gemm::kWide, st));
+        }
       }
     }
     if (dH != nullptr) {

@@ -29,7 +29,9 @@ namespace {  // internal linkage: each including source file gets its own copy
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-enum OutMode { kStoreF32 = 0, kAccumF32 = 1, kStoreBF16 = 2 };
+// kStoreF32Stats: fp32 store plus, per row, the (max, sum of exp(x - max)) pair of each
+// wave's WN columns (an online-logsumexp partial) at stats[row * stats_ld + col / WN].
+enum OutMode { kStoreF32 = 0, kAccumF32 = 1, kStoreBF16 = 2, kStoreF32Stats = 3 };
 
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
@@ -52,6 +54,8 @@ struct Args {
   const long long* dev_count = nullptr;
   int64_t count_base = 0;
   int dev_dim = 0;
+  float2* stats = nullptr;  // kStoreF32Stats only
+  int64_t stats_ld = 0;
 };
 
 // The K slice of this workgroup row (split-K), applied to a copy of the arguments.
@@ -287,6 +291,39 @@ __device__ __forceinline__ void init_tile(const Args& a, f32x16 (&acc)[FM][FN], 
   }
 }
 
+// Row partials of an online logsumexp over this wave's WN columns (kStoreF32Stats).
+// Lane (fr, fh) holds, for each of its rows, the FN values at columns j*32 + fr; the
+// partial is folded over j in the lane, then over the 32 lanes of its half-wave
+// (butterfly; every lane ends with the same pair), and written by lane fr == 0.
+// Columns at or past N do not take part.
+template <int BM, int WM, int WN, int FM, int FN>
+__device__ __forceinline__ void row_stats(const Args& a, f32x16 (&acc)[FM][FN], int64_t m0,
+                                          int64_t n0, int wm, int wn, int fr, int fh) {
+  const int64_t nb = n0 + wn * WN;  // first column of this wave
+  const int64_t part = nb / WN;
+  if (nb >= a.N) return;  // no partial slot for a wave wholly past the last column
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float m = -INFINITY, s = 0.f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        if (nb + j * 32 + fr < a.N) m = fmaxf(m, acc[i][j][r]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        if (nb + j * 32 + fr < a.N) s += __expf(acc[i][j][r] - m);
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) {
+        const float m2 = __shfl_xor(m, o, 64);
+        const float s2 = __shfl_xor(s, o, 64);
+        lse_merge(m, s, m2, s2);
+      }
+      const int64_t row = m0 + wm * WM + i * 32 + 8 * (r / 4) + 4 * fh + (r % 4);
+      if (fr == 0 && row < a.M) a.stats[row * a.stats_ld + part] = make_float2(m, s);
+    }
+}
+
 // Epilogue: accumulator register r of block (i, j) holds C[8(r/4) + 4 fh + r%4][fr]
 // of the block.  Each group of 4 registers is 4 consecutive rows of one column, so a
 // row pointer is formed once per group; whole tiles skip the bounds tests.
@@ -460,7 +497,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_nt_dma(Args a_in) {
     if (kt + 1 < nk) step(sA1, sB1, sA0, sB0, kt + 1);
   }
 
-  store_tile<MODE, BM, BN, WM, WN, FM, FN>(a, acc, m0, n0, wm, wn, fr, fh);
+  if constexpr (MODE == kStoreF32Stats) row_stats<BM, WM, WN, FM, FN>(a, acc, m0, n0, wm, wn, fr, fh);
+  store_tile<MODE == kStoreF32Stats ? kStoreF32 : MODE, BM, BN, WM, WN, FM, FN>(a, acc, m0, n0, wm, wn, fr, fh);
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, int ST, int SH, int MODE>
@@ -499,13 +537,23 @@ inline bool dma_ok(const Args& a, int bm, int bn) {
 
 template <int MODE>
 hipError_t run(const Args& a, TileShape shape, hipStream_t st) {
-  if (shape == kWide) {
-    if (dma_ok(a, 256, 256)) return launch_dma<256, 256, 64, 4, 2, 2, 1, MODE>(a, st);
-    return launch_cfg<256, 256, 64, 4, 2, MODE>(a, st);
+  if constexpr (MODE == kStoreF32Stats) {
+    // the row partials come from the direct-to-LDS kernel's wide tile only (its waves
+    // cover kStatsCols columns each)
+    if (shape != kWide || !dma_ok(a, 256, 256)) return hipErrorInvalidValue;
+    return launch_dma<256, 256, 64, 4, 2, 2, 1, MODE>(a, st);
+  } else {
+    if (shape == kWide) {
+      if (dma_ok(a, 256, 256)) return launch_dma<256, 256, 64, 4, 2, 2, 1, MODE>(a, st);
+      return launch_cfg<256, 256, 64, 4, 2, MODE>(a, st);
+    }
+    if (dma_ok(a, 128, 128)) return launch_dma<128, 128, 64, 2, 2, 2, 1, MODE>(a, st);
+    return launch_cfg<128, 128, 64, 2, 2, MODE>(a, st);
   }
-  if (dma_ok(a, 128, 128)) return launch_dma<128, 128, 64, 2, 2, 2, 1, MODE>(a, st);
-  return launch_cfg<128, 128, 64, 2, 2, MODE>(a, st);
 }
+
+// columns per row partial of kStoreF32Stats (the wide tile's wave width)
+constexpr int kStatsCols = 128;
 
 // Split-K plan for a product whose 256x256 tiles cannot fill the chip: the number of
 // K slices (a multiple of the 64-deep K step each) and the partial buffer it needs.
