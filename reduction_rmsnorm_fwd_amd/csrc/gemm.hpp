@@ -292,9 +292,9 @@ __device__ __forceinline__ void init_tile(const Args& a, f32x16 (&acc)[FM][FN], 
 }
 
 // Row partials of an online logsumexp over this wave's WN columns (kStoreF32Stats).
-// Lane (fr, fh) holds, for each of its rows, the FN values at columns j*32 + fr; the
-// partial is folded over j in the lane, then over the 32 lanes of its half-wave
-// (butterfly; every lane ends with the same pair), and written by lane fr == 0.
+// Lane (fr, fh) holds, for each of its rows, the FN values at columns j*32 + fr.  The
+// row max is folded over j and over the 32 lanes of the half-wave (butterfly), then the
+// sum of exp(x - max) the same way; lane fr == 0 writes the pair.
 // Columns at or past N do not take part.
 template <int BM, int WM, int WN, int FM, int FN>
 __device__ __forceinline__ void row_stats(const Args& a, f32x16 (&acc)[FM][FN], int64_t m0,
@@ -306,19 +306,19 @@ __device__ __forceinline__ void row_stats(const Args& a, f32x16 (&acc)[FM][FN], 
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float m = -INFINITY, s = 0.f;
+      // the row's max over the wave's columns first (max only), then one exp per value
+      float m = -INFINITY;
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         if (nb + j * 32 + fr < a.N) m = fmaxf(m, acc[i][j][r]);
 #pragma unroll
+      for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      float s = 0.f;
+#pragma unroll
       for (int j = 0; j < FN; ++j)
         if (nb + j * 32 + fr < a.N) s += __expf(acc[i][j][r] - m);
 #pragma unroll
-      for (int o = 1; o < 32; o <<= 1) {
-        const float m2 = __shfl_xor(m, o, 64);
-        const float s2 = __shfl_xor(s, o, 64);
-        lse_merge(m, s, m2, s2);
-      }
+      for (int o = 1; o < 32; o <<= 1) s += __shfl_xor(s, o, 64);
       const int64_t row = m0 + wm * WM + i * 32 + 8 * (r / 4) + 4 * fh + (r % 4);
       if (fr == 0 && row < a.M) a.stats[row * a.stats_ld + part] = make_float2(m, s);
     }
