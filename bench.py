@@ -28,6 +28,35 @@ METRIC = "HBM GB/s & % of peak per fused op (fwd+bwd); xent/FLCE tokens/s"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
 FLUSH_BYTES = 1 << 30        # written between isolated calls: beyond L2 and the 256 MB MALL
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_step_llama3-8b.json")
+
+
+def sources_sha256():
+    """Hash of the kernel sources and the C ABI header (same recipe as the one stamped
+    into the counter summary when the FETCH_SIZE / WRITE_SIZE runs were taken)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join("reduction_rmsnorm_fwd_amd", "csrc")
+    files = sorted([os.path.join(csrc, f) for f in os.listdir(os.path.join(ROOT, csrc))]
+                   + [os.path.join("include", "fo.h")])
+    for f in files:
+        h.update(f.encode())
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Per-op HBM bytes per call from the committed counter runs, or None when the
+    kernels have changed since those counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256") != sources_sha256():
+        return None
+    return {k: v["traffic_bytes"] for k, v in t.get("per_op", {}).items()}
 
 
 def parse():
@@ -202,6 +231,7 @@ def gpu_bench(args):
         v = sorted(v)
         return v[len(v) // 2]
 
+    traffic = measured_traffic()
     per_op = {}
     for i, (name, _, work, bound) in enumerate(wl.ops):
         ms = sum(in_step[i]) / len(in_step[i])
@@ -223,6 +253,7 @@ def gpu_bench(args):
             e["tokens_per_s"] = round(wl.T / (t_ref * 1e-3), 1)
         if name == "xent_fwd_bwd":
             e["tokens_per_s"] = round(wl.T / (t_ref * 1e-3), 1)
+        e["traffic_MB"] = round(traffic[name] / 1e6, 1) if traffic and name in traffic else None
         per_op[name] = e
 
     ms_step = wall / args.steps * 1e3
@@ -257,18 +288,21 @@ def gpu_bench(args):
         work = wl.ops[i][2]
         ach = work / (ms * 1e-3) / 1e12
         out["roofline"] = {
-            "kernel": "fo_flce_fwd_bwd (per call: gemm_nt x3 per 2048-token chunk, cross-entropy "
-                      "row kernel, transposes)",
+            "kernel": "fo_flce_fwd_bwd (per call: per 2048-row chunk the logits and split-K dH "
+                      "bf16 MFMA products, ce_apply, two transposes; the dW product per "
+                      "chunk pair; W transpose, compaction, gather/scatter)",
             "bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic.get("flce_fwd_bwd") if traffic else None,
+            "traffic_unit": "bytes per launch",
             "ms_per_launch": round(ms, 4),
         }
     return out, wl
 
 
 def cpu_baseline():
-    """The fp64 oracle, as it stands, on a bounded sample of the same step: 128 of the
-    8192 tokens for every layer op and 32 tokens for the lm head; times are scaled up
+    """The fp64 oracle, as it stands, on a bounded sample of the same step: 4096 of the
+    8192 tokens for every layer op and 2048 tokens for the lm head; times are scaled up
     linearly in tokens (every op is per-token) to the step's 8192 tokens."""
     import numpy as np
     import torch
@@ -280,7 +314,7 @@ def cpu_baseline():
     except Exception:  # noqa: BLE001
         blas_threads = os.cpu_count() or 1
     c3, c5 = synth.CONFIGS[3], synth.CONFIGS[5]
-    n_layer, n_head = 128, 32
+    n_layer, n_head = 4096, 2048
     s3 = synth.scaled(c3, n_layer)
     t = {}
     r = synth.rmsnorm_inputs(s3)
