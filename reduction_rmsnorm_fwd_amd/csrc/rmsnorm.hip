@@ -12,7 +12,7 @@
 // row RW waves (RW grows with d so a lane holds at most 16 elements per operand); every
 // lane owns a fixed set of columns and accumulates their dw contribution in registers
 // across all the rows its workgroup visits.  The waves of a workgroup are folded
-// through LDS in a fixed order into one fp32 partial row per workgroup (at most 256
+// through LDS in a fixed order into one fp32 partial row per workgroup (at most 512
 // workgroups, so the partials stay a few MB), and a second small kernel sums the
 // partial rows in a fixed order.  Any other shape takes a workgroup-per-row path that
 // reads the row twice (the second read from L2).
@@ -24,8 +24,8 @@ namespace fo {
 namespace {
 
 constexpr int kFwdWaves = 4;     // rows (waves) per workgroup, forward
-constexpr int kBwdWaves = 16;    // waves per workgroup, backward
-constexpr int kMaxPartials = 256;  // dw partial rows (workgroups of the backward)
+constexpr int kBwdWaves = 8;     // waves per workgroup, backward
+constexpr int kMaxPartials = 512;  // dw partial rows (workgroups of the backward)
 constexpr int kGenericThreads = 256;
 
 // ----------------------------------------------------------------- forward, fast
@@ -113,10 +113,12 @@ __global__ __launch_bounds__(kGenericThreads) void rmsnorm_fwd_block(
 // A workgroup of kBwdWaves waves works on kBwdWaves/RW rows at a time, RW waves per
 // row; lane (w, l) of a row owns the vectors (w*64 + l) + i*RW*64, i < NV, and keeps
 // its columns' dw contribution in registers across all rows the workgroup visits.
-// The per-row dot products are combined across the RW waves through LDS (every wave
-// runs the same number of row rounds, so the barriers match).  At the end the waves'
-// column partials are folded through LDS in a fixed order into one fp32 partial row
-// per workgroup: partial[blockIdx.x, :].
+// With RW > 1 the per-row dot products are combined across the RW waves through LDS
+// (every wave runs the same number of row rounds, so the barriers match).  The next
+// round's rows (and their saved 1/rms) are loaded before the current round is reduced,
+// so a round's cross-wave barrier never leaves the memory pipe empty.  At the end the
+// waves' column partials are folded through LDS in a fixed order into one fp32 partial
+// row per workgroup: partial[blockIdx.x, :].
 template <typename T, int NV, int RW>
 __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
     int64_t T_, int nvec, int d, const T* dy, int64_t lddy, const T* x, int64_t ldx,
@@ -143,12 +145,12 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
   const float inv_d = 1.0f / (float)d;
   const int64_t stride = (int64_t)gridDim.x * RG;
   const int64_t rounds = ceil_div(T_ - (int64_t)blockIdx.x * RG, stride);
-  // The next round's rows are loaded before the current round is reduced, so a
-  // round's cross-wave barrier never leaves the memory pipe empty.
   Pack<T> gv[NV], xv[NV], gn[NV], xn[NV];
-  auto load_round = [&](int64_t rd, Pack<T>* g, Pack<T>* xx) {
+  float rv = 0.f, rn = 0.f;  // the saved 1/rms of the row (loaded with the row)
+  auto load_round = [&](int64_t rd, Pack<T>* g, Pack<T>* xx, float& r) {
     const int64_t row = (int64_t)blockIdx.x * RG + rg + rd * stride;
     const bool live = rd < rounds && row < T_;
+    if (rstd != nullptr && live) r = rstd[row];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int v = vbase + i * RW * kWave;
@@ -161,11 +163,11 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
       }
     }
   };
-  load_round(0, gv, xv);
+  load_round(0, gv, xv, rv);
   for (int64_t rd = 0; rd < rounds; ++rd) {
     const int64_t row = (int64_t)blockIdx.x * RG + rg + rd * stride;
     const bool live = row < T_;
-    load_round(rd + 1, gn, xn);
+    load_round(rd + 1, gn, xn, rn);
     float dot = 0.f, ss = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
       __syncthreads();  // slots are rewritten next round
     }
     if (live) {
-      const float r = rstd != nullptr ? rstd[row] : 1.0f / sqrtf(ss * inv_d + eps);
+      const float r = rstd != nullptr ? rv : 1.0f / sqrtf(ss * inv_d + eps);
       const float k = r * r * r * (dot * inv_d);
       T* dxr = dx + row * lddx;
 #pragma unroll
@@ -214,6 +216,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
       gv[i] = gn[i];
       xv[i] = xn[i];
     }
+    rv = rn;
   }
   // fold the row groups' column partials in order 0,1,2,... (RW waves of a group own
   // disjoint columns, so they write their slots in the same step)
@@ -289,28 +292,50 @@ __global__ __launch_bounds__(256) void rmsnorm_dw_partial_block(
   partial[g * d + j] = acc;
 }
 
-// dw[j] = sum_g partial[g, j]: 16 row phases per column (phase p sums its rows in
-// order), then the 16 phase sums in order p = 0..15.  A workgroup covers 64 columns.
-__global__ __launch_bounds__(1024) void rmsnorm_dw_reduce(int64_t G, int64_t d,
-                                                         const float* __restrict__ partial,
-                                                         float* __restrict__ dw) {
-  __shared__ float sh[16][64];
-  const int c = threadIdx.x & 63;
-  const int ph = threadIdx.x >> 6;
-  const int64_t j = (int64_t)blockIdx.x * 64 + c;
-  const int64_t per = (G + 15) / 16;
+// dw[j] = sum_g partial[g, j].  A workgroup covers 16 columns as 4 float4 lanes; its
+// 64 row phases each sum a contiguous block of partial rows in order (the loads of up
+// to 8 rows issued before the first add), then 16 threads add the 64 phase sums in
+// order 0..63.  The many small workgroups keep every CU loading.
+constexpr int kReducePhases = 64;
+constexpr int kReduceCols = 16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void rmsnorm_dw_reduce(int64_t G, int64_t d,
+                                                        const float* __restrict__ partial,
+                                                        float* __restrict__ dw) {
+  __shared__ float sh[kReducePhases][kReduceCols + 1];
+  const int q = threadIdx.x & 3;  // column quad
+  const int ph = threadIdx.x >> 2;
+  const int64_t j = (int64_t)blockIdx.x * kReduceCols + q * 4;
+  const int64_t per = (G + kReducePhases - 1) / kReducePhases;
   const int64_t g0 = ph * per;
   const int64_t g1 = (g0 + per < G) ? g0 + per : G;
-  float acc = 0.f;
-  if (j < d)
-    for (int64_t g = g0; g < g1; ++g) acc += partial[g * d + j];
-  sh[ph][c] = acc;
-  __syncthreads();
-  if (ph == 0 && j < d) {
-    float t = sh[0][c];
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+  if (j + 3 < d && d % 4 == 0 && (reinterpret_cast<uintptr_t>(partial) & 15) == 0) {
+    for (int64_t g = g0; g < g1; g += 8) {
+      f32x4 v[8];
 #pragma unroll
-    for (int p = 1; p < 16; ++p) t += sh[p][c];
-    dw[j] = t;
+      for (int u = 0; u < 8; ++u)
+        if (g + u < g1) v[u] = *reinterpret_cast<const f32x4*>(partial + (g + u) * d + j);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (g + u < g1)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) a[c] += v[u][c];
+    }
+  } else {
+    for (int64_t g = g0; g < g1; ++g)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (j + c < d) a[c] += partial[g * d + j + c];
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) sh[ph][q * 4 + c] = a[c];
+  __syncthreads();
+  if (threadIdx.x < kReduceCols) {
+    const int64_t jc = (int64_t)blockIdx.x * kReduceCols + threadIdx.x;
+    float t = sh[0][threadIdx.x];
+    for (int p = 1; p < kReducePhases; ++p) t += sh[p][threadIdx.x];
+    if (jc < d) dw[jc] = t;
   }
 }
 
@@ -364,6 +389,36 @@ int fwd_impl(int64_t T_, int64_t d, const void* x, int64_t ldx, const void* w, f
 // Upper bound of the dw partial rows of either backward path (workspace sizing).
 int64_t bwd_groups(int64_t T_) { return T_ < kMaxPartials ? T_ : kMaxPartials; }
 
+// Launch plan of the fast backward: waves per row (rw), vectors per lane and operand
+// (nv), and the workgroup count (= dw partial rows).
+struct BwdPlan {
+  int rw, nv;
+  int64_t groups;
+};
+
+template <typename T>
+BwdPlan bwd_plan(int64_t T_, int nvec) {
+  // fewest waves per row that keep each lane at <= 16 elements per operand
+  constexpr int kMaxNV = 16 / Vec<T>::N;
+  BwdPlan p{1, 1, 0};
+  while (p.rw < kBwdWaves && ceil_div(nvec, (int64_t)p.rw * kWave) > kMaxNV) p.rw *= 2;
+  const int64_t per = ceil_div(nvec, (int64_t)p.rw * kWave);
+  p.nv = per <= 1 ? 1 : per <= 2 ? 2 : kMaxNV;
+  const int64_t rows_in_flight = kBwdWaves / p.rw;
+  p.groups = ceil_div(T_, rows_in_flight);
+  if (p.groups > kMaxPartials) p.groups = kMaxPartials;
+  return p;
+}
+
+template <typename T, int NV, int RW>
+void launch_bwd(const BwdPlan& p, int64_t T_, int nvec, int d, const T* dy, int64_t lddy,
+                const T* x, int64_t ldx, const T* w, const float* rstd, float eps, T* dx,
+                int64_t lddx, float* partial, hipStream_t st) {
+  rmsnorm_bwd_wave<T, NV, RW>
+      <<<dim3((unsigned)p.groups), dim3(kBwdWaves * kWave), (size_t)d * sizeof(float), st>>>(
+          T_, nvec, d, dy, lddy, x, ldx, w, rstd, eps, dx, lddx, partial);
+}
+
 template <typename T>
 int bwd_impl(int64_t T_, int64_t d, const void* dy, int64_t lddy, const void* x,
              int64_t ldx, const void* w, const float* rstd, float eps, void* dx,
@@ -376,32 +431,23 @@ int bwd_impl(int64_t T_, int64_t d, const void* dy, int64_t lddy, const void* x,
   int64_t G;
   if (vector_ok<T>(d, dy, lddy, x, ldx, dx, lddx, w)) {
     const int nvec = (int)(d / Vec<T>::N);
-    // fewest waves per row that keep each lane at <= 16 elements per operand
+    const BwdPlan p = bwd_plan<T>(T_, nvec);
+    G = p.groups;
     constexpr int kMaxNV = 16 / Vec<T>::N;
-    int rw = 1;
-    while (rw < kBwdWaves && ceil_div(nvec, (int64_t)rw * kWave) > kMaxNV) rw *= 2;
-    const int64_t per = ceil_div(nvec, (int64_t)rw * kWave);
-    const int nv = per <= 1 ? 1 : per <= 2 ? 2 : 4;
-    const int64_t rows_in_flight = kBwdWaves / rw;
-    G = ceil_div(T_, rows_in_flight);
-    if (G > kMaxPartials) G = kMaxPartials;
-    const dim3 grid((unsigned)G), block(kBwdWaves * kWave);
-    const size_t lds = (size_t)d * sizeof(float);
     auto go = [&](auto nv_c, auto rw_c) {
-      rmsnorm_bwd_wave<T, decltype(nv_c)::value, decltype(rw_c)::value><<<grid, block, lds, st>>>(
-          T_, nvec, (int)d, dyp, lddy, xp, ldx, wp, rstd, eps, dxp, lddx, partial);
+      launch_bwd<T, decltype(nv_c)::value, decltype(rw_c)::value>(
+          p, T_, nvec, (int)d, dyp, lddy, xp, ldx, wp, rstd, eps, dxp, lddx, partial, st);
     };
     auto go_rw = [&](auto rw_c) {
-      if (nv == 1) go(std::integral_constant<int, 1>{}, rw_c);
-      else if (nv == 2 || kMaxNV == 2) go(std::integral_constant<int, 2>{}, rw_c);
+      if (p.nv == 1) go(std::integral_constant<int, 1>{}, rw_c);
+      else if (p.nv == 2 || kMaxNV == 2) go(std::integral_constant<int, 2>{}, rw_c);
       else go(std::integral_constant<int, kMaxNV>{}, rw_c);
     };
-    switch (rw) {
+    switch (p.rw) {
       case 1: go_rw(std::integral_constant<int, 1>{}); break;
       case 2: go_rw(std::integral_constant<int, 2>{}); break;
       case 4: go_rw(std::integral_constant<int, 4>{}); break;
-      case 8: go_rw(std::integral_constant<int, 8>{}); break;
-      default: go_rw(std::integral_constant<int, 16>{}); break;
+      default: go_rw(std::integral_constant<int, 8>{}); break;
     }
   } else {
     // r[t] after the partials in the workspace
@@ -414,7 +460,7 @@ int bwd_impl(int64_t T_, int64_t d, const void* dy, int64_t lddy, const void* x,
     rmsnorm_dw_partial_block<T><<<dim3((unsigned)ceil_div(d, 256), (unsigned)G), dim3(256), 0, st>>>(
         T_, d, dyp, lddy, xp, ldx, r, rows_per_group, partial);
   }
-  rmsnorm_dw_reduce<<<dim3((unsigned)ceil_div(d, 64)), dim3(1024), 0, st>>>(G, d, partial, dw);
+  rmsnorm_dw_reduce<<<dim3((unsigned)ceil_div(d, kReduceCols)), dim3(256), 0, st>>>(G, d, partial, dw);
   return launch_status();
 }
 

@@ -12,10 +12,11 @@
 // host-computed fp64 frequency, range-reduced against 2*pi in fp64, and only the
 // reduced angle (|r| <= pi) is rounded to fp32 for sincosf.  That keeps the angle
 // error near 1e-7 rad at any position, where an fp32 product would be off by 1e-3 rad
-// at position 16383.  Then the workgroup streams every head of Q and K of its tokens:
-// a unit is one 16-byte vector of the low half and the matching vector of the high
-// half of one head, read once and written once.  A token at position 0 is the
-// identity rotation: it is skipped (neither read nor written), so its data stays
+// at position 16383.  The workgroup streams every head of Q and K of its tokens: a
+// unit is one 16-byte vector of the low half and the matching vector of the high half
+// of one head, read once and written once; the first units' loads are issued before
+// the table is built, so the table's fp64 work hides under their latency.  A token at
+// position 0 is the identity rotation: it is not written, so its data stays
 // bit-identical, signed zeros included.
 #include "fo_common.hpp"
 
@@ -55,16 +56,6 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(
   const int P = D / 2;
   const int64_t t0 = (int64_t)blockIdx.x * tok;
   const int ntok = (T_ - t0 < tok) ? (int)(T_ - t0) : tok;
-  if (threadIdx.x < ntok) ident[threadIdx.x] = pos[t0 + threadIdx.x] == 0;
-  for (int u = threadIdx.x; u < ntok * P; u += kThreads) {
-    const int tl = u / P, i = u - tl * P;
-    const double a = (double)pos[t0 + tl] * fr.f[i];
-    float c, s;
-    rope_cs(a, c, s);
-    cs[tl][i][0] = c;
-    cs[tl][i][1] = sgn * s;
-  }
-  __syncthreads();
   const int PV = P / VEC;  // vectors per half head
   const int per_tok = (nq + nkv) * PV;
   const int nunits = ntok * per_tok;
@@ -81,25 +72,36 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(
         const int rem = u - tl * per_tok;
         const int h = rem / PV;
         const int pv = rem - h * PV;
-        if (!ident[tl]) {
-          const int64_t t = t0 + tl;
-          T* base = (h < nq) ? q + t * ldq + (int64_t)h * D : k + t * ldk + (int64_t)(h - nq) * D;
-          lo[m] = base + pv * VEC;
-          tlu[m] = tl;
-          pvu[m] = pv;
-          if constexpr (VEC > 1) {
-            a[m] = load_pack(lo[m]);
-            b[m] = load_pack(lo[m] + P);
-          } else {
-            a[m].v[0] = lo[m][0];
-            b[m].v[0] = lo[m][P];
-          }
+        const int64_t t = t0 + tl;
+        T* base = (h < nq) ? q + t * ldq + (int64_t)h * D : k + t * ldk + (int64_t)(h - nq) * D;
+        lo[m] = base + pv * VEC;
+        tlu[m] = tl;
+        pvu[m] = pv;
+        if constexpr (VEC > 1) {
+          a[m] = load_pack(lo[m]);
+          b[m] = load_pack(lo[m] + P);
+        } else {
+          a[m].v[0] = lo[m][0];
+          b[m].v[0] = lo[m][P];
         }
       }
     }
+    if (ub == 0) {
+      // the table is built while the first loads are in flight
+      if (threadIdx.x < ntok) ident[threadIdx.x] = pos[t0 + threadIdx.x] == 0;
+      for (int u = threadIdx.x; u < ntok * P; u += kThreads) {
+        const int tl = u / P, i = u - tl * P;
+        const double ang = (double)pos[t0 + tl] * fr.f[i];
+        float c, sn;
+        rope_cs(ang, c, sn);
+        cs[tl][i][0] = c;
+        cs[tl][i][1] = sgn * sn;
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int m = 0; m < kMaxU; ++m) {
-      if (lo[m] == nullptr) continue;
+      if (lo[m] == nullptr || ident[tlu[m]]) continue;  // position 0: left untouched
       Pack<T> oa, ob;
 #pragma unroll
       for (int j = 0; j < VEC; ++j) {
