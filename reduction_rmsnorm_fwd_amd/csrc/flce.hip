@@ -12,10 +12,15 @@
 //                               logsumexp partials, so one read of Z_c gives the loss
 //                               rows and dZ_c (bf16), scaled by dloss/N with N counted
 //                               once over all T targets up front
-//   3. dH_c = dZ_c (W^T)^T      bf16 MFMA (W^T made once per call), bf16 out
-//   4. dW (+)= dZ_c^T H_c       bf16 MFMA on transposed copies of dZ_c and H_c, fp32
-//                               accumulation across chunks in dW (or a workspace
-//                               buffer, cast to bf16 once at the end)
+//   3. dH_c = dZ_c W            bf16 MFMA reading W as it is stored ([V, H]: k-major
+//                               for this product), bf16 out
+//   4. dW (+)= dZ_c^T H_c       bf16 MFMA reading dZ_c and H_c as stored (token-major:
+//                               k-major for this product), fp32 accumulation across
+//                               chunks in dW (or a workspace buffer, cast to bf16 once
+//                               at the end); two chunks per product when there are
+//                               several, so dW is read and rewritten half as often
+// The k-major operands go through LDS untransposed and are read with the transposing
+// LDS loads of gfx950, so no operand is ever transposed in memory.
 // Rows whose target is ignored (or out of range) contribute nothing, so the valid rows
 // are compacted first (one scan kernel; their hidden states gathered into a workspace
 // copy) and the chunks run over valid rows only; row and K extents of the last chunk
@@ -30,13 +35,13 @@ namespace {
 constexpr int64_t kAutoChunk = 2048;
 
 struct Layout {
-  int64_t C, Cpad, Vpad, ldz;
-  bool pair;      // dW over two chunks per product
-  int64_t nparts;  // logsumexp partials per logits row
-  int64_t Kbuf;   // row length of the transposed dW operands
-  gemm::SplitPlan dh_split;  // split-K of the dH product (a full chunk)
-  size_t off_cnt, off_loss, off_z, off_wt, off_zbuf, off_dz, off_dzt, off_hct, off_dw,
-      off_part, off_stats, off_idx, off_pos, off_tgv, off_hv, off_dhv, total;
+  int64_t C, Vpad, ldz;
+  bool pair;        // dW over two chunks per product
+  int64_t dzrows;   // rows of the dZ buffer (one chunk, or two when paired)
+  int64_t nparts;   // logsumexp partials per logits row
+  int64_t dh_smax;  // split-K slice bound of the dH product (1: no split)
+  size_t off_cnt, off_loss, off_z, off_zbuf, off_dz, off_dw, off_part, off_stats, off_idx,
+      off_pos, off_tgv, off_hv, off_dhv, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
@@ -44,26 +49,26 @@ Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
   int64_t C = chunk > 0 ? chunk : kAutoChunk;
   if (C > T) C = T > 0 ? T : 1;
   L.C = C;
-  L.Cpad = align_up((size_t)C, 8);
   L.Vpad = align_up((size_t)V, 64);
   L.ldz = L.Vpad;
+  L.pair = T > C;
+  L.dzrows = L.pair ? 2 * C : C;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
   L.off_cnt = take(256);
   L.off_loss = take((size_t)(T > 0 ? T : 1) * 4);
   L.off_z = take((size_t)(T > 0 ? T : 1) * 4);
-  L.off_wt = take((size_t)H * L.Vpad * 2);
   L.off_zbuf = take((size_t)C * L.ldz * 4);
-  L.off_dz = take((size_t)C * L.Vpad * 2);
-  // dW products take two chunks at a time (K = 2C) when C is a multiple of 64, so
-  // the fp32 dW is read and rewritten half as often
-  L.pair = C % 64 == 0 && T > C;
-  L.Kbuf = L.pair ? 2 * C : L.Cpad;
-  L.off_dzt = take((size_t)V * L.Kbuf * 2);
-  L.off_hct = take((size_t)H * L.Kbuf * 2);
+  L.off_dz = take((size_t)L.dzrows * L.Vpad * 2);
   L.off_dw = take(dw_dtype == FO_BF16 ? (size_t)V * H * 4 : 0);
-  L.dh_split = gemm::split_plan(C, H, L.Vpad);
-  L.off_part = take(L.dh_split.splits > 1 ? (size_t)L.dh_split.splits * C * H * 4 : 0);
+  // dH of a chunk has few 256x256 tiles: split it over the vocabulary, the slice count
+  // chosen on the device from the chunk's valid rows (at most 8, each >= 2048 deep)
+  L.dh_smax = 1;
+  if (gemm::split_plan(C, H, L.Vpad).splits > 1) {
+    L.dh_smax = L.Vpad / 2048 < 8 ? L.Vpad / 2048 : 8;
+    if (L.dh_smax < 1) L.dh_smax = 1;
+  }
+  L.off_part = take(L.dh_smax > 1 ? (size_t)L.dh_smax * C * H * 4 : 0);
   const size_t Tn = (size_t)(T > 0 ? T : 1);
   L.nparts = ceil_div(V, gemm::kStatsCols);
   L.off_stats = take((size_t)C * L.nparts * 8);
@@ -74,12 +79,6 @@ Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
   L.off_dhv = take(Tn * H * 2);
   L.total = o;
   return L;
-}
-
-__global__ void fill_bf16_zero(bf16* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = from_f32<bf16>(0.f);
 }
 
 __global__ void fill_f32_zero(float* p, int64_t n) {
@@ -124,9 +123,10 @@ __global__ __launch_bounds__(256) void scatter_rows(const bf16* __restrict__ dHv
 // Cross-entropy of one chunk of logits Z (fp32, rows of stride ldz) whose per-row
 // online-logsumexp partials were produced by the logits product: merge the row's
 // partials (fixed order) into lse, write the row's loss, then one pass over the row
-// writes dZ = (dloss/N)(softmax (1 + 2 c lse) - onehot) in bf16.  Rows past the
-// chunk's valid count get zero dZ rows up to the next multiple of 64 (K padding of
-// the dW product).  One 256-thread workgroup per row.
+// writes dZ = (dloss/N)(softmax (1 + 2 c lse) - onehot) in bf16, and zeros in the
+// row's padding columns [V, ldd) (the K tail of the dH product).  Rows past the
+// chunk's valid count are never read by the products and are left alone.  One
+// 256-thread workgroup per row.
 constexpr int kApplyThreads = 256;
 __global__ __launch_bounds__(kApplyThreads) void ce_apply(
     const float* __restrict__ Z, int64_t ldz, const float2* __restrict__ stats, int64_t nparts,
@@ -137,13 +137,7 @@ __global__ __launch_bounds__(kApplyThreads) void ce_apply(
   const int64_t row = blockIdx.x;
   int64_t eff = cnt->n_valid - rows_base;
   eff = eff < 0 ? 0 : (eff > rows ? rows : eff);
-  if (row >= eff) {
-    if (dZ != nullptr && row < (eff + 63) / 64 * 64) {
-      bf16* dr = dZ + row * ldd;
-      for (int64_t e = threadIdx.x; e < V; e += kApplyThreads) dr[e] = from_f32<bf16>(0.f);
-    }
-    return;
-  }
+  if (row >= eff) return;
   float m = -INFINITY, s = 0.f;
   const float2* sp = stats + row * nparts;
   for (int64_t p = threadIdx.x; p < nparts; p += kApplyThreads) {
@@ -184,6 +178,7 @@ __global__ __launch_bounds__(kApplyThreads) void ce_apply(
       dr[v] = from_f32<bf16>(g);
     }
   }
+  for (int64_t v = V + threadIdx.x; v < ldd; v += kApplyThreads) dr[v] = from_f32<bf16>(0.f);
 }
 
 #define FO_HIP(...)                                \
@@ -199,11 +194,8 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
   const long long* nv = &cnt->n_valid;
   float* row_loss = reinterpret_cast<float*>(ws + L.off_loss);
   float* row_z = reinterpret_cast<float*>(ws + L.off_z);
-  bf16* Wt = reinterpret_cast<bf16*>(ws + L.off_wt);
   float* Z = reinterpret_cast<float*>(ws + L.off_zbuf);
-  bf16* dZ = reinterpret_cast<bf16*>(ws + L.off_dz);
-  bf16* dZt = reinterpret_cast<bf16*>(ws + L.off_dzt);
-  bf16* Hct = reinterpret_cast<bf16*>(ws + L.off_hct);
+  bf16* dZbuf = reinterpret_cast<bf16*>(ws + L.off_dz);
   int* idx = reinterpret_cast<int*>(ws + L.off_idx);
   int* pos_of = reinterpret_cast<int*>(ws + L.off_pos);
   int64_t* tgv = reinterpret_cast<int64_t*>(ws + L.off_tgv);
@@ -217,16 +209,14 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
     xent::compact_targets<<<1, 1024, 0, st>>>(T, V, tg, ignore, cnt, idx, pos_of, tgv);
     gather_rows<<<(unsigned)T, 256, 0, st>>>(Hm, H, idx, cnt, Hv);
     FO_HIP(hipGetLastError());
-    if (dH != nullptr) {
-      FO_HIP(gemm::transpose(W, H, Wt, L.Vpad, V, H, L.Vpad, st));
-      // columns [V, Vpad) of dZ are the zero K-padding of the dH contraction
-      fill_bf16_zero<<<1024, 256, 0, st>>>(dZ, L.C * L.Vpad);
-      FO_HIP(hipGetLastError());
-    }
     const bool need_grad = dH != nullptr || dW != nullptr;
     for (int64_t c0 = 0; c0 < T; c0 += L.C) {
       const int64_t cl = (T - c0 < L.C) ? T - c0 : L.C;  // rows at most (valid rows: on device)
-      const int64_t clp = align_up((size_t)cl, 8);
+      // a pair of chunks shares the dZ buffer: chunk 0 of the pair in rows [0, C),
+      // chunk 1 in rows [C, 2C), so the pair's dZ rows are contiguous for dW
+      const int64_t slot = L.pair ? (c0 / L.C) % 2 : 0;
+      const int64_t koff = slot * L.C;
+      bf16* dZ = dZbuf + koff * L.Vpad;
       // 1. logits of the chunk's valid rows
       gemm::Args g;
       g.A = Hv + c0 * H; g.lda = H;
@@ -241,48 +231,43 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
           Z, L.ldz, stats, L.nparts, tgv + c0, cnt, c0, cl, V, zc, dloss,
           need_grad ? dZ : nullptr, L.Vpad, row_loss + c0, row_z + c0);
       FO_HIP(hipGetLastError());
-      // 3. dH rows of the chunk (split over the vocabulary when a chunk's 256x256 tiles
-      //    cannot fill the chip; the fp32 partials are summed in a fixed order)
+      // 3. dH rows of the chunk: dZ_c [cl, Vpad] times W read k-major ([V, H]; its rows
+      //    past V read as zeros against dZ's zero padding columns).  Split over the
+      //    vocabulary when the chunk's 256x256 tiles cannot fill the chip; the fp32
+      //    partials are summed in a fixed order.
       if (dH != nullptr) {
         gemm::Args h;
         h.A = dZ; h.lda = L.Vpad;
-        h.B = Wt; h.ldb = L.Vpad;
+        h.B = W; h.ldb = H; h.b_rows = V;
         h.M = cl; h.N = H; h.K = L.Vpad;
         h.dev_count = nv; h.count_base = c0; h.dev_dim = 1;
-        const gemm::SplitPlan sp = gemm::split_plan(cl, H, L.Vpad);
-        if (sp.splits > 1 && sp.splits <= L.dh_split.splits) {
+        if (L.dh_smax > 1) {
           float* part = reinterpret_cast<float*>(ws + L.off_part);
           h.C = part; h.ldc = H;
-          h.k_split = sp.k_split; h.c_split = cl * H;
-          FO_HIP(gemm::run<gemm::kStoreF32>(h, gemm::kWide, st));
-          gemm::reduce_splits_bf16<<<2048, 256, 0, st>>>(part, sp.splits, cl * H, H,
-                                                         dHv + c0 * H, H, nv, c0);
+          h.split_max = L.dh_smax; h.c_split = cl * H;
+          FO_HIP((gemm::run<gemm::kStoreF32, false, true>(h, gemm::kWide, st)));
+          gemm::reduce_splits_bf16<<<2048, 256, 0, st>>>(part, L.dh_smax, cl * H, H,
+                                                         dHv + c0 * H, H, nv, c0, L.Vpad,
+                                                         L.dh_smax);
           FO_HIP(hipGetLastError());
         } else {
           h.C = dHv + c0 * H; h.ldc = H;
-          FO_HIP(gemm::run<gemm::kStoreBF16>(h, gemm::kNarrow, st));
+          FO_HIP((gemm::run<gemm::kStoreBF16, false, true>(h, gemm::kNarrow, st)));
         }
       }
-      // 4. dW contribution.  The chunk's transposed operands go to slot 0 or 1 of the
-      //    K dimension; the product runs once both slots are filled (or at the end),
-      //    with K = the valid rows since the pair's start rounded up to 64 (the rows
-      //    after the valid ones are zero in both transposed operands).
-      if (dW != nullptr) {
-        const int64_t slot = L.pair ? (c0 / L.C) % 2 : 0;
-        const int64_t koff = slot * L.C;
-        FO_HIP(gemm::transpose(dZ, L.Vpad, dZt + koff, L.Kbuf, cl, V, clp, st));
-        FO_HIP(gemm::transpose(Hv + c0 * H, H, Hct + koff, L.Kbuf, cl, H, clp, st));
-        if (!L.pair || slot == 1 || c0 + L.C >= T) {
-          const int64_t base = c0 - koff;
-          gemm::Args w;
-          w.A = dZt; w.lda = L.Kbuf;
-          w.B = Hct; w.ldb = L.Kbuf;
-          w.C = dW32; w.ldc = H;
-          w.M = V; w.N = H; w.K = koff + clp;
-          w.dev_count = nv; w.count_base = base; w.dev_dim = 2;
-          if (base == 0) FO_HIP(gemm::run<gemm::kStoreF32>(w, gemm::kWide, st));
-          else FO_HIP(gemm::run<gemm::kAccumF32>(w, gemm::kWide, st));
-        }
+      // 4. dW contribution of the pair's rows, once both chunks of a pair are in (or at
+      //    the end): dZ^T Hv with both operands read k-major (token-major as stored),
+      //    K = the valid rows since the pair's first row, read on the device.
+      if (dW != nullptr && (!L.pair || slot == 1 || c0 + L.C >= T)) {
+        const int64_t base = c0 - koff;
+        gemm::Args w;
+        w.A = dZbuf; w.lda = L.Vpad;
+        w.B = Hv + base * H; w.ldb = H;
+        w.C = dW32; w.ldc = H;
+        w.M = V; w.N = H; w.K = koff + cl;
+        w.dev_count = nv; w.count_base = base; w.dev_dim = 2;
+        if (base == 0) FO_HIP((gemm::run<gemm::kStoreF32, true, true>(w, gemm::kWide, st)));
+        else FO_HIP((gemm::run<gemm::kAccumF32, true, true>(w, gemm::kWide, st)));
       }
     }
     if (dH != nullptr) {

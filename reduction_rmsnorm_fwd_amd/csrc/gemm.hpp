@@ -1,23 +1,27 @@
-// bf16 MFMA GEMM for gfx950 (fp32 accumulate), both operands K-contiguous:
+// bf16 MFMA GEMM for gfx950 (fp32 accumulate):
 //   C[m, n] (=|+=) sum_k A[m, k] * B[n, k]
-// used for the three contractions of the fused linear cross-entropy.  The other
-// operand layouts are produced by the LDS-tiled transpose below.
+// used for the three contractions of the fused linear cross-entropy.  Each operand is
+// stored either k-contiguous (element (x, k) at p[x*ld + k]) or k-major (at
+// p[k*ld + x]); the direct-to-LDS kernel reads both without a transposed copy (the
+// k-major one through the transposing LDS loads of gfx950).
 //
-// Tiling: a 256-thread workgroup (4 wave64s in a 2x2 grid) owns a BM x BN tile of C;
-// each wave owns (BM/2) x (BN/2) as 32x32 blocks of v_mfma_f32_32x32x16_bf16.  The K
-// loop stages BK-deep slices of A and B in LDS (double-buffered, padded rows so the
-// 16-byte fragment reads of the 32 rows of a block fall in different banks); the
-// next slice's global loads are issued before the current slice's MFMAs, so HBM/L2
-// latency hides behind the matrix math.  One barrier per slice.
+// Tiling (direct-to-LDS kernel): a 512-thread workgroup (8 wave64s in a 4x2 grid)
+// owns a 256x256 tile of C; each wave owns 64x128 as 2x4 blocks of
+// v_mfma_f32_32x32x16_bf16.  The K loop stages 64-deep slices of A and B in LDS
+// (two stages, unpadded and XOR-swizzled), filled by buffer loads that write LDS
+// directly; the next slice's loads are issued before the current slice's MFMAs, so
+// HBM/L2 latency hides behind the matrix math.  One barrier per slice.  A register-
+// staged kernel (padded LDS rows) serves k-contiguous operands the buffer path cannot
+// address (misaligned rows).
 //
 // MFMA operand layout (32x32x16 bf16): lane l supplies A[l%32][8(l/32) .. 8(l/32)+7]
 // and B[8(l/32) .. +7][l%32]; it receives D[8(r/4) + 4(l/32) + r%4][l%32] in
 // accumulator register r = 0..15.
 //
 // Launch order is XCD-aware: consecutive workgroup ids are dealt round-robin to the 8
-// XCDs, so ids are remapped so that each XCD receives a contiguous range of tiles,
-// walked in column groups of kGroupM tile rows; tiles that share A rows or B rows
-// then run on the same XCD and share its L2.
+// XCDs, so ids are remapped so that each XCD receives a contiguous range of (split-K
+// slice, tile) pairs, walked in column groups of kGroupM tile rows; tiles that share
+// A rows or B rows then run on the same XCD and share its L2.
 #pragma once
 
 #include "fo_common.hpp"
@@ -43,8 +47,8 @@ struct Args {
   void* C;
   int64_t M, N, K;
   int64_t lda, ldb, ldc;
-  // split-K: workgroup row blockIdx.y covers K range [y*k_split, (y+1)*k_split) and
-  // writes its fp32 partial at C + y*c_split (elements); k_split = 0: no split
+  // split-K: slice y covers the K range [y*k_split, (y+1)*k_split) and writes its
+  // fp32 partial at C + y*c_split (elements); k_split = 0: no split
   int64_t k_split = 0;
   int64_t c_split = 0;
   // device-side extent: when dev_count is set, the effective M (dev_dim 1) or K
@@ -54,57 +58,96 @@ struct Args {
   const long long* dev_count = nullptr;
   int64_t count_base = 0;
   int dev_dim = 0;
+  // split_max > 0: split-K with the slice count chosen on the device from the
+  // effective M (dyn_splits, at most split_max slices); k_split unused
+  int64_t split_max = 0;
+  // k-major B only: B has b_rows k-rows (counted from the product's first k); the
+  // rows past them read as zeros.  0: all K rows exist.
+  int64_t b_rows = 0;
   float2* stats = nullptr;  // kStoreF32Stats only
   int64_t stats_ld = 0;
 };
 
-// The K slice of this workgroup row (split-K), applied to a copy of the arguments.
-__device__ __forceinline__ Args split_args(const Args& in) {
-  Args a = in;
+constexpr int64_t kCus = 256;
+
+// Split-K slice count for an M x N product of 256x256 tiles over K: the count s <=
+// smax (each slice at least 2048 deep) that minimises the workgroup waves per unit of
+// K, ceil(tiles*s / kCus) / s; ties go to the smaller s (fewer partials to sum).
+__host__ __device__ inline int64_t dyn_splits(int64_t M, int64_t N, int64_t K, int64_t smax) {
+  const int64_t tiles = ceil_div(M, 256) * ceil_div(N, 256);
+  if (tiles <= 0) return 1;
+  int64_t best = 1, bw = ceil_div(tiles, kCus);
+  for (int64_t s = 2; s <= smax && K / s >= 2048; ++s) {
+    const int64_t w = ceil_div(tiles * s, kCus);
+    if (w * best < bw * s) { best = s; bw = w; }
+  }
+  return best;
+}
+
+// K extent of each of s split-K slices (a multiple of the 64-deep K step).
+__host__ __device__ inline int64_t split_len(int64_t K, int64_t s) {
+  return ceil_div(ceil_div(K, s), 64) * 64;
+}
+
+// What this workgroup computes: the arguments with the device-side extent applied,
+// the split-K slice and the output tile.  The (slice, tile) pairs of the effective
+// work take the first workgroup ids (a device-side count may cut it below the grid's
+// size; the workgroups past it return false at once), and are remapped so that each
+// XCD (ids x, x+8, x+16, ... run on XCD x % 8) gets one contiguous range of them: a
+// run of tiles of one slice, walked kGroupM tile rows at a time along n, so the
+// workgroups resident on an XCD share operand panels in its L2.
+template <int BM, int BN, bool AT = false, bool BT = false>
+__device__ __forceinline__ bool locate(const Args& in, Args& a, int64_t& om, int64_t& on) {
+  a = in;
   if (in.dev_count != nullptr) {
     int64_t e = *in.dev_count - in.count_base;
     if (e < 0) e = 0;
     if (in.dev_dim == 1) {
       a.M = e < in.M ? e : in.M;
     } else {
-      e = (e + 63) / 64 * 64;
+      // a k-contiguous operand is read in 8-deep chunks (the caller keeps zeros up to
+      // the next multiple of 8); k-major operands stop at the exact row
+      if (!AT || !BT) e = (e + 7) / 8 * 8;
       a.K = e < in.K ? e : in.K;
     }
   }
-  if (in.k_split > 0) {
-    const int64_t kb = (int64_t)blockIdx.y * in.k_split;
-    a.A += kb;
-    a.B += kb;
-    a.K = (in.K - kb < in.k_split) ? in.K - kb : in.k_split;
-    a.C = static_cast<float*>(in.C) + (int64_t)blockIdx.y * in.c_split;
-  }
-  return a;
-}
-
-// Maps a linear workgroup id to (tile_m, tile_n).
-__device__ __forceinline__ void tile_of(int64_t bid, int64_t nbl, int64_t tm, int64_t tn,
-                                        int64_t& om, int64_t& on) {
-  // XCD remap: ids x, x+8, x+16, ... (all on XCD x % 8) become one contiguous range.
-  const int64_t per = nbl / kXcds;
-  const int64_t rem = nbl % kXcds;
+  if (a.b_rows <= 0 || a.b_rows > a.K) a.b_rows = a.K;
+  int64_t ns = 1, ks = 0;
+  if (in.split_max > 0) ks = split_len(a.K, dyn_splits(a.M, a.N, a.K, in.split_max));
+  else if (in.k_split > 0) ks = in.k_split;
+  if (ks > 0) ns = ceil_div(a.K, ks);
+  const int64_t tm = ceil_div(a.M, BM), tn = ceil_div(a.N, BN);
+  const int64_t tiles = tm * tn, total = tiles * ns;
+  const int64_t bid = blockIdx.x;
+  if (bid >= total) return false;
+  const int64_t per = total / kXcds, rem = total % kXcds;
   const int64_t x = bid % kXcds, i = bid / kXcds;
-  int64_t pid;
-  if (x < rem) pid = x * (per + 1) + i;
-  else pid = rem * (per + 1) + (x - rem) * per + i;
-  // grouped order: kGroupM tile rows advance together along n
+  const int64_t pid = x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+  const int64_t sl = pid / tiles, t = pid - sl * tiles;
   const int64_t width = (int64_t)kGroupM * tn;
-  const int64_t g = pid / width;
+  const int64_t g = t / width;
   const int64_t first_m = g * kGroupM;
   const int64_t gm = (tm - first_m < kGroupM) ? tm - first_m : kGroupM;
-  const int64_t r = pid - g * width;
+  const int64_t r = t - g * width;
   om = first_m + r % gm;
   on = r / gm;
+  if (ks > 0) {
+    const int64_t kb = sl * ks;
+    a.A += AT ? kb * in.lda : kb;
+    a.B += BT ? kb * in.ldb : kb;
+    a.K = (a.K - kb < ks) ? a.K - kb : ks;
+    a.b_rows = a.b_rows - kb < 0 ? 0 : (a.b_rows - kb < a.K ? a.b_rows - kb : a.K);
+    a.C = static_cast<float*>(in.C) + sl * in.c_split;
+  }
+  return true;
 }
 
 // WGM x WGN waves; wave tile (BM/WGM) x (BN/WGN) as FM x FN blocks of 32x32.
 template <int BM, int BN, int BK, int WGM, int WGN, int MODE>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_nt(Args a_in) {
-  const Args a = split_args(a_in);
+  Args a;
+  int64_t tm, tn;
+  if (!locate<BM, BN>(a_in, a, tm, tn)) return;
   constexpr int NT = WGM * WGN * 64;
   constexpr int PAD = 8;
   constexpr int LDS_ROW = BK + PAD;                 // elements
@@ -119,11 +162,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_nt(Args a_in) {
   __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDS_ROW];
   __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * LDS_ROW];
 
-  const int64_t tm_n = ceil_div(a_in.M, BM), tn_n = ceil_div(a_in.N, BN);
-  int64_t tm, tn;
-  tile_of(blockIdx.x, (int64_t)gridDim.x, tm_n, tn_n, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
-  if (m0 >= a.M) return;  // past a device-side row count
   if (MODE == kAccumF32 && a.K == 0) return;  // nothing to add
 
   const int tid = threadIdx.x;
@@ -354,99 +393,198 @@ __device__ __forceinline__ void store_tile(const Args& a, f32x16 (&acc)[FM][FN],
     }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int ST, int SH, int MODE>
+// One operand of the direct-to-LDS kernel: an X (rows of C: m or n) by BK (k) slice
+// per stage.  Two storage orders:
+//  - K-contiguous (T = false): element (x, k) at p[x*ld + k].  LDS holds [X][BK]; the
+//    16-byte chunk c of row r sits at slot c ^ ((r >> SH) & (CPR-1)).  A fragment
+//    (8 consecutive k of one row) is one ds_read_b128.
+//  - X-contiguous (T = true): element (x, k) at p[k*ld + x].  LDS holds [BK][X]; the
+//    16-byte chunk c of k-row r sits at slot c ^ ((r & 3) << 2), so the four k-rows a
+//    transposing read touches at once fall in four different 64-byte bank groups.  A
+//    fragment is two ds_read_b64_tr_b16: in each 16-lane group, lane j points at the
+//    4 x-values (4(j&3) .. +3) of k-row j>>2, and lane i receives the 4 k-values of
+//    x = i, i.e. 4 consecutive k of one row of the operand, as the MFMA wants them.
+// DMA: each wave issues PW buffer_load_dwordx4 ... lds per slice; lane l of an
+// instruction fills LDS slot l of it, so the swizzle is applied by choosing which
+// global chunk lane l loads.  Rows past the operand (and, T = false, k past K) read
+// as zeros through the buffer range / an out-of-range offset.
+template <int X, int BK, int NW, int SH, bool T>
+struct DmaOperand {
+  static constexpr int CPR = T ? X / 8 : BK / 8;  // 16-byte chunks per LDS row
+  static constexpr int RPI = 64 / CPR;            // LDS rows per DMA instruction
+  static constexpr int ROWS = T ? BK : X;         // LDS rows per slice
+  static constexpr int PW = ROWS / RPI / NW;      // DMA instructions per wave per slice
+  static_assert(ROWS % (RPI * NW) == 0, "DMA split");
+  static_assert(!T || (CPR >= 16 && BK % 16 == 0), "transposed tile shape");
+  uint32_t off[PW];          // per-lane byte offset of each instruction's chunk
+  __amdgpu_buffer_rsrc_t rs;  // k-contiguous: the tile's row panel
+  const bf16* base;          // k-major: the tile's first column at k = 0
+  int64_t ldk;               // k-major: elements per k row
+  int64_t K;                 // k extent (k-major: the k rows that exist)
+
+  __device__ __forceinline__ int row_of(int i, int wave, int lane) const {
+    return (wave * PW + i) * RPI + lane / CPR;
+  }
+  // the global chunk lane `lane` loads in instruction i (chunk c of LDS row r sits at
+  // slot c ^ swizzle(r), and lane l fills slot l % CPR)
+  __device__ __forceinline__ int chunk_of(int i, int wave, int lane) const {
+    const int r = row_of(i, wave, lane), slot = lane % CPR;
+    if constexpr (!T) return slot ^ ((r >> SH) & (CPR - 1));
+    else return slot ^ ((r & 3) << 2);
+  }
+
+  __device__ __forceinline__ void init(const bf16* p, int64_t ld, int64_t x0, int64_t xn,
+                                       int64_t k_extent, int wave, int lane) {
+    K = k_extent;
+    if constexpr (!T) {
+      const int64_t rows = (xn - x0 < X) ? xn - x0 : X;
+      rs = __builtin_amdgcn_make_buffer_rsrc((void*)(p + x0 * ld), (short)0,
+                                             (int)(rows * ld * 2), kBufFlags);
+#pragma unroll
+      for (int i = 0; i < PW; ++i)
+        off[i] = (uint32_t)(row_of(i, wave, lane) * ld * 2 + chunk_of(i, wave, lane) * 16);
+    } else {
+      base = p + x0;
+      ldk = ld;
+#pragma unroll
+      for (int i = 0; i < PW; ++i) {
+        const int c = chunk_of(i, wave, lane);
+        off[i] = x0 + c * 8 < xn ? (uint32_t)(row_of(i, wave, lane) * ld * 2 + c * 16) : kOob;
+      }
+    }
+  }
+
+  // slice of k0 .. k0+BK-1 into the stage at dst (ROWS x CPR chunks)
+  __device__ __forceinline__ void dma(bf16* dst, int64_t k0, int wave, int lane) const {
+    if constexpr (!T) {
+      const uint32_t kb = (uint32_t)k0 * 2;
+      // only the slice holding the K tail needs the per-lane range test (K % 8 == 0,
+      // so a chunk is wholly in or out)
+      const bool tail = k0 + BK > K;
+      const int krem = (int)(K - k0);
+#pragma unroll
+      for (int i = 0; i < PW; ++i) {
+        const uint32_t o = (!tail || chunk_of(i, wave, lane) * 8 < krem) ? off[i] + kb : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_vptr)(dst + (wave * PW + i) * RPI * CPR * 8),
+                                                 16, o, 0, 0, 0);
+      }
+    } else {
+      // a buffer over this slice's k rows only: rows past K read as zeros, and no
+      // offset exceeds 64 rows
+      const int64_t nrow = (K - k0 < BK) ? K - k0 : BK;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(base + k0 * ldk), (short)0, (int)(nrow > 0 ? nrow * ldk * 2 : 0), kBufFlags);
+#pragma unroll
+      for (int i = 0; i < PW; ++i) {
+        // (a local copy: handing the member straight to the builtin makes this hipcc
+        // drop the host launch stubs of later instantiations of the kernel)
+        const uint32_t o = off[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(dst + (wave * PW + i) * RPI * CPR * 8),
+                                                 16, o, 0, 0, 0);
+      }
+    }
+  }
+};
+
+// Per-lane LDS byte offsets of the F fragments (32 rows of the operand each) of a
+// wave whose first operand row is xoff; frag() adds the k step.
+template <int X, int BK, int SH, int F, bool T>
+struct FragReader {
+  uint32_t base[F];
+  __device__ __forceinline__ void init(int xoff, int lane) {
+    if constexpr (!T) {
+      constexpr int CPR = BK / 8;
+      const int fr = lane & 31;
+      // every fragment row is fr plus a multiple of 32 and (32 >> SH) & (CPR-1) == 0,
+      // so the swizzle term depends only on the lane
+      static_assert(((32 >> SH) & (CPR - 1)) == 0, "swizzle period must divide 32");
+#pragma unroll
+      for (int f = 0; f < F; ++f) base[f] = (uint32_t)((xoff + f * 32 + fr) * BK * 2);
+    } else {
+      const int g = lane >> 4, j = lane & 15;
+      const int krow = 8 * (g >> 1) + (j >> 2);
+      const int sw = (j >> 2) << 2;
+      const int lco = 2 * (g & 1) + ((j & 3) >> 1);
+      const int within = 8 * (j & 1);
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        const int c0 = (xoff + f * 32) / 8;  // first chunk of the fragment's 32 columns
+        base[f] = (uint32_t)(krow * X * 2 + (((c0 ^ sw) + lco) * 16) + within);
+      }
+    }
+  }
+  // fragment f, k step kk (16 deep) of the stage at src
+  __device__ __forceinline__ bf16x8 frag(const bf16* src, int f, int kk, int lane) const {
+    const char* b = reinterpret_cast<const char*>(src);
+    if constexpr (!T) {
+      constexpr int CPR = BK / 8;
+      const int fr = lane & 31, fh = lane >> 5;
+      const int sw = (fr >> SH) & (CPR - 1);
+      const int kof = ((kk * 2 + fh) ^ sw) * 16;
+      return *reinterpret_cast<const bf16x8*>(b + base[f] + kof);
+    } else {
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      const char* p0 = b + base[f] + kk * 16 * X * 2;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(p0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(p0 + 4 * X * 2));
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8, v);
+    }
+  }
+};
+
+template <int BM, int BN, int BK, int WGM, int WGN, int ST, int SH, int MODE, bool AT = false,
+          bool BT = false>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_nt_dma(Args a_in) {
-  const Args a = split_args(a_in);
+  Args a;
+  int64_t tm, tn;
+  if (!locate<BM, BN, AT, BT>(a_in, a, tm, tn)) return;
   constexpr int NW = WGM * WGN;
-  constexpr int CPR = BK / 8;                 // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;               // rows per DMA instruction
-  constexpr int A_PW = BM / RPI / NW;         // DMA instructions per wave per slice
-  constexpr int B_PW = BN / RPI / NW;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
-  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "DMA split");
   static_assert(ST == 2 || ST == 3, "stages");
   static_assert(BK == 32 || BK == 64, "BK");
+  using OpA = DmaOperand<BM, BK, NW, SH, AT>;
+  using OpB = DmaOperand<BN, BK, NW, SH, BT>;
 
   __shared__ __attribute__((aligned(1024))) bf16 sA0[BM * BK], sB0[BN * BK];
   __shared__ __attribute__((aligned(1024))) bf16 sA1[BM * BK], sB1[BN * BK];
   __shared__ __attribute__((aligned(1024))) bf16 sA2[ST == 3 ? BM * BK : 8], sB2[ST == 3 ? BN * BK : 8];
 
-  const int64_t tm_n = ceil_div(a_in.M, BM), tn_n = ceil_div(a_in.N, BN);
-  int64_t tm, tn;
-  tile_of(blockIdx.x, (int64_t)gridDim.x, tm_n, tn_n, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
-  if (m0 >= a.M) return;  // past a device-side row count
   if (MODE == kAccumF32 && a.K == 0) return;  // nothing to add
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
 
-  const int64_t rows_a = (a.M - m0 < BM) ? a.M - m0 : BM;
-  const int64_t rows_b = (a.N - n0 < BN) ? a.N - n0 : BN;
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.A + m0 * a.lda), (short)0, (int)(rows_a * a.lda * 2), kBufFlags);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.B + n0 * a.ldb), (short)0, (int)(rows_b * a.ldb * 2), kBufFlags);
-
-  // per-lane source row / chunk of each DMA instruction (fixed over K)
-  const int rl = lane / CPR, slot = lane % CPR;
-  uint32_t offa[A_PW], offb[B_PW];
-  int ca[A_PW], cb[B_PW];
-#pragma unroll
-  for (int i = 0; i < A_PW; ++i) {
-    const int r = (wave * A_PW + i) * RPI + rl;
-    ca[i] = slot ^ ((r >> SH) & (CPR - 1));
-    offa[i] = (uint32_t)(r * a.lda * 2 + ca[i] * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < B_PW; ++i) {
-    const int r = (wave * B_PW + i) * RPI + rl;
-    cb[i] = slot ^ ((r >> SH) & (CPR - 1));
-    offb[i] = (uint32_t)(r * a.ldb * 2 + cb[i] * 16);
-  }
-  // K offset of each lane's chunk inside a slice; only the slice holding the K tail
-  // needs the per-lane range test (K % 8 == 0, so a chunk is wholly in or out).
-  const int64_t k_full = (a.K / BK) * BK;
+  OpA opa;
+  OpB opb;
+  opa.init(a.A, a.lda, m0, a.M, a.K, wave, lane);
+  opb.init(a.B, a.ldb, n0, a.N, BT ? a.b_rows : a.K, wave, lane);
   auto dma = [&](bf16* dA, bf16* dB, int64_t k0) {
-    const uint32_t kb = (uint32_t)(k0 * 2);
-    const bool tail = k0 >= k_full;
-    const int krem = (int)(a.K - k0);
-#pragma unroll
-    for (int i = 0; i < A_PW; ++i) {
-      const uint32_t off = (!tail || ca[i] * 8 < krem) ? offa[i] + kb : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_vptr)(dA + (wave * A_PW + i) * RPI * BK), 16, off, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < B_PW; ++i) {
-      const uint32_t off = (!tail || cb[i] * 8 < krem) ? offb[i] + kb : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (lds_vptr)(dB + (wave * B_PW + i) * RPI * BK), 16, off, 0, 0, 0);
-    }
+    opa.dma(dA, k0, wave, lane);
+    opb.dma(dB, k0, wave, lane);
   };
 
   f32x16 acc[FM][FN];
   const int fr = lane & 31;
   const int fh = lane >> 5;
-  // Every fragment row this lane reads is fr plus a multiple of 32, and
-  // (32 >> SH) & (CPR-1) == 0, so the swizzle term depends only on the lane: the
-  // chunk of k-step kk sits at slot (2kk + fh) ^ sw of each of those rows.
-  static_assert(((32 >> SH) & (CPR - 1)) == 0, "swizzle period must divide 32");
-  const int sw = (fr >> SH) & (CPR - 1);
-  const int a_row = (wm * WM + fr) * BK;
-  const int b_row = (wn * WN + fr) * BK;
+  FragReader<BM, BK, SH, FM, AT> ra;
+  FragReader<BN, BK, SH, FN, BT> rb;
+  ra.init(wm * WM, lane);
+  rb.init(wn * WN, lane);
   auto compute = [&](const bf16* cA, const bf16* cB) {
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 af[FM], bfr[FN];
-      const int kof = ((kk * 2 + fh) ^ sw) * 8;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(cA + a_row + i * 32 * BK + kof);
+      for (int i = 0; i < FM; ++i) af[i] = ra.frag(cA, i, kk, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(cB + b_row + j * 32 * BK + kof);
+      for (int j = 0; j < FN; ++j) bfr[j] = rb.frag(cB, j, kk, lane);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -455,7 +593,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_nt_dma(Args a_in) {
     }
   };
 
-  constexpr int PER_WAVE = A_PW + B_PW;
+  constexpr int PER_WAVE = OpA::PW + OpB::PW;
   const int64_t nk = ceil_div(a.K, BK);
   // One step: wait until slice kt has landed (allowing the younger slices still in
   // flight), barrier (slice kt visible to all waves; every wave is done with slice
@@ -501,13 +639,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_nt_dma(Args a_in) {
   store_tile<MODE == kStoreF32Stats ? kStoreF32 : MODE, BM, BN, WM, WN, FM, FN>(a, acc, m0, n0, wm, wn, fr, fh);
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int ST, int SH, int MODE>
+template <int BM, int BN, int BK, int WGM, int WGN, int ST, int SH, int MODE, bool AT = false,
+          bool BT = false>
 hipError_t launch_dma(const Args& a, hipStream_t st) {
   const int64_t tiles = ceil_div(a.M, BM) * ceil_div(a.N, BN);
   if (tiles == 0) return hipSuccess;
-  const unsigned splits = a.k_split > 0 ? (unsigned)ceil_div(a.K, a.k_split) : 1u;
-  gemm_nt_dma<BM, BN, BK, WGM, WGN, ST, SH, MODE>
-      <<<dim3((unsigned)tiles, splits), dim3(WGM * WGN * 64), 0, st>>>(a);
+  const int64_t splits = a.split_max > 0 ? a.split_max
+                       : a.k_split > 0   ? ceil_div(a.K, a.k_split)
+                                         : 1;
+  gemm_nt_dma<BM, BN, BK, WGM, WGN, ST, SH, MODE, AT, BT>
+      <<<dim3((unsigned)(tiles * splits)), dim3(WGM * WGN * 64), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -515,9 +656,11 @@ template <int BM, int BN, int BK, int WGM, int WGN, int MODE>
 hipError_t launch_cfg(const Args& a, hipStream_t st) {
   const int64_t tiles = ceil_div(a.M, BM) * ceil_div(a.N, BN);
   if (tiles == 0) return hipSuccess;
-  const unsigned splits = a.k_split > 0 ? (unsigned)ceil_div(a.K, a.k_split) : 1u;
+  const int64_t splits = a.split_max > 0 ? a.split_max
+                       : a.k_split > 0   ? ceil_div(a.K, a.k_split)
+                                         : 1;
   gemm_nt<BM, BN, BK, WGM, WGN, MODE>
-      <<<dim3((unsigned)tiles, splits), dim3(WGM * WGN * 64), 0, st>>>(a);
+      <<<dim3((unsigned)(tiles * splits)), dim3(WGM * WGN * 64), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -528,26 +671,44 @@ hipError_t launch_cfg(const Args& a, hipStream_t st) {
 // register-staged kernel runs (same arithmetic, same results).
 enum TileShape { kWide = 0, kNarrow = 1 };
 
+// Whether the direct-to-LDS kernel can read the operands: 16-byte aligned bases and
+// rows, 32-bit buffer offsets within a tile's row panel (k-contiguous) and k-contiguous
+// rows read in whole 8-deep chunks (K % 8 == 0); a k-major operand's rows hold at
+// least the X extent rounded up to 8 (its last chunk is read whole).
+template <bool AT, bool BT>
 inline bool dma_ok(const Args& a, int bm, int bn) {
   const bool aligned = ((reinterpret_cast<uintptr_t>(a.A) | reinterpret_cast<uintptr_t>(a.B)) & 15) == 0;
   const int64_t lim = (int64_t)1 << 31;
-  return aligned && a.K % 8 == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
-         (int64_t)bm * a.lda * 2 < lim && (int64_t)bn * a.ldb * 2 < lim;
+  auto op_ok = [&](bool t, int64_t ld, int64_t x, int tile) {
+    if (ld % 8 != 0) return false;
+    if (t) return ld >= (x + 7) / 8 * 8 && 64 * ld * 2 < lim;
+    return a.K % 8 == 0 && (int64_t)tile * ld * 2 < lim;
+  };
+  return aligned && op_ok(AT, a.lda, a.M, bm) && op_ok(BT, a.ldb, a.N, bn);
 }
 
-template <int MODE>
+// Runs C (op)= A B^T.  AT / BT: A or B is stored k-major (element (x, k) at
+// p[k*ld + x]); those layouts exist in the direct-to-LDS kernel only.
+template <int MODE, bool AT = false, bool BT = false>
 hipError_t run(const Args& a, TileShape shape, hipStream_t st) {
   if constexpr (MODE == kStoreF32Stats) {
     // the row partials come from the direct-to-LDS kernel's wide tile only (its waves
     // cover kStatsCols columns each)
-    if (shape != kWide || !dma_ok(a, 256, 256)) return hipErrorInvalidValue;
-    return launch_dma<256, 256, 64, 4, 2, 2, 1, MODE>(a, st);
+    if (shape != kWide || !dma_ok<AT, BT>(a, 256, 256)) return hipErrorInvalidValue;
+    return launch_dma<256, 256, 64, 4, 2, 2, 1, MODE, AT, BT>(a, st);
+  } else if constexpr (AT || BT) {
+    if (shape == kWide) {
+      if (!dma_ok<AT, BT>(a, 256, 256)) return hipErrorInvalidValue;
+      return launch_dma<256, 256, 64, 4, 2, 2, 1, MODE, AT, BT>(a, st);
+    }
+    if (!dma_ok<AT, BT>(a, 128, 128)) return hipErrorInvalidValue;
+    return launch_dma<128, 128, 64, 2, 2, 2, 1, MODE, AT, BT>(a, st);
   } else {
     if (shape == kWide) {
-      if (dma_ok(a, 256, 256)) return launch_dma<256, 256, 64, 4, 2, 2, 1, MODE>(a, st);
+      if (dma_ok<false, false>(a, 256, 256)) return launch_dma<256, 256, 64, 4, 2, 2, 1, MODE>(a, st);
       return launch_cfg<256, 256, 64, 4, 2, MODE>(a, st);
     }
-    if (dma_ok(a, 128, 128)) return launch_dma<128, 128, 64, 2, 2, 2, 1, MODE>(a, st);
+    if (dma_ok<false, false>(a, 128, 128)) return launch_dma<128, 128, 64, 2, 2, 2, 1, MODE>(a, st);
     return launch_cfg<128, 128, 64, 2, 2, MODE>(a, st);
   }
 }
@@ -571,19 +732,22 @@ inline SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
 }
 
 // out[m, n] = bf16(sum_s part[s, m, n]) summed in the order s = 0, 1, ...
-// (dev_rows: only rows m < *dev_rows - rows_base exist.)
+// (dev_rows: only rows m < *dev_rows - rows_base exist; split_max > 0: the slice count
+// is dyn_splits of those rows, as the product chose it, for a K-deep product.)
 __global__ __launch_bounds__(256) void reduce_splits_bf16(const float* __restrict__ part,
                                                           int64_t splits, int64_t MN,
                                                           int64_t N, bf16* __restrict__ out,
                                                           int64_t ldo,
                                                           const long long* dev_rows,
-                                                          int64_t rows_base) {
+                                                          int64_t rows_base, int64_t K,
+                                                          int64_t split_max) {
   int64_t len = MN;  // elements to reduce; MN stays the stride between partials
   if (dev_rows != nullptr) {
     int64_t eff = *dev_rows - rows_base;
     eff = eff < 0 ? 0 : eff;
     if (eff * N < len) len = eff * N;
   }
+  if (split_max > 0) splits = ceil_div(K, split_len(K, dyn_splits(len / N, N, K, split_max)));
   for (int64_t e4 = (int64_t)blockIdx.x * 256 + threadIdx.x; e4 * 4 < len;
        e4 += (int64_t)gridDim.x * 256) {
     const int64_t e = e4 * 4;
@@ -598,80 +762,6 @@ __global__ __launch_bounds__(256) void reduce_splits_bf16(const float* __restric
       out[m * ldo + n] = from_f32<bf16>(v[q]);
     }
   }
-}
-
-// dst[c, r] = src[r, c] for r < R, c < Cn; dst[c, r] = 0 for R <= r < Rpad.
-// 64x64 tiles: 16-byte loads along src rows into LDS, 16-byte stores along dst rows
-// gathered from LDS columns (rows of 65 words: a column walk hits distinct banks).
-// Requires 16-byte aligned src/dst rows (lds % 8 == 0, ldd % 8 == 0) and Cn % 8 == 0.
-__global__ __launch_bounds__(256) void transpose_bf16_v(const bf16* __restrict__ src, int64_t lds,
-                                                        bf16* __restrict__ dst, int64_t ldd,
-                                                        int64_t R, int64_t Cn, int64_t Rpad) {
-  __shared__ uint32_t tile[64][65];  // tile[r][c/2]: bf16 pairs of row r
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  const int t = threadIdx.x;
-  // load: 64 rows x 8 vectors; thread t -> (row t/8 + 32i, vector t%8)
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = t / 8 + 32 * i, v = t % 8;
-    const int64_t gr = r0 + r, gc = c0 + v * 8;
-    u32x4 d = u32x4{0, 0, 0, 0};
-    if (gr < R && gc < Cn) d = *reinterpret_cast<const u32x4*>(src + gr * lds + gc);
-    tile[r][v * 4 + 0] = d.x;
-    tile[r][v * 4 + 1] = d.y;
-    tile[r][v * 4 + 2] = d.z;
-    tile[r][v * 4 + 3] = d.w;
-  }
-  __syncthreads();
-  // store: dst row c (64 of them) x 8 vectors of 8 src rows; thread t -> (c t/8 + 32i, vector t%8)
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = t / 8 + 32 * i, v = t % 8;
-    const int64_t gc = c0 + c, gr = r0 + v * 8;
-    if (gc >= Cn || gr >= Rpad) continue;
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = tile[v * 8 + 2 * q][c / 2], hi = tile[v * 8 + 2 * q + 1][c / 2];
-      const uint32_t a = (c & 1) ? (lo >> 16) : (lo & 0xffffu);
-      const uint32_t b = (c & 1) ? (hi >> 16) : (hi & 0xffffu);
-      w[q] = a | (b << 16);
-    }
-    if (gr + 8 <= Rpad) {
-      *reinterpret_cast<u32x4*>(dst + gc * ldd + gr) = u32x4{w[0], w[1], w[2], w[3]};
-    } else {
-      const bf16* e = reinterpret_cast<const bf16*>(w);
-      for (int q = 0; q < 8 && gr + q < Rpad; ++q) dst[gc * ldd + gr + q] = e[q];
-    }
-  }
-}
-
-// Scalar form for shapes the vector form does not take.
-__global__ __launch_bounds__(256) void transpose_bf16(const bf16* __restrict__ src, int64_t lds,
-                                                      bf16* __restrict__ dst, int64_t ldd,
-                                                      int64_t R, int64_t Cn, int64_t Rpad) {
-  __shared__ bf16 tile[64][65];
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < R && c < Cn) ? src[r * lds + c] : from_f32<bf16>(0.f);
-  }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < Cn && r < Rpad) dst[c * ldd + r] = tile[tx][i];
-  }
-}
-
-inline hipError_t transpose(const bf16* src, int64_t lds, bf16* dst, int64_t ldd, int64_t R,
-                            int64_t Cn, int64_t Rpad, hipStream_t st) {
-  const dim3 grid((unsigned)ceil_div(Cn, 64), (unsigned)ceil_div(Rpad, 64));
-  const bool vec = lds % 8 == 0 && ldd % 8 == 0 && Cn % 8 == 0 &&
-                   ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
-  if (vec) transpose_bf16_v<<<grid, dim3(256), 0, st>>>(src, lds, dst, ldd, R, Cn, Rpad);
-  else transpose_bf16<<<grid, dim3(256), 0, st>>>(src, lds, dst, ldd, R, Cn, Rpad);
-  return hipGetLastError();
 }
 
 }  // namespace
