@@ -413,8 +413,13 @@ struct DmaOperand {
   static constexpr int CPR = T ? X / 8 : BK / 8;  // 16-byte chunks per LDS row
   static constexpr int RPI = 64 / CPR;            // LDS rows per DMA instruction
   static constexpr int ROWS = T ? BK : X;         // LDS rows per slice
-  static constexpr int PW = ROWS / RPI / NW;      // DMA instructions per wave per slice
-  static_assert(ROWS % (RPI * NW) == 0, "DMA split");
+  // Waves that issue the DMA: with 8 waves, the first 4 (one per SIMD) issue all of
+  // it, so the other wave of each SIMD keeps its MFMAs going while the issuing one
+  // waits for the vector memory queue to take its loads (a few percent faster than
+  // all 8 waves issuing at the same moment after the barrier).
+  static constexpr int DW = NW >= 8 ? NW / 2 : NW;
+  static constexpr int PW = ROWS / RPI / DW;      // DMA instructions per issuing wave
+  static_assert(ROWS % (RPI * DW) == 0, "DMA split");
   static_assert(!T || (CPR >= 16 && BK % 16 == 0), "transposed tile shape");
   uint32_t off[PW];          // per-lane byte offset of each instruction's chunk
   __amdgpu_buffer_rsrc_t rs;  // k-contiguous: the tile's row panel
@@ -456,6 +461,7 @@ struct DmaOperand {
 
   // slice of k0 .. k0+BK-1 into the stage at dst (ROWS x CPR chunks)
   __device__ __forceinline__ void dma(bf16* dst, int64_t k0, int wave, int lane) const {
+    if (wave >= DW) return;
     if constexpr (!T) {
       const uint32_t kb = (uint32_t)k0 * 2;
       // only the slice holding the K tail needs the per-lane range test (K % 8 == 0,
