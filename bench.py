@@ -28,6 +28,8 @@ METRIC = "HBM GB/s & % of peak per fused op (fwd+bwd); xent/FLCE tokens/s"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
 FLUSH_BYTES = 1 << 30        # written between isolated calls: beyond L2 and the 256 MB MALL
+COPY_BYTES = 1 << 30         # copy probe: 1 GiB read + 1 GiB written
+MFMA_PROBE_ITERS = 100000    # MFMA probe rounds per wave (about 12 ms)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_step_llama3-8b.json")
 
 
@@ -64,7 +66,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--iso-reps", type=int, default=10, help="isolated calls per op")
+    p.add_argument("--iso-reps", type=int, default=50, help="isolated calls per memory-bound op")
+    p.add_argument("--iso-reps-flce", type=int, default=10, help="isolated calls of the FLCE")
+    p.add_argument("--no-probes", action="store_true",
+                   help="skip the copy / MFMA ceiling probes and the unaligned-shape lines")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-isolated", action="store_true")
     p.add_argument("--only", default="", help="comma list of ops to run (profiling)")
@@ -159,6 +164,95 @@ class Workload:
         ]
 
 
+def measured_peaks(fo, torch, stream, med):
+    """Ceilings on this device, same process: the library's streaming copy probe over
+    1 GiB (caches flushed before each call) and its register-only MFMA probe."""
+    n = COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    ts = []
+    for r in range(11):
+        scratch.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fo.fo_probe_copy(src, dst)
+        b.record(stream)
+        b.synchronize()
+        if r:
+            ts.append(a.elapsed_time(b))
+    assert torch.equal(dst[:1024], src[:1024])
+    copy_gbs = 2 * COPY_BYTES / (med(ts) * 1e-3) / 1e9
+    del src, dst, scratch
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(n_cu * 8, dtype=torch.float32, device="cuda")
+    ts = []
+    flops = 0
+    for r in range(6):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        flops = fo.fo_probe_mfma(n_cu, MFMA_PROBE_ITERS, out)
+        b.record(stream)
+        b.synchronize()
+        if r:
+            ts.append(a.elapsed_time(b))
+    mfma_tfs = flops / (med(ts) * 1e-3) / 1e12
+    print(f"# probes: copy {copy_gbs:.0f} GB/s, mfma {mfma_tfs:.0f} TFLOP/s", file=sys.stderr,
+          flush=True)
+    return {"copy_GBps": round(copy_gbs, 1), "copy_bytes": 2 * COPY_BYTES,
+            "mfma_TFLOPs": round(mfma_tfs, 1), "mfma_cus": n_cu,
+            "note": "fo_probe_copy (16-byte non-temporal, 1 GiB read + 1 GiB written) and "
+                    "fo_probe_mfma (v_mfma_f32_32x32x16_bf16 on registers, 2 waves/SIMD)"}
+
+
+def unaligned_lines(fo, synth, torch, stream, med):
+    """The scalar (unaligned) paths at the Llama-3-8B token count, reported apart from
+    the aligned per-op lines: RMSNorm with d = 4097 and SwiGLU with F = 14337 (rows not
+    a multiple of the 16-byte vector)."""
+    import dataclasses
+    c3 = synth.CONFIGS[3]
+    cu = dataclasses.replace(c3, d=4097, F=14337)
+    r = synth.rmsnorm_inputs(cu)
+    x, w, dy = (r[k].to("cuda") for k in ("x", "w", "dy"))
+    T, d = x.shape
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    dw = torch.empty(d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(fo.fo_rmsnorm_bwd_workspace(T, d), dtype=torch.uint8, device="cuda")
+    s = synth.swiglu_inputs(cu)
+    g, u = s["gate"].to("cuda"), s["up"].to("cuda")
+    h = torch.empty_like(g)
+    F = g.shape[1]
+    b = 2
+    cases = [
+        ("rmsnorm_fwd_d4097", lambda: fo.fo_rmsnorm_fwd(x, w, cu.eps, y=y, rstd=rstd),
+         2 * T * d * b + d * b + 4 * T),
+        ("rmsnorm_bwd_d4097", lambda: fo.fo_rmsnorm_bwd(dy, x, w, rstd, cu.eps, dx=dx, dw=dw, ws=ws),
+         3 * T * d * b + d * b + 4 * T + 4 * d),
+        ("swiglu_fwd_F14337", lambda: fo.fo_swiglu_fwd(g, u, h=h), 3 * T * F * b),
+    ]
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    res = {}
+    for name, fn, byt in cases:
+        fn()
+        ts = []
+        for _ in range(20):
+            scratch.fill_(1.0)
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            e.record(stream)
+            e.synchronize()
+            ts.append(a.elapsed_time(e))
+        t = med(ts)
+        res[name] = {"ms_isolated_median": round(t, 4), "algorithmic_MB": round(byt / 1e6, 3),
+                     "GBps": round(byt / (t * 1e-3) / 1e9, 1),
+                     "frac_hbm_peak": round(byt / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    print("# unaligned lines done", file=sys.stderr, flush=True)
+    return res
+
+
 def gpu_bench(args):
     import torch
     import reduction_rmsnorm_fwd_amd as fo
@@ -213,9 +307,9 @@ def gpu_bench(args):
     iso = [None] * nops
     if not args.no_isolated:
         scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
-        for i, (name, fn, _, _) in enumerate(wl.ops):
+        for i, (name, fn, _, bound) in enumerate(wl.ops):
             ts = []
-            for _ in range(args.iso_reps):
+            for _ in range(args.iso_reps if bound == "hbm" else args.iso_reps_flce):
                 scratch.fill_(1.0)  # evict L2 and the Infinity Cache
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
@@ -231,6 +325,8 @@ def gpu_bench(args):
         v = sorted(v)
         return v[len(v) // 2]
 
+    peaks = None if args.no_probes else measured_peaks(fo, torch, stream, med)
+    unaligned = None if args.no_probes or only else unaligned_lines(fo, synth, torch, stream, med)
     traffic = measured_traffic()
     per_op = {}
     for i, (name, _, work, bound) in enumerate(wl.ops):
@@ -253,6 +349,11 @@ def gpu_bench(args):
             e["tokens_per_s"] = round(wl.T / (t_ref * 1e-3), 1)
         if name == "xent_fwd_bwd":
             e["tokens_per_s"] = round(wl.T / (t_ref * 1e-3), 1)
+        if peaks is not None:
+            if bound == "hbm":
+                e["frac_measured_copy"] = round(e["GBps"] / peaks["copy_GBps"], 4)
+            else:
+                e["frac_measured_mfma"] = round(e["TFLOPs"] / peaks["mfma_TFLOPs"], 4)
         e["traffic_MB"] = round(traffic[name] / 1e6, 1) if traffic and name in traffic else None
         per_op[name] = e
 
@@ -281,6 +382,23 @@ def gpu_bench(args):
         },
         "per_op": per_op,
     }
+    # fwd+bwd pairs: (bytes_fwd + bytes_bwd) / (t_fwd + t_bwd), isolated medians
+    pairs = {}
+    for base in ("rmsnorm", "rope", "swiglu"):
+        f, b = per_op.get(base + "_fwd"), per_op.get(base + "_bwd")
+        if f and b and "ms_isolated_median" in f and "ms_isolated_median" in b:
+            byt = (f["algorithmic_MB"] + b["algorithmic_MB"]) * 1e6
+            t = (f["ms_isolated_median"] + b["ms_isolated_median"]) * 1e-3
+            pairs[base] = {"GBps": round(byt / t / 1e9, 1),
+                           "frac_hbm_peak": round(byt / t / 1e9 / HBM_PEAK_GBS, 4)}
+            if peaks is not None:
+                pairs[base]["frac_measured_copy"] = round(byt / t / 1e9 / peaks["copy_GBps"], 4)
+    if pairs:
+        out["fwd_bwd"] = pairs
+    if peaks is not None:
+        out["measured_peaks"] = peaks
+    if unaligned is not None:
+        out["unaligned"] = unaligned
     # dominant op of the step: the fused linear cross-entropy (MFMA-bound)
     if "flce_fwd_bwd" in per_op:
         i = [o[0] for o in wl.ops].index("flce_fwd_bwd")
@@ -297,6 +415,9 @@ def gpu_bench(args):
             "traffic_unit": "bytes per launch",
             "ms_per_launch": round(ms, 4),
         }
+        if peaks is not None:
+            out["roofline"]["measured_peak"] = peaks["mfma_TFLOPs"]
+            out["roofline"]["frac_measured"] = round(ach / peaks["mfma_TFLOPs"], 4)
     return out, wl
 
 

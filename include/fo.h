@@ -163,6 +163,20 @@ int fo_flce_fwd_bwd(int dtype, int64_t T, int64_t H, int64_t V, const void* hidd
                     int32_t* status, int64_t chunk_tokens, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* ---- Measurement probes (not ops: they give the ceilings the ops are measured
+ * against, on the same device, in the same process) ----
+ * fo_probe_copy: dst = src for `bytes` bytes (a multiple of 16; both 16-byte aligned,
+ *   device memory, not overlapping), one non-temporal read and write per byte.
+ *   FO_ERR_STRIDE for a misaligned pointer or size, FO_ERR_NULL for NULL pointers.
+ * fo_probe_mfma: 2 * n_cu workgroups of 4 wave64s (2 waves per SIMD when they spread
+ *   over the n_cu CUs), each wave issuing `iters` x 4 independent
+ *   v_mfma_f32_32x32x16_bf16 on register operands: n_cu * 8 * iters * 4 * 32768 flops.
+ *   out: device float[n_cu * 8], overwritten (the wave sums, so the loop is not
+ *   optimised away).  iters < 2^31.
+ */
+int fo_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+int fo_probe_mfma(int32_t n_cu, int64_t iters, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,8 @@ SIGNATURES = {
                                        _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_size_t,
                                        _c_ptr]),
     "fo_flce_workspace": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int]),
+    "fo_probe_copy": (ctypes.c_int, [_c_ptr, _c_ptr, ctypes.c_size_t, _c_ptr]),
+    "fo_probe_mfma": (ctypes.c_int, [ctypes.c_int32, _c_i64, _c_ptr, _c_ptr]),
     "fo_flce_fwd_bwd": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr,
                                        _c_ptr, _c_i64, ctypes.c_float, ctypes.c_float, _c_ptr,
                                        _c_ptr, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
@@ -297,3 +299,19 @@ def fo_flce_fwd_bwd(hidden, weight, targets, ignore_index=-100, z_loss=0.0, dlos
     o["dhidden"] = dhidden
     o["dweight"] = dweight
     return o
+
+
+def fo_probe_copy(src, dst):
+    """dst.copy of src through the library's streaming copy probe (same byte count)."""
+    lib = load()
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst differ in size")
+    _check("fo_probe_copy", lib.fo_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream()))
+
+
+def fo_probe_mfma(n_cu, iters, out):
+    """Runs the MFMA probe; returns the flops it performs."""
+    lib = load()
+    _check("fo_probe_mfma", lib.fo_probe_mfma(int(n_cu), int(iters), _ptr(out), _stream()))
+    return int(n_cu) * 8 * int(iters) * 4 * 32 * 32 * 16 * 2

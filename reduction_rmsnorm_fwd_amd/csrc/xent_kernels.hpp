@@ -151,26 +151,7 @@ struct RowArgs {
   const Counters* cnt;
   float* row_loss;  // [T] loss_t (0 for invalid rows)
   float* row_z;     // [T] c lse^2 (0 for invalid rows)
-  // Compacted rows (fused linear cross-entropy): only rows < *dev_rows - rows_base
-  // exist; the ones after that up to the next multiple of 64 get a zero gradient row
-  // (they are K padding of the next contraction), the rest are left alone.
-  const long long* dev_rows = nullptr;
-  int64_t rows_base = 0;
 };
-
-// true if this row is past a device-side row count (and handled here)
-template <typename Tout>
-__device__ __forceinline__ bool beyond_rows(const RowArgs& a, int64_t row, Tout* dz, int nt) {
-  if (a.dev_rows == nullptr) return false;
-  int64_t eff = *a.dev_rows - a.rows_base;
-  eff = eff < 0 ? 0 : (eff > a.T ? a.T : eff);
-  if (row < eff) return false;
-  if (dz != nullptr && row < (eff + 63) / 64 * 64) {
-    Tout* dr = dz + row * a.ldd;
-    for (int64_t e = threadIdx.x; e < a.V; e += nt) dr[e] = from_f32<Tout>(0.f);
-  }
-  return true;
-}
 
 // Register-resident row kernel.  Requires V % VEC == 0, aligned rows, nvec <= NT*NV.
 template <typename Tin, typename Tout, int NV, int NT>
@@ -180,7 +161,6 @@ __global__ __launch_bounds__(NT) void row_reg(RowArgs a, const Tin* z, Tout* dz)
   __shared__ float shm[NT / kWave], shs[NT / kWave];
   __shared__ float sh_zy;
   const int64_t row = blockIdx.x;
-  if (beyond_rows(a, row, dz, NT)) return;
   const long long y = a.tg[row];
   const int64_t nvec = a.V / VEC;
   if (!row_valid(y, a.V, a.ignore)) {
@@ -266,7 +246,6 @@ __global__ __launch_bounds__(NT) void row_stream(RowArgs a, const Tin* z, Tout* 
   __shared__ float shm[NT / kWave], shs[NT / kWave];
   __shared__ float sh_zy;
   const int64_t row = blockIdx.x;
-  if (beyond_rows(a, row, dz, NT)) return;
   const long long y = a.tg[row];
   if (!row_valid(y, a.V, a.ignore)) {
     if (dz != nullptr) {

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in fo.SIGNATURES, f"binding lacks {n}"
@@ -134,3 +134,13 @@ def test_flce_validation(lib):
     assert call(a4=ctypes.c_void_p(0x1002)) == STRIDE   # misaligned hidden
     assert call(a19=ws - 1) == WS
     assert call(a17=-1) == SHAPE
+
+
+def test_probe_validation(lib):
+    assert lib.fo_probe_copy(P, P, 0, N) == OK  # nothing to copy
+    assert lib.fo_probe_copy(N, P, 16, N) == NULL
+    assert lib.fo_probe_copy(P, P, 24, N) == STRIDE
+    assert lib.fo_probe_copy(ctypes.c_void_p(0x1008), P, 16, N) == STRIDE
+    assert lib.fo_probe_mfma(0, 10, P, N) == SHAPE
+    assert lib.fo_probe_mfma(256, 0, P, N) == SHAPE
+    assert lib.fo_probe_mfma(256, 10, N, N) == NULL
