@@ -43,7 +43,7 @@ def test_configs_small(gpu, cid, T):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("d", [13, 1000, 4097, 8, 12288])
+@pytest.mark.parametrize("d", [13, 1000, 1025, 2049, 4097, 8, 8193, 12288])
 def test_unaligned_and_wide_rows(gpu, dtype, d):
     cfg = synth.Config(0, "odd", dtype, T=37, d=d, n_q=1, n_kv=1, head_dim=2, F=1, V=2,
                        eps=1e-5, theta=1e4, logit_std=1, z_loss=0, ignore_frac=0,
