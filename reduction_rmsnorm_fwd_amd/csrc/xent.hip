@@ -11,14 +11,23 @@ extern "C" size_t fo_xent_workspace(int64_t T, int64_t V) {
 
 namespace {
 
+// compute units of the current device (one persistent row workgroup each)
+int64_t cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
 template <typename T>
 int xent_impl(const xent::RowArgs& a, const void* z, void* dz, float* loss, float* z_loss,
               int64_t* n_valid, int32_t* status, hipStream_t st) {
   if (a.T > 0) {
     xent::count_targets<<<1, 1024, 0, st>>>(a.T, a.V, a.tg, a.ignore,
                                             const_cast<xent::Counters*>(a.cnt));
-    if (xent::launch_rows<T, T>(a, static_cast<const T*>(z), static_cast<T*>(dz), st) !=
-        hipSuccess)
+    if (xent::launch_rows<T, T>(a, static_cast<const T*>(z), static_cast<T*>(dz), st,
+                                cu_count()) != hipSuccess)
       return FO_ERR_HIP;
   } else {
     xent::count_targets<<<1, 1024, 0, st>>>(0, a.V, a.tg, a.ignore,

@@ -20,6 +20,8 @@
 // reads the row a second time for the gradient.
 #pragma once
 
+#include <type_traits>
+
 #include "fo_common.hpp"
 
 namespace fo {
@@ -238,6 +240,178 @@ __global__ __launch_bounds__(NT) void row_reg(RowArgs a, const Tin* z, Tout* dz)
   }
 }
 
+// Persistent prefetching row kernel (register-resident rows of NV vectors per thread,
+// 1024 threads).  A workgroup per CU walks the rows blockIdx.x, +gridDim.x, ...  The
+// first NL vectors of each thread's share of the NEXT row are copied into LDS by
+// buffer_load ... lds while the current row is reduced and written, so the CU keeps
+// reads in flight through its compute and store phases (one row per CU in registers
+// leaves no room to overlap two rows otherwise).  Per row:
+//   1. issue the loads of vectors NL..NV-1 (into registers)
+//   2. wait for every outstanding access (this row's LDS copy, the previous row's
+//      stores, step 1), barrier, read the LDS copy into registers, barrier
+//   3. issue the LDS copy of the next row (an empty buffer range for an ignored or
+//      missing row: no memory traffic)
+//   4. online (max, sum) over the row, workgroup merge, loss, gradient, stores.
+// Vector i of thread t is row vector t + i*1024 in both the LDS copy and the
+// registers, so every LDS access is 16 consecutive bytes per lane.  The targets of a
+// workgroup's rows are staged in LDS kTgCache at a time, so no target load sits
+// between the prefetch and its use.
+typedef __attribute__((address_space(3))) void* lds_vptr;
+constexpr int kPfThreads = 1024;
+constexpr int kTgCache = 1024;
+
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  // s_waitcnt with only vmcnt constrained (6-bit count: bits 3:0 and 15:14)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <typename Tin, typename Tout, int NV, int NL>
+__global__ __launch_bounds__(kPfThreads) void row_pf(RowArgs a, const Tin* z, Tout* dz) {
+  constexpr int NT = kPfThreads;
+  constexpr int VEC = Vec<Tin>::N;
+  constexpr int kFlags = 0x00020000;  // raw buffer, 32-bit data format
+  static_assert(NL > 0 && NL < NV, "split");
+  static_assert(Vec<Tout>::N == VEC, "same element width in and out");
+  __shared__ __attribute__((aligned(16))) u32x4 stage[NL * NT];
+  __shared__ long long tgc[kTgCache];
+  __shared__ float shm[NT / kWave], shs[NT / kWave];
+  __shared__ float sh_zy;
+  const int wave = threadIdx.x / kWave;
+  const int nvec = (int)(a.V / VEC);
+  const int64_t G = gridDim.x;
+  const int row_bytes = (int)(a.V * (int64_t)sizeof(Tin));
+  // target of this workgroup's k-th row (k within the cached batch)
+  auto load_targets = [&](int64_t k0) {
+    __syncthreads();
+    for (int t = threadIdx.x; t < kTgCache; t += NT) {
+      const int64_t r = blockIdx.x + (k0 + t) * G;
+      tgc[t] = r < a.T ? a.tg[r] : a.ignore;
+    }
+    __syncthreads();
+  };
+  auto live_row = [&](int64_t r, long long y) { return r < a.T && row_valid(y, a.V, a.ignore); };
+  // the buffer over row r's logits, or an empty one (ignored row, past the end)
+  auto row_rsrc = [&](int64_t r, bool live) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(z + (live ? r : 0) * a.ldz), (short)0,
+                                             live ? row_bytes : 0, kFlags);
+  };
+  auto stage_row = [&](int64_t r, bool live) {
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(r, live);
+    // lane offset in a VGPR, the vector index's offset in an SGPR
+    const uint32_t voff = threadIdx.x * 16u;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_vptr)(stage + i * NT + wave * kWave), 16,
+                                               voff, i * NT * 16, 0, 0);
+  };
+  // a target read from LDS is the same in every lane: keep it in scalar registers
+  auto uniform = [](long long v) {
+    const unsigned long long u = (unsigned long long)v;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+  };
+  load_targets(0);
+  stage_row(blockIdx.x, live_row(blockIdx.x, uniform(tgc[0])));
+  int64_t k = 0;  // index of `row` in this workgroup's sequence
+  for (int64_t row = blockIdx.x; row < a.T; row += G, ++k) {
+    if (k % kTgCache == 0 && k > 0) load_targets(k);
+    const long long y = uniform(tgc[k % kTgCache]);
+    const bool valid = row_valid(y, a.V, a.ignore);
+    // 1. the register part of the row (an empty buffer when the row is ignored)
+    Pack<Tin> xv[NV];
+    {
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(row, valid);
+      const uint32_t voff = threadIdx.x * 16u;
+#pragma unroll
+      for (int i = NL; i < NV; ++i)
+        xv[i].raw = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, i * NT * 16, 0));
+    }
+    // 2. all of it has landed (the LDS copy was issued one row ago)
+    wait_vm_n<0>();
+    __syncthreads();
+    // (the lane index is made opaque once per row, so the compiler recomputes the
+    // per-vector addresses and indices from it instead of holding dozens of them
+    // across the loop: no spills)
+    int tix = (int)threadIdx.x;
+    asm volatile("" : "+v"(tix));
+    if (valid) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) xv[i].raw = stage[i * NT + tix];
+    }
+    __syncthreads();
+    // 3. the next row's LDS copy overlaps this row's reduction and stores
+    {
+      const int64_t kn = k + 1;
+      const long long yn = uniform(kn % kTgCache == 0
+                                       ? (row + G < a.T ? a.tg[row + G] : a.ignore)
+                                       : tgc[kn % kTgCache]);
+      stage_row(row + G, live_row(row + G, yn));
+    }
+    Tout* dr = dz != nullptr ? dz + row * a.ldd : nullptr;
+    if (!valid) {
+      if (dr != nullptr) zero_row<Tout, VEC, NT>(dr, nvec);
+      if (threadIdx.x == 0) { a.row_loss[row] = 0.f; a.row_z[row] = 0.f; }
+      continue;
+    }
+    // 4. as the register-resident kernel; the target logit comes from the registers of
+    //    the thread that holds it
+    const int yv = (int)(y / VEC);
+    const int yj = (int)(y - (long long)yv * VEC);
+    float m = -INFINITY, s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = tix + i * NT;
+      if (v < nvec) {
+        if (v == yv) {
+#pragma unroll
+          for (int j = 0; j < VEC; ++j)
+            if (j == yj) sh_zy = to_f32(xv[i].v[j]);
+        }
+        float vm = to_f32(xv[i].v[0]);
+#pragma unroll
+        for (int j = 1; j < VEC; ++j) vm = fmaxf(vm, to_f32(xv[i].v[j]));
+        if (vm > m) { s *= ex<Tin>(m - vm); m = vm; }
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) s += ex<Tin>(to_f32(xv[i].v[j]) - m);
+      }
+    }
+    const float lse = block_lse<NT>(m, s, shm, shs);  // (its barrier publishes sh_zy)
+    if (threadIdx.x == 0) {
+      const float zt = a.zc * lse * lse;
+      a.row_loss[row] = (lse - sh_zy) + zt;
+      a.row_z[row] = zt;
+    }
+    if (dr == nullptr) continue;
+    const float scale = a.dloss / (float)a.cnt->n_valid;
+    const float coef = scale * fmaf(2.f * a.zc, lse, 1.f);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(xv[i].raw));
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = tix + i * NT;
+      if (v < nvec) {
+        float g[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) g[j] = coef * ex<Tin>(to_f32(xv[i].v[j]) - lse);
+        if (v == yv) {
+#pragma unroll
+          for (int j = 0; j < VEC; ++j)
+            if (j == yj) g[j] -= scale;
+        }
+        Pack<Tout> o;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) o.v[j] = from_f32<Tout>(g[j]);
+        store_pack(dr + (int64_t)v * VEC, o);
+      }
+    }
+  }
+  // the last LDS copy (an empty range unless the grid is cut short) lands before exit
+  wait_vm_n<0>();
+}
+
 // Streaming row kernel: any V, any alignment (VEC = 1) or aligned vectors (VEC > 1).
 // The second read of the row is a cached load (the row was just read, it is usually
 // still in L2 or the Infinity Cache).
@@ -337,8 +511,11 @@ __global__ __launch_bounds__(1024) void finalize(int64_t T_, const float* __rest
 }
 
 // Chooses and launches the row kernel for rows [0, a.T) of z/dz.
+constexpr int kPfStage = 9;  // vectors per thread staged in LDS (144 KB)
+
 template <typename Tin, typename Tout>
-hipError_t launch_rows(const RowArgs& a, const Tin* z, Tout* dz, hipStream_t st) {
+hipError_t launch_rows(const RowArgs& a, const Tin* z, Tout* dz, hipStream_t st,
+                       int64_t n_cu) {
   constexpr int VEC = Vec<Tin>::N;
   const bool vec = a.V % VEC == 0 && a.ldz % VEC == 0 && aligned16(z) &&
                    (dz == nullptr || (a.ldd % VEC == 0 && aligned16(dz)));
@@ -359,7 +536,15 @@ hipError_t launch_rows(const RowArgs& a, const Tin* z, Tout* dz, hipStream_t st)
       case 3: case 4: row_reg<Tin, Tout, 4, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
       case 5: case 6: case 7: case 8: row_reg<Tin, Tout, 8, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
       case 9: case 10: case 11: case 12: row_reg<Tin, Tout, 12, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
-      case 13: case 14: case 15: case 16: row_reg<Tin, Tout, 16, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      case 13: case 14: case 15: case 16:
+        if constexpr (std::is_same<Tin, bf16>::value && std::is_same<Tout, bf16>::value) {
+          // one persistent workgroup per CU, the next row prefetched into LDS
+          const unsigned g = (unsigned)(a.T < n_cu ? a.T : n_cu);
+          row_pf<Tin, Tout, 16, kPfStage><<<dim3(g), kPfThreads, 0, st>>>(a, z, dz);
+        } else {
+          row_reg<Tin, Tout, 16, 1024><<<grid, 1024, 0, st>>>(a, z, dz);
+        }
+        break;
       default: row_stream<Tin, Tout, VEC, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
     }
   } else {
