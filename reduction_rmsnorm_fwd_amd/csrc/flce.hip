@@ -7,11 +7,16 @@
 //   Z = H W^T,  (loss, dZ) = cross_entropy(Z),  dH = dZ W,  dW = dZ^T H
 // The full [T, V] logits never exist: tokens go through in chunks of C rows, and per
 // chunk
-//   1. Z_c = H_c W^T            bf16 MFMA, fp32 out, into a [C, V] fp32 buffer
-//   2. CE over Z_c's rows       the logits product also leaves each row's online
-//                               logsumexp partials, so one read of Z_c gives the loss
-//                               rows and dZ_c (bf16), scaled by dloss/N with N counted
-//                               once over all T targets up front
+//   1. Z_c = H_c W^T            bf16 MFMA; the epilogue never stores Z_c itself: per
+//                               row and 128-column block it keeps the online-logsumexp
+//                               partial (m, sum exp(z - m)), writes E = exp(z - m) in
+//                               bf16 into the chunk's dZ rows, and the target's logit
+//                               in fp32
+//   2. CE over the chunk's rows the partials give each row's lse, hence its loss (with
+//                               the target logit); one in-place pass turns E into
+//                               dZ_c = (dloss/N)(E exp(m - lse)(1 + 2 c lse) - onehot)
+//                               (the target column from its fp32 logit), with N
+//                               counted once over all T targets up front
 //   3. dH_c = dZ_c W            bf16 MFMA reading W as it is stored ([V, H]: k-major
 //                               for this product), bf16 out
 //   4. dW (+)= dZ_c^T H_c       bf16 MFMA reading dZ_c and H_c as stored (token-major:
@@ -35,13 +40,13 @@ namespace {
 constexpr int64_t kAutoChunk = 2048;
 
 struct Layout {
-  int64_t C, Vpad, ldz;
+  int64_t C, Vpad;
   bool pair;        // dW over two chunks per product
   int64_t dzrows;   // rows of the dZ buffer (one chunk, or two when paired)
   int64_t nparts;   // logsumexp partials per logits row
   int64_t dh_smax;  // split-K slice bound of the dH product (1: no split)
-  size_t off_cnt, off_loss, off_z, off_zbuf, off_dz, off_dw, off_part, off_stats, off_idx,
-      off_pos, off_tgv, off_hv, off_dhv, total;
+  size_t off_cnt, off_loss, off_z, off_dz, off_dw, off_part, off_stats, off_idx,
+      off_pos, off_tgv, off_hv, off_dhv, off_zy, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
@@ -50,7 +55,6 @@ Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
   if (C > T) C = T > 0 ? T : 1;
   L.C = C;
   L.Vpad = align_up((size_t)V, 64);
-  L.ldz = L.Vpad;
   L.pair = T > C;
   L.dzrows = L.pair ? 2 * C : C;
   size_t o = 0;
@@ -58,7 +62,6 @@ Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
   L.off_cnt = take(256);
   L.off_loss = take((size_t)(T > 0 ? T : 1) * 4);
   L.off_z = take((size_t)(T > 0 ? T : 1) * 4);
-  L.off_zbuf = take((size_t)C * L.ldz * 4);
   L.off_dz = take((size_t)L.dzrows * L.Vpad * 2);
   L.off_dw = take(dw_dtype == FO_BF16 ? (size_t)V * H * 4 : 0);
   // dH of a chunk has few 256x256 tiles: split it over the vocabulary, the slice count
@@ -77,6 +80,7 @@ Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
   L.off_tgv = take(Tn * 8);
   L.off_hv = take(Tn * H * 2);
   L.off_dhv = take(Tn * H * 2);
+  L.off_zy = take(Tn * 4);
   L.total = o;
   return L;
 }
@@ -120,17 +124,18 @@ __global__ __launch_bounds__(256) void scatter_rows(const bf16* __restrict__ dHv
         p >= 0 ? *reinterpret_cast<const u32x4*>(src + v * 8) : u32x4{0, 0, 0, 0};
 }
 
-// Cross-entropy of one chunk of logits Z (fp32, rows of stride ldz) whose per-row
-// online-logsumexp partials were produced by the logits product: merge the row's
-// partials (fixed order) into lse, write the row's loss, then one pass over the row
-// writes dZ = (dloss/N)(softmax (1 + 2 c lse) - onehot) in bf16, and zeros in the
-// row's padding columns [V, ldd) (the K tail of the dH product).  Rows past the
-// chunk's valid count are never read by the products and are left alone.  One
-// 256-thread workgroup per row.
+// Cross-entropy of one chunk from what the logits product left: per row its
+// online-logsumexp partials (m_p, s_p) for each 128-column block p, its target logit zy,
+// and (gradient wanted) E = exp(z - m_p) in bf16 in the row of dZ.  Merges the row's
+// partials (fixed order) into lse, writes the row's loss, then rewrites the row in place
+// as dZ = (dloss/N)(softmax (1 + 2 c lse) - onehot) in bf16, softmax = E exp(m_p - lse),
+// the target column computed from zy; zeros go to the padding columns [V, ldd) (the K
+// tail of the dH product).  Rows past the chunk's valid count are never read by the
+// products and are left alone.  One 256-thread workgroup per row.
 constexpr int kApplyThreads = 256;
 __global__ __launch_bounds__(kApplyThreads) void ce_apply(
-    const float* __restrict__ Z, int64_t ldz, const float2* __restrict__ stats, int64_t nparts,
-    const int64_t* __restrict__ tg, const xent::Counters* __restrict__ cnt, int64_t rows_base,
+    const float2* __restrict__ stats, int64_t nparts, const int64_t* __restrict__ tg,
+    const float* __restrict__ zy, const xent::Counters* __restrict__ cnt, int64_t rows_base,
     int64_t rows, int64_t V, float zc, float dloss, bf16* __restrict__ dZ, int64_t ldd,
     float* __restrict__ row_loss, float* __restrict__ row_z) {
   __shared__ float shm[kApplyThreads / kWave], shs[kApplyThreads / kWave];
@@ -145,38 +150,34 @@ __global__ __launch_bounds__(kApplyThreads) void ce_apply(
     lse_merge(m, s, q.x, q.y);
   }
   const float lse = xent::block_lse<kApplyThreads>(m, s, shm, shs);
-  const float* zr = Z + row * ldz;
   const long long y = tg[row];
+  const float zt_logit = zy[row];
   if (threadIdx.x == 0) {
     const float zt = zc * lse * lse;
-    row_loss[row] = (lse - zr[y]) + zt;
+    row_loss[row] = (lse - zt_logit) + zt;
     row_z[row] = zt;
   }
   if (dZ == nullptr) return;
   const float scale = dloss / (float)cnt->n_valid;
   const float coef = scale * fmaf(2.f * zc, lse, 1.f);
+  const float gy = coef * __expf(zt_logit - lse) - scale;  // the target column
   bf16* dr = dZ + row * ldd;
-  if (V % 4 == 0) {
-    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-    for (int64_t v = threadIdx.x; v < V / 4; v += kApplyThreads) {
-      typedef float f32x4 __attribute__((ext_vector_type(4)));
-      const f32x4 z4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(zr) + v);
-      const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
-      union { u32x2 raw; bf16 e[4]; } o;
+  constexpr int kCols = gemm::kStatsCols;
+  const int64_t V8 = V / 8 * 8;  // 8-column groups never straddle a 128-column block
+  for (int64_t v = (int64_t)threadIdx.x * 8; v < V8; v += kApplyThreads * 8) {
+    const float f = coef * __expf(sp[v / kCols].x - lse);
+    union { u32x4 raw; bf16 e[8]; } o;
+    o.raw = *reinterpret_cast<const u32x4*>(dr + v);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float g = coef * __expf(zz[j] - lse);
-        if (v * 4 + j == y) g -= scale;
-        o.e[j] = from_f32<bf16>(g);
-      }
-      *reinterpret_cast<u32x2*>(dr + v * 4) = o.raw;
+    for (int j = 0; j < 8; ++j) {
+      const float g = v + j == y ? gy : f * to_f32(o.e[j]);
+      o.e[j] = from_f32<bf16>(g);
     }
-  } else {
-    for (int64_t v = threadIdx.x; v < V; v += kApplyThreads) {
-      float g = coef * __expf(zr[v] - lse);
-      if (v == y) g -= scale;
-      dr[v] = from_f32<bf16>(g);
-    }
+    *reinterpret_cast<u32x4*>(dr + v) = o.raw;
+  }
+  for (int64_t v = V8 + threadIdx.x; v < V; v += kApplyThreads) {
+    const float g = v == y ? gy : coef * __expf(sp[v / kCols].x - lse) * to_f32(dr[v]);
+    dr[v] = from_f32<bf16>(g);
   }
   for (int64_t v = V + threadIdx.x; v < ldd; v += kApplyThreads) dr[v] = from_f32<bf16>(0.f);
 }
@@ -194,7 +195,7 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
   const long long* nv = &cnt->n_valid;
   float* row_loss = reinterpret_cast<float*>(ws + L.off_loss);
   float* row_z = reinterpret_cast<float*>(ws + L.off_z);
-  float* Z = reinterpret_cast<float*>(ws + L.off_zbuf);
+  float* zy = reinterpret_cast<float*>(ws + L.off_zy);
   bf16* dZbuf = reinterpret_cast<bf16*>(ws + L.off_dz);
   int* idx = reinterpret_cast<int*>(ws + L.off_idx);
   int* pos_of = reinterpret_cast<int*>(ws + L.off_pos);
@@ -217,18 +218,20 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
       const int64_t slot = L.pair ? (c0 / L.C) % 2 : 0;
       const int64_t koff = slot * L.C;
       bf16* dZ = dZbuf + koff * L.Vpad;
-      // 1. logits of the chunk's valid rows
+      // 1. logits of the chunk's valid rows: row partials, target logits and (gradient
+      //    wanted) exp(z - m) in the chunk's dZ rows
       gemm::Args g;
       g.A = Hv + c0 * H; g.lda = H;
       g.B = W; g.ldb = H;
-      g.C = Z; g.ldc = L.ldz;
+      g.C = need_grad ? dZ : nullptr; g.ldc = L.Vpad;
       g.M = cl; g.N = V; g.K = H;
       g.dev_count = nv; g.count_base = c0; g.dev_dim = 1;
       g.stats = stats; g.stats_ld = L.nparts;
-      FO_HIP(gemm::run<gemm::kStoreF32Stats>(g, gemm::kWide, st));
-      // 2. loss rows and dZ from the row partials: one read of the logits
+      g.tgt = tgv + c0; g.zy = zy + c0;
+      FO_HIP(gemm::run<gemm::kStoreExpStats>(g, gemm::kWide, st));
+      // 2. loss rows, and dZ in place from the row partials
       ce_apply<<<(unsigned)cl, kApplyThreads, 0, st>>>(
-          Z, L.ldz, stats, L.nparts, tgv + c0, cnt, c0, cl, V, zc, dloss,
+          stats, L.nparts, tgv + c0, zy + c0, cnt, c0, cl, V, zc, dloss,
           need_grad ? dZ : nullptr, L.Vpad, row_loss + c0, row_z + c0);
       FO_HIP(hipGetLastError());
       // 3. dH rows of the chunk: dZ_c [cl, Vpad] times W read k-major ([V, H]; its rows

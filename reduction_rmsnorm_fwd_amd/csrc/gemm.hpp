@@ -33,9 +33,12 @@ namespace {  // internal linkage: each including source file gets its own copy
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// kStoreF32Stats: fp32 store plus, per row, the (max, sum of exp(x - max)) pair of each
-// wave's WN columns (an online-logsumexp partial) at stats[row * stats_ld + col / WN].
-enum OutMode { kStoreF32 = 0, kAccumF32 = 1, kStoreBF16 = 2, kStoreF32Stats = 3 };
+// kStoreExpStats (logits of a cross-entropy): per row and per wave's WN columns, the
+// online-logsumexp partial (m, sum of exp(x - m)) at stats[row * stats_ld + col / WN];
+// C (bf16, may be null: then nothing else is stored) receives exp(x - m) of that
+// partial's m, in (0, 1]; and the fp32 value at the row's target column tgt[row] goes to
+// zy[row].
+enum OutMode { kStoreF32 = 0, kAccumF32 = 1, kStoreBF16 = 2, kStoreExpStats = 3 };
 
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
@@ -64,8 +67,10 @@ struct Args {
   // k-major B only: B has b_rows k-rows (counted from the product's first k); the
   // rows past them read as zeros.  0: all K rows exist.
   int64_t b_rows = 0;
-  float2* stats = nullptr;  // kStoreF32Stats only
+  float2* stats = nullptr;  // kStoreExpStats only
   int64_t stats_ld = 0;
+  const int64_t* tgt = nullptr;  // kStoreExpStats: target column of each row
+  float* zy = nullptr;           // kStoreExpStats: the row's value at that column
 };
 
 constexpr int64_t kCus = 256;
@@ -330,35 +335,52 @@ __device__ __forceinline__ void init_tile(const Args& a, f32x16 (&acc)[FM][FN], 
   }
 }
 
-// Row partials of an online logsumexp over this wave's WN columns (kStoreF32Stats).
-// Lane (fr, fh) holds, for each of its rows, the FN values at columns j*32 + fr.  The
-// row max is folded over j and over the 32 lanes of the half-wave (butterfly), then the
-// sum of exp(x - max) the same way; lane fr == 0 writes the pair.
-// Columns at or past N do not take part.
+// Epilogue of kStoreExpStats.  Lane (fr, fh) holds, for each of its rows, the FN values
+// at columns j*32 + fr of this wave's WN.  Per row: the value at the target column goes
+// to zy if that column is one of this wave's; the max over the wave's columns is folded
+// over j and over the 32 lanes of the half-wave (butterfly); every value is replaced by
+// exp(x - max) and their sum folded the same way; lane fr == 0 writes (max, sum).
+// Columns at or past N do not take part (their values are not stored).
 template <int BM, int WM, int WN, int FM, int FN>
-__device__ __forceinline__ void row_stats(const Args& a, f32x16 (&acc)[FM][FN], int64_t m0,
+__device__ __forceinline__ void exp_stats(const Args& a, f32x16 (&acc)[FM][FN], int64_t m0,
                                           int64_t n0, int wm, int wn, int fr, int fh) {
   const int64_t nb = n0 + wn * WN;  // first column of this wave
   const int64_t part = nb / WN;
   if (nb >= a.N) return;  // no partial slot for a wave wholly past the last column
+  // the wave's WM (= 64) rows: lane l loads row l's target, as a column relative to the
+  // wave's first column, or -1 when it is not one of the wave's columns; the lanes that
+  // hold a row's values fetch it with a shuffle
+  static_assert(WM == 64, "one target per lane");
+  const int lane = fr + 32 * fh;
+  const int64_t lrow = m0 + wm * WM + lane;
+  const int64_t ly = lrow < a.M ? a.tgt[lrow] : -1;
+  const int lrel = (ly >= nb && ly < nb + WN && ly < a.N) ? (int)(ly - nb) : -1;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      // the row's max over the wave's columns first (max only), then one exp per value
-      float m = -INFINITY;
+      const int rw = i * 32 + 8 * (r / 4) + 4 * fh + (r % 4);  // row within the wave
+      const int64_t row = m0 + wm * WM + rw;
+      const int yrel = __shfl(lrel, rw, 64);
+      float m = -INFINITY, zv = 0.f;
+      bool has = false;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j) {
         if (nb + j * 32 + fr < a.N) m = fmaxf(m, acc[i][j][r]);
+        if (yrel == j * 32 + fr) { zv = acc[i][j][r]; has = true; }
+      }
+      if (has) a.zy[row] = zv;
 #pragma unroll
       for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
       float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        if (nb + j * 32 + fr < a.N) s += __expf(acc[i][j][r] - m);
+      for (int j = 0; j < FN; ++j) {
+        const float e = __expf(acc[i][j][r] - m);
+        acc[i][j][r] = e;
+        if (nb + j * 32 + fr < a.N) s += e;
+      }
 #pragma unroll
       for (int o = 1; o < 32; o <<= 1) s += __shfl_xor(s, o, 64);
-      const int64_t row = m0 + wm * WM + i * 32 + 8 * (r / 4) + 4 * fh + (r % 4);
       if (fr == 0 && row < a.M) a.stats[row * a.stats_ld + part] = make_float2(m, s);
     }
 }
@@ -641,8 +663,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_nt_dma(Args a_in) {
     if (kt + 1 < nk) step(sA1, sB1, sA0, sB0, kt + 1);
   }
 
-  if constexpr (MODE == kStoreF32Stats) row_stats<BM, WM, WN, FM, FN>(a, acc, m0, n0, wm, wn, fr, fh);
-  store_tile<MODE == kStoreF32Stats ? kStoreF32 : MODE, BM, BN, WM, WN, FM, FN>(a, acc, m0, n0, wm, wn, fr, fh);
+  if constexpr (MODE == kStoreExpStats) {
+    exp_stats<BM, WM, WN, FM, FN>(a, acc, m0, n0, wm, wn, fr, fh);
+    if (a.C != nullptr) store_tile<kStoreBF16, BM, BN, WM, WN, FM, FN>(a, acc, m0, n0, wm, wn, fr, fh);
+  } else {
+    store_tile<MODE, BM, BN, WM, WN, FM, FN>(a, acc, m0, n0, wm, wn, fr, fh);
+  }
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, int ST, int SH, int MODE, bool AT = false,
@@ -697,7 +723,7 @@ inline bool dma_ok(const Args& a, int bm, int bn) {
 // p[k*ld + x]); those layouts exist in the direct-to-LDS kernel only.
 template <int MODE, bool AT = false, bool BT = false>
 hipError_t run(const Args& a, TileShape shape, hipStream_t st) {
-  if constexpr (MODE == kStoreF32Stats) {
+  if constexpr (MODE == kStoreExpStats) {
     // the row partials come from the direct-to-LDS kernel's wide tile only (its waves
     // cover kStatsCols columns each)
     if (shape != kWide || !dma_ok<AT, BT>(a, 256, 256)) return hipErrorInvalidValue;
@@ -719,7 +745,7 @@ hipError_t run(const Args& a, TileShape shape, hipStream_t st) {
   }
 }
 
-// columns per row partial of kStoreF32Stats (the wide tile's wave width)
+// columns per row partial of kStoreExpStats (the wide tile's wave width)
 constexpr int kStatsCols = 128;
 
 // Split-K plan for a product whose 256x256 tiles cannot fill the chip: the number of
