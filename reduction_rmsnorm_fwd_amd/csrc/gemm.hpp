@@ -335,12 +335,37 @@ __device__ __forceinline__ void init_tile(const Args& a, f32x16 (&acc)[FM][FN], 
   }
 }
 
+// All-reduce over each 32-lane half of a wave (the 32 columns of a fragment row): xor
+// 1 and 2 within quads, then the half-row and row mirrors (DPP, no LDS traffic), then
+// xor 16 (ds_swizzle, bit-mask mode) — two LDS-path operations instead of five.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xor16_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+__device__ __forceinline__ float half_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm 1,0,3,2
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm 2,3,0,1
+  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+  return fmaxf(x, xor16_f(x));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  x += dpp_f<0x140>(x);
+  return x + xor16_f(x);
+}
+
 // Epilogue of kStoreExpStats.  Lane (fr, fh) holds, for each of its rows, the FN values
 // at columns j*32 + fr of this wave's WN.  Per row: the value at the target column goes
-// to zy if that column is one of this wave's; the max over the wave's columns is folded
-// over j and over the 32 lanes of the half-wave (butterfly); every value is replaced by
-// exp(x - max) and their sum folded the same way; lane fr == 0 writes (max, sum).
-// Columns at or past N do not take part (their values are not stored).
+// to zy if that column is one of this wave's; the max over the wave's columns is reduced
+// over j and over the 32 lanes of the half-wave; every value is replaced by exp(x - max)
+// and their sum reduced the same way; lane fr == 0 writes (max, sum).  Columns at or
+// past N do not take part (their values are not stored).
 template <int BM, int WM, int WN, int FM, int FN>
 __device__ __forceinline__ void exp_stats(const Args& a, f32x16 (&acc)[FM][FN], int64_t m0,
                                           int64_t n0, int wm, int wn, int fr, int fh) {
@@ -348,39 +373,47 @@ __device__ __forceinline__ void exp_stats(const Args& a, f32x16 (&acc)[FM][FN], 
   const int64_t part = nb / WN;
   if (nb >= a.N) return;  // no partial slot for a wave wholly past the last column
   // the wave's WM (= 64) rows: lane l loads row l's target, as a column relative to the
-  // wave's first column, or -1 when it is not one of the wave's columns; the lanes that
-  // hold a row's values fetch it with a shuffle
+  // wave's first column, or -1 when it is not one of the wave's columns; most waves hold
+  // no target at all and skip the lookup
   static_assert(WM == 64, "one target per lane");
   const int lane = fr + 32 * fh;
   const int64_t lrow = m0 + wm * WM + lane;
   const int64_t ly = lrow < a.M ? a.tgt[lrow] : -1;
   const int lrel = (ly >= nb && ly < nb + WN && ly < a.N) ? (int)(ly - nb) : -1;
+  if (__ballot(lrel >= 0) != 0) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rw = i * 32 + 8 * (r / 4) + 4 * fh + (r % 4);  // row within the wave
+        const int yrel = __shfl(lrel, rw, 64);
+        float zv = 0.f;
+        bool has = false;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (yrel == j * 32 + fr) { zv = acc[i][j][r]; has = true; }
+        if (has) a.zy[m0 + wm * WM + rw] = zv;
+      }
+  }
+  const bool all_cols = nb + WN <= a.N;  // no column of the wave is past N
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int rw = i * 32 + 8 * (r / 4) + 4 * fh + (r % 4);  // row within the wave
-      const int64_t row = m0 + wm * WM + rw;
-      const int yrel = __shfl(lrel, rw, 64);
-      float m = -INFINITY, zv = 0.f;
-      bool has = false;
+      const int64_t row = m0 + wm * WM + i * 32 + 8 * (r / 4) + 4 * fh + (r % 4);
+      float m = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if (nb + j * 32 + fr < a.N) m = fmaxf(m, acc[i][j][r]);
-        if (yrel == j * 32 + fr) { zv = acc[i][j][r]; has = true; }
-      }
-      if (has) a.zy[row] = zv;
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      for (int j = 0; j < FN; ++j)
+        if (all_cols || nb + j * 32 + fr < a.N) m = fmaxf(m, acc[i][j][r]);
+      m = half_max(m);
       float s = 0.f;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const float e = __expf(acc[i][j][r] - m);
         acc[i][j][r] = e;
-        if (nb + j * 32 + fr < a.N) s += e;
+        if (all_cols || nb + j * 32 + fr < a.N) s += e;
       }
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) s += __shfl_xor(s, o, 64);
+      s = half_sum(s);
       if (fr == 0 && row < a.M) a.stats[row * a.stats_ld + part] = make_float2(m, s);
     }
 }
