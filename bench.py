@@ -407,7 +407,7 @@ def gpu_bench(args):
         ach = work / (ms * 1e-3) / 1e12
         out["roofline"] = {
             "kernel": "fo_flce_fwd_bwd (per call: per 2048-row chunk the logits and split-K dH "
-                      "bf16 MFMA products and ce_apply; the dW product per chunk pair; "
+                      "bf16 MFMA products and ce_apply; one dW product over all chunks; "
                       "compaction, gather/scatter)",
             "bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),

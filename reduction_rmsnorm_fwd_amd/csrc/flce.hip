@@ -19,11 +19,13 @@
 //                               counted once over all T targets up front
 //   3. dH_c = dZ_c W            bf16 MFMA reading W as it is stored ([V, H]: k-major
 //                               for this product), bf16 out
-//   4. dW (+)= dZ_c^T H_c       bf16 MFMA reading dZ_c and H_c as stored (token-major:
-//                               k-major for this product), fp32 accumulation across
-//                               chunks in dW (or a workspace buffer, cast to bf16 once
-//                               at the end); two chunks per product when there are
-//                               several, so dW is read and rewritten half as often
+//   4. dW (+)= dZ_g^T H_g       bf16 MFMA reading dZ and H as stored (token-major:
+//                               k-major for this product) over a group of chunks whose
+//                               dZ rows sit together in one buffer (as many chunks as
+//                               fit in kDzBudget: all four of an 8192-token batch with
+//                               a 128K vocabulary), fp32 accumulation across groups in
+//                               dW (or a workspace buffer, cast to bf16 once at the
+//                               end); one group means dW is written once, never read
 // The k-major operands go through LDS untransposed and are read with the transposing
 // LDS loads of gfx950, so no operand is ever transposed in memory.
 // Rows whose target is ignored (or out of range) contribute nothing, so the valid rows
@@ -38,11 +40,13 @@ namespace fo {
 namespace {
 
 constexpr int64_t kAutoChunk = 2048;
+// bytes of bf16 dZ rows kept for one dW product (a group of chunks)
+constexpr int64_t kDzBudget = (int64_t)2 << 30;
 
 struct Layout {
   int64_t C, Vpad;
-  bool pair;        // dW over two chunks per product
-  int64_t dzrows;   // rows of the dZ buffer (one chunk, or two when paired)
+  int64_t group;    // chunks per dW product
+  int64_t dzrows;   // rows of the dZ buffer (group chunks)
   int64_t nparts;   // logsumexp partials per logits row
   int64_t dh_smax;  // split-K slice bound of the dH product (1: no split)
   size_t off_cnt, off_loss, off_z, off_dz, off_dw, off_part, off_stats, off_idx,
@@ -55,8 +59,10 @@ Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
   if (C > T) C = T > 0 ? T : 1;
   L.C = C;
   L.Vpad = align_up((size_t)V, 64);
-  L.pair = T > C;
-  L.dzrows = L.pair ? 2 * C : C;
+  const int64_t nchunks = T > C ? ceil_div(T, C) : 1;
+  const int64_t fit = kDzBudget / (C * L.Vpad * 2);
+  L.group = nchunks < fit ? nchunks : (fit > 1 ? fit : 1);
+  L.dzrows = L.group * C;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
   L.off_cnt = take(256);
@@ -213,9 +219,9 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
     const bool need_grad = dH != nullptr || dW != nullptr;
     for (int64_t c0 = 0; c0 < T; c0 += L.C) {
       const int64_t cl = (T - c0 < L.C) ? T - c0 : L.C;  // rows at most (valid rows: on device)
-      // a pair of chunks shares the dZ buffer: chunk 0 of the pair in rows [0, C),
-      // chunk 1 in rows [C, 2C), so the pair's dZ rows are contiguous for dW
-      const int64_t slot = L.pair ? (c0 / L.C) % 2 : 0;
+      // the chunks of a group share the dZ buffer, chunk s of the group in rows
+      // [sC, (s+1)C), so the group's dZ rows are contiguous for dW
+      const int64_t slot = (c0 / L.C) % L.group;
       const int64_t koff = slot * L.C;
       bf16* dZ = dZbuf + koff * L.Vpad;
       // 1. logits of the chunk's valid rows: row partials, target logits and (gradient
@@ -258,10 +264,10 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
           FO_HIP((gemm::run<gemm::kStoreBF16, false, true>(h, gemm::kNarrow, st)));
         }
       }
-      // 4. dW contribution of the pair's rows, once both chunks of a pair are in (or at
+      // 4. dW contribution of the group's rows, once all its chunks are in (or at
       //    the end): dZ^T Hv with both operands read k-major (token-major as stored),
-      //    K = the valid rows since the pair's first row, read on the device.
-      if (dW != nullptr && (!L.pair || slot == 1 || c0 + L.C >= T)) {
+      //    K = the valid rows since the group's first row, read on the device.
+      if (dW != nullptr && (slot == L.group - 1 || c0 + L.C >= T)) {
         const int64_t base = c0 - koff;
         gemm::Args w;
         w.A = dZbuf; w.lda = L.Vpad;
