@@ -21,11 +21,12 @@
 //                               for this product), bf16 out
 //   4. dW (+)= dZ_g^T H_g       bf16 MFMA reading dZ and H as stored (token-major:
 //                               k-major for this product) over a group of chunks whose
-//                               dZ rows sit together in one buffer (as many chunks as
-//                               fit in kDzBudget: all four of an 8192-token batch with
-//                               a 128K vocabulary), fp32 accumulation across groups in
-//                               dW (or a workspace buffer, cast to bf16 once at the
-//                               end); one group means dW is written once, never read
+//                               dZ rows sit together in one buffer (at most four
+//                               chunks within kDzBudget: all four of an 8192-token
+//                               batch with a 128K vocabulary), fp32 accumulation
+//                               across groups in dW (or a workspace buffer, cast to
+//                               bf16 once at the end); one group means dW is written
+//                               once, never read
 // The k-major operands go through LDS untransposed and are read with the transposing
 // LDS loads of gfx950, so no operand is ever transposed in memory.
 // Rows whose target is ignored (or out of range) contribute nothing, so the valid rows
@@ -40,7 +41,9 @@ namespace fo {
 namespace {
 
 constexpr int64_t kAutoChunk = 2048;
-// bytes of bf16 dZ rows kept for one dW product (a group of chunks)
+// a dW product covers a group of at most kMaxGroup chunks whose bf16 dZ rows take at
+// most kDzBudget bytes (so the dZ buffer scales with the chunk size the caller picks)
+constexpr int64_t kMaxGroup = 4;
 constexpr int64_t kDzBudget = (int64_t)2 << 30;
 
 struct Layout {
@@ -60,8 +63,9 @@ Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
   L.C = C;
   L.Vpad = align_up((size_t)V, 64);
   const int64_t nchunks = T > C ? ceil_div(T, C) : 1;
-  const int64_t fit = kDzBudget / (C * L.Vpad * 2);
-  L.group = nchunks < fit ? nchunks : (fit > 1 ? fit : 1);
+  int64_t fit = kDzBudget / (C * L.Vpad * 2);
+  fit = fit < kMaxGroup ? (fit > 1 ? fit : 1) : kMaxGroup;
+  L.group = nchunks < fit ? nchunks : fit;
   L.dzrows = L.group * C;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };

@@ -37,6 +37,7 @@ def compare(h, w, t, zc, o, dloss=1.0):
     (37, 64, 1000, 16),        # ragged chunks and tiles
     (200, 256, 4097, 64),      # vocabulary not a multiple of the vector
     (300, 512, 8192, 0),
+    (200, 128, 1000, 16),      # 13 chunks: dW over four groups, accumulated across them
 ])
 def test_small(gpu, T, H, V, chunk):
     cfg = synth.flce_small(T, H, V, seed=T)
@@ -58,11 +59,14 @@ def test_chunk_size_and_dweight_dtype(gpu):
     i = synth.flce_inputs(cfg)
     a = run(gpu, i["hidden"], i["weight"], i["targets"], cfg.z_loss, chunk=384)
     b = run(gpu, i["hidden"], i["weight"], i["targets"], cfg.z_loss, chunk=128)
+    g = run(gpu, i["hidden"], i["weight"], i["targets"], cfg.z_loss, chunk=32)  # 3 dW groups
     c = run(gpu, i["hidden"], i["weight"], i["targets"], cfg.z_loss, chunk=128,
             dwt=torch.bfloat16)
     assert abs(a["loss"].item() - b["loss"].item()) <= 1e-6 * abs(a["loss"].item())
     assert torch.equal(a["dhidden"], b["dhidden"])  # rows do not depend on the chunking
     check_bf16(b["dweight"], a["dweight"].double(), "dweight chunk")
+    assert torch.equal(a["dhidden"], g["dhidden"])
+    check_bf16(g["dweight"], a["dweight"].double(), "dweight groups")
     assert c["dweight"].dtype == torch.bfloat16
     assert torch.equal(c["dweight"], b["dweight"].to(torch.bfloat16))
 
