@@ -205,6 +205,32 @@ def measured_peaks(fo, torch, stream, med):
                     "fo_probe_mfma (v_mfma_f32_32x32x16_bf16 on registers, 2 waves/SIMD)"}
 
 
+def same_size_copies(fo, torch, stream, med, byte_counts, reps):
+    """Per byte count B: the isolated time (caches flushed before each call, median of
+    reps) of the library's streaming copy probe moving B/2 bytes in and B/2 out, i.e. the
+    ceiling a plain copy of the same size reaches, start-up and drain included."""
+    halves = {b: (int(b) // 2) // 16 * 16 for b in byte_counts}
+    n = max(halves.values()) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    out = {}
+    for b, h in halves.items():
+        s_, d_ = src[:h // 4], dst[:h // 4]
+        ts = []
+        for _ in range(reps):
+            scratch.fill_(1.0)
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fo.fo_probe_copy(s_, d_)
+            e.record(stream)
+            e.synchronize()
+            ts.append(a.elapsed_time(e))
+        out[b] = med(ts)
+    del src, dst, scratch
+    return out
+
+
 def unaligned_lines(fo, synth, torch, stream, med):
     """The scalar (unaligned) paths at the Llama-3-8B token count, reported apart from
     the aligned per-op lines: RMSNorm with d = 4097 and SwiGLU with F = 14337 (rows not
@@ -326,6 +352,9 @@ def gpu_bench(args):
         return v[len(v) // 2]
 
     peaks = None if args.no_probes else measured_peaks(fo, torch, stream, med)
+    hbm_bytes = [work for (_, _, work, bound), t in zip(wl.ops, iso) if bound == "hbm" and t]
+    same = (None if args.no_probes or not hbm_bytes
+            else same_size_copies(fo, torch, stream, med, hbm_bytes, args.iso_reps))
     unaligned = None if args.no_probes or only else unaligned_lines(fo, synth, torch, stream, med)
     traffic = measured_traffic()
     per_op = {}
@@ -352,6 +381,9 @@ def gpu_bench(args):
         if peaks is not None:
             if bound == "hbm":
                 e["frac_measured_copy"] = round(e["GBps"] / peaks["copy_GBps"], 4)
+                if same is not None and work in same:
+                    e["same_size_copy_ms"] = round(same[work], 4)
+                    e["frac_same_size_copy"] = round(same[work] / t_ref, 4)
             else:
                 e["frac_measured_mfma"] = round(e["TFLOPs"] / peaks["mfma_TFLOPs"], 4)
         e["traffic_MB"] = round(traffic[name] / 1e6, 1) if traffic and name in traffic else None
