@@ -146,9 +146,11 @@ int fo_xent_fwd_bwd(int dtype, int64_t T, int64_t V, const void* logits, int64_t
 /* ---- Fused linear cross-entropy ([HFK] Liger FusedLinearCrossEntropy: the lm-head
  * projection fused with the loss so the full logits never exist) ----
  * Computes the cross-entropy above on Z = hidden * weight^T without materialising Z:
- * tokens are processed in chunks of `chunk_tokens` (0 = automatic); per chunk
+ * tokens are processed in chunks of `chunk_tokens` (0 = automatic: 2048); per chunk
  *   Z_c = H_c W^T (bf16 MFMA, fp32 accumulate) -> dZ_c (bf16) -> dH_c = dZ_c W,
- *   dW += dZ_c^T H_c (fp32 accumulation across chunks).
+ *   and per group of up to four chunks (their bf16 dZ rows within 2 GiB)
+ *   dW += dZ_g^T H_g (fp32 accumulation across groups).  The workspace holds one
+ *   group's dZ rows, so it scales with chunk_tokens * V, not with T * V.
  *   hidden [T,H] and weight [V,H] bf16, contiguous rows, H % 8 == 0, 16-byte aligned.
  *   dhidden [T,H] bf16 (may be NULL), dweight [V,H] of dweight_dtype FO_F32 or FO_BF16
  *   (cast once at the end; may be NULL).  Scalars as for fo_xent_fwd_bwd.
