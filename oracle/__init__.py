@@ -19,8 +19,9 @@ states the textbook reading it implements and the readings taken where the pages
 are silent.  Every function is pinned by the ``-m "not gpu"`` tests against closed
 forms, invariants, finite differences and independent library routines.  Parity
 unpinned by the pages themselves (fixed by a stated reading, pinned only against
-that reading): the RoPE pairing convention, the z-loss formula, and the position
-of eps inside the RMSNorm root.
+that reading): the RoPE pairing convention, the z-loss formula, the position
+of eps inside the RMSNorm root, and the AdamW formula behind the Adam kernel's
+printed signature.
 """
 from .ops import (  # noqa: F401
     rmsnorm_fwd, rmsnorm_bwd,
@@ -28,4 +29,5 @@ from .ops import (  # noqa: F401
     silu, swiglu_fwd, swiglu_bwd,
     xent_fwd_bwd, xent_rows,
     flce_fwd_bwd,
+    adamw_scalars, adamw_step,
 )

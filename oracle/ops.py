@@ -241,3 +241,40 @@ def flce_fwd_bwd(hidden, weight, targets, ignore_index=-100, z_loss=0.0, dloss=1
     return dict(loss=float(loss_sum / n) if n else 0.0,
                 z_loss=float(z_sum / n) if n else 0.0,
                 n_valid=n, n_bad=int(bad.sum()), dhidden=dH, dweight=dW)
+
+
+# ---------------------------------------------------------------------------
+# AdamW step — [FastLLM] 关键实现细节, "Triton Adam 优化器": one fused pass over a
+# parameter tensor that scales the gradient (a device scalar), updates both moments,
+# applies weight decay and the parameter update, and does nothing at all while a
+# device no-op flag is set; the host supplies step_size, bias_correction and
+# decay_factor.  The page prints the kernel's signature but no formula, so the reading
+# is the textbook AdamW with decoupled weight decay (Loshchilov & Hutter) in the
+# bias-corrected form whose host scalars those names describe:
+#   step_size = lr / (1 - beta1^t), bias_correction = sqrt(1 - beta2^t),
+#   decay_factor = 1 - lr * weight_decay.
+# ---------------------------------------------------------------------------
+def adamw_scalars(lr, beta1, beta2, weight_decay, step):
+    """Host scalars of step t (t >= 1): (step_size, bias_correction, decay_factor)."""
+    step_size = lr / (1.0 - beta1 ** step)
+    bias_correction = float(np.sqrt(1.0 - beta2 ** step))
+    decay_factor = 1.0 - lr * weight_decay
+    return step_size, bias_correction, decay_factor
+
+
+def adamw_step(p, g, m, v, step_size, beta1, beta2, bias_correction, decay_factor, eps,
+               grad_scale=1.0, noop=False):
+    """One AdamW update of one tensor, elementwise:
+        g' = grad_scale * g
+        m' = beta1 m + (1 - beta1) g'
+        v' = beta2 v + (1 - beta2) g'^2
+        p' = decay_factor p - step_size m' / (sqrt(v') / bias_correction + eps)
+    With noop set nothing changes.  Returns (p', m', v')."""
+    p, g, m, v = _f64(p), _f64(g), _f64(m), _f64(v)
+    if noop:
+        return p.copy(), m.copy(), v.copy()
+    gs = grad_scale * g
+    m1 = beta1 * m + (1.0 - beta1) * gs
+    v1 = beta2 * v + (1.0 - beta2) * gs * gs
+    p1 = decay_factor * p - step_size * m1 / (np.sqrt(v1) / bias_correction + eps)
+    return p1, m1, v1

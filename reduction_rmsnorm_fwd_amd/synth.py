@@ -34,6 +34,7 @@ TID = {
     "x": 1, "dy": 2, "w": 3, "q": 4, "k": 5, "dq": 6, "dk": 7,
     "gate": 8, "up": 9, "dh": 10, "logits": 11, "targets": 12, "ignore": 13,
     "docs": 14, "hidden": 15, "weight": 16,
+    "param": 17, "grad": 18, "exp_avg": 19, "exp_avg_sq": 20,
 }
 
 
@@ -218,3 +219,28 @@ def flce_small(T: int, H: int, V: int, seed: int, ignore_frac: float = 0.1,
                   head_dim=2, F=1, V=V, eps=1e-5, theta=1e4, logit_std=0.0,
                   z_loss=z_loss, ignore_frac=ignore_frac, packed=False,
                   doc_lengths=(T,), seed=seed, flce_H=H, flce_w_std=w_std)
+
+
+# Parameter tensors of one Llama-3-8B decoder layer (fp32 master copies): q, k, v, o
+# projections, gate/up/down of the MLP, the two RMSNorm weights.
+LLAMA3_8B_LAYER_PARAMS = (
+    ("wq", 4096 * 4096), ("wk", 1024 * 4096), ("wv", 1024 * 4096), ("wo", 4096 * 4096),
+    ("w_gate", 14336 * 4096), ("w_up", 14336 * 4096), ("w_down", 4096 * 14336),
+    ("attn_norm", 4096), ("mlp_norm", 4096),
+)
+
+
+def adamw_inputs(sizes, seed: int):
+    """Optimizer state of a list of fp32 parameter tensors with the given element
+    counts: parameters N(0, 0.02^2), gradients N(0, 1e-3^2), first moments
+    N(0, 1e-4^2), second moments |N(0, 1e-3^2)| (non-negative, as squares are).
+    Tensor i draws from its own streams, keyed by (seed, tensor id, i)."""
+    out = dict(params=[], grads=[], exp_avgs=[], exp_avg_sqs=[])
+    for i, n in enumerate(sizes):
+        key = seed * 100003 + i
+        out["params"].append(torch.from_numpy(normal_f32(key, TID["param"], n, std=0.02)))
+        out["grads"].append(torch.from_numpy(normal_f32(key, TID["grad"], n, std=1e-3)))
+        out["exp_avgs"].append(torch.from_numpy(normal_f32(key, TID["exp_avg"], n, std=1e-4)))
+        out["exp_avg_sqs"].append(
+            torch.from_numpy(np.abs(normal_f32(key, TID["exp_avg_sq"], n, std=1e-3))))
+    return out
