@@ -165,6 +165,28 @@ int fo_flce_fwd_bwd(int dtype, int64_t T, int64_t H, int64_t V, const void* hidd
                     int32_t* status, int64_t chunk_tokens, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* ---- Fused AdamW step ([FastLLM] 关键实现细节, "Triton Adam 优化器": gradient scaling,
+ * both moments, weight decay and the parameter update in one pass, skipped as a whole
+ * while a device no-op flag is set; read as AdamW with decoupled weight decay) ----
+ * For each of the n_tensors fp32 tensors i (numel[i] elements each, any alignment;
+ * tensors must not overlap one another), elementwise and in place:
+ *   g' = s g;  m = beta1 m + (1 - beta1) g';  v = beta2 v + (1 - beta2) g'^2;
+ *   p = decay_factor p - step_size m / (sqrt(v) / bias_correction + eps)
+ * with s = *grad_scale (device float; NULL means 1).  If noop_flag (device int32,
+ * may be NULL) points at a nonzero value, nothing is written.  The host computes the
+ * step's scalars, e.g. step_size = lr / (1 - beta1^t), bias_correction =
+ * sqrt(1 - beta2^t), decay_factor = 1 - lr * weight_decay.
+ *   numel, params, grads, exp_avgs, exp_avg_sqs: HOST arrays of n_tensors entries (the
+ *   pointers in them are device pointers; NULL allowed where numel[i] == 0).
+ * One launch covers up to 36 tensors; more take several launches on `stream`.
+ * 28 bytes of HBM traffic per element.  FO_ERR_SHAPE for n_tensors < 0 or numel < 0.
+ */
+int fo_adamw_step(int32_t n_tensors, const int64_t* numel, float* const* params,
+                  const float* const* grads, float* const* exp_avgs, float* const* exp_avg_sqs,
+                  const int32_t* noop_flag, const float* grad_scale, float step_size,
+                  float beta1, float beta2, float bias_correction, float decay_factor,
+                  float eps, void* stream);
+
 /* ---- Measurement probes (not ops: they give the ceilings the ops are measured
  * against, on the same device, in the same process) ----
  * fo_probe_copy: dst = src for `bytes` bytes (a multiple of 16; both 16-byte aligned,

@@ -17,7 +17,7 @@ __all__ = [
     "load", "FoError", "FO_F32", "FO_BF16",
     "fo_rmsnorm_fwd", "fo_rmsnorm_bwd", "fo_rope_fwd", "fo_rope_bwd",
     "fo_swiglu_fwd", "fo_swiglu_bwd", "fo_xent_fwd_bwd", "fo_flce_fwd_bwd",
-    "fo_rmsnorm_bwd_workspace", "fo_xent_workspace", "fo_flce_workspace",
+    "fo_rmsnorm_bwd_workspace", "fo_xent_workspace", "fo_flce_workspace", "fo_adamw_step",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfo.so")
@@ -57,6 +57,10 @@ SIGNATURES = {
                                        _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_size_t,
                                        _c_ptr]),
     "fo_flce_workspace": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int]),
+    "fo_adamw_step": (ctypes.c_int, [ctypes.c_int32, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                     _c_ptr, _c_ptr, ctypes.c_float, ctypes.c_float,
+                                     ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                     ctypes.c_float, _c_ptr]),
     "fo_probe_copy": (ctypes.c_int, [_c_ptr, _c_ptr, ctypes.c_size_t, _c_ptr]),
     "fo_probe_mfma": (ctypes.c_int, [ctypes.c_int32, _c_i64, _c_ptr, _c_ptr]),
     "fo_flce_fwd_bwd": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr,
@@ -299,6 +303,37 @@ def fo_flce_fwd_bwd(hidden, weight, targets, ignore_index=-100, z_loss=0.0, dlos
     o["dhidden"] = dhidden
     o["dweight"] = dweight
     return o
+
+
+def fo_adamw_step(params, grads, exp_avgs, exp_avg_sqs, step_size, beta1, beta2,
+                  bias_correction, decay_factor, eps, noop_flag=None, grad_scale=None):
+    """One fused AdamW step over lists of fp32 device tensors (updated in place).
+    noop_flag: optional int32 device tensor of one element; grad_scale: optional fp32
+    device tensor of one element."""
+    import torch
+    lib = load()
+    n = len(params)
+    if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == n):
+        raise ValueError("params, grads, exp_avgs and exp_avg_sqs differ in length")
+    for group in (params, grads, exp_avgs, exp_avg_sqs):
+        for t in group:
+            if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("AdamW tensors must be contiguous fp32 device tensors")
+    for a, b, c, d in zip(params, grads, exp_avgs, exp_avg_sqs):
+        if not (a.numel() == b.numel() == c.numel() == d.numel()):
+            raise ValueError("tensor sizes differ within one parameter")
+    if noop_flag is not None and (noop_flag.dtype != torch.int32 or not noop_flag.is_cuda):
+        raise ValueError("noop_flag must be an int32 device tensor")
+    if grad_scale is not None and (grad_scale.dtype != torch.float32 or not grad_scale.is_cuda):
+        raise ValueError("grad_scale must be an fp32 device tensor")
+    arr = ctypes.c_void_p * max(n, 1)
+    numel = (ctypes.c_int64 * max(n, 1))(*[t.numel() for t in params])
+    ptrs = [arr(*[t.data_ptr() for t in g]) for g in (params, grads, exp_avgs, exp_avg_sqs)]
+    _check("fo_adamw_step", lib.fo_adamw_step(
+        n, ctypes.cast(numel, ctypes.c_void_p), *[ctypes.cast(p, ctypes.c_void_p) for p in ptrs],
+        _ptr(noop_flag) if noop_flag is not None else None,
+        _ptr(grad_scale) if grad_scale is not None else None,
+        step_size, beta1, beta2, bias_correction, decay_factor, eps, _stream()))
 
 
 def fo_probe_copy(src, dst):

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in fo.SIGNATURES, f"binding lacks {n}"
@@ -115,7 +115,7 @@ def test_xent_validation(lib):
 def test_flce_validation(lib):
     f = lib.fo_flce_fwd_bwd
     ws = lib.fo_flce_workspace(64, 32, 100, 0, F32)
-    assert ws > 32 * 100 * 2  # at least the transposed weight
+    assert ws > 64 * 128 * 2  # at least the chunk's bf16 dZ rows (vocabulary padded to 64)
     assert lib.fo_flce_workspace(64, 32, 100, 0, BF16) >= ws + 100 * 32 * 4
     args = [BF16, 64, 32, 100, P, P, P, -100, 1e-4, 1.0, P, P, F32, P, N, N, N, 0, P, ws, N]
 
@@ -134,6 +134,24 @@ def test_flce_validation(lib):
     assert call(a4=ctypes.c_void_p(0x1002)) == STRIDE   # misaligned hidden
     assert call(a19=ws - 1) == WS
     assert call(a17=-1) == SHAPE
+
+
+def test_adamw_validation(lib):
+    f = lib.fo_adamw_step
+    i64 = ctypes.c_int64
+    ptrs = ctypes.c_void_p * 2
+    numel = (i64 * 2)(5, 0)
+    good = ptrs(P, P)
+    half = ptrs(P, None)  # NULL allowed for the empty second tensor
+    hyp = (1e-3, 0.9, 0.999, 0.5, 0.99, 1e-8, N)
+    assert f(-1, N, N, N, N, N, N, N, *hyp) == SHAPE
+    assert f(0, N, N, N, N, N, N, N, *hyp) == OK          # nothing to do
+    assert f(2, N, good, good, good, good, N, N, *hyp) == NULL
+    assert f(2, numel, good, N, good, good, N, N, *hyp) == NULL
+    assert f(2, numel, ptrs(None, P), half, half, half, N, N, *hyp) == NULL
+    assert f(2, (i64 * 2)(5, -1), good, good, good, good, N, N, *hyp) == SHAPE
+    assert f(2, (i64 * 2)(0, 0), ptrs(None, None), ptrs(None, None), ptrs(None, None),
+             ptrs(None, None), N, N, *hyp) == OK           # all empty: no launch
 
 
 def test_probe_validation(lib):
