@@ -71,6 +71,7 @@ def parse():
     p.add_argument("--no-probes", action="store_true",
                    help="skip the copy / MFMA ceiling probes and the unaligned-shape lines")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-next", action="store_true", help="skip the rows after the step (AdamW)")
     p.add_argument("--no-isolated", action="store_true")
     p.add_argument("--only", default="", help="comma list of ops to run (profiling)")
     p.add_argument("--calib-copy", action="store_true",
@@ -231,6 +232,50 @@ def same_size_copies(fo, torch, stream, med, byte_counts, reps):
     return out
 
 
+ADAMW_LAYERS = 4  # Llama-3-8B decoder layers whose parameters one AdamW call updates
+
+
+def adamw_line(fo, synth, torch, stream, med, reps, copy_gbs):
+    """The fused AdamW step (a row after the step's ops, reported apart from the step):
+    one fo_adamw_step call over the fp32 parameters, gradients and moments of
+    ADAMW_LAYERS Llama-3-8B decoder layers (9 tensors each, one launch), isolated with
+    caches flushed; 28 bytes per element.  The state of one layer is drawn by the seeded
+    generator and cloned on the device for the others (values do not change timing)."""
+    sizes = [n for _, n in synth.LLAMA3_8B_LAYER_PARAMS]
+    one = synth.adamw_inputs(sizes, seed=11)
+    base = {k: [t.to("cuda") for t in one[k]] for k in one}
+    d = {k: [t.clone() for _ in range(ADAMW_LAYERS) for t in base[k]] for k in base}
+    del one, base
+    n = sum(t.numel() for t in d["params"])
+    sc = dict(step_size=3e-4 / (1 - 0.9 ** 10), beta1=0.9, beta2=0.95,
+              bias_correction=(1 - 0.95 ** 10) ** 0.5, decay_factor=1 - 3e-4 * 0.1, eps=1e-8)
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    ts = []
+    for r in range(reps + 2):
+        scratch.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fo.fo_adamw_step(d["params"], d["grads"], d["exp_avgs"], d["exp_avg_sqs"], **sc)
+        b.record(stream)
+        b.synchronize()
+        if r >= 2:
+            ts.append(a.elapsed_time(b))
+    del scratch
+    ms = med(ts)
+    byt = 28 * n
+    e = {"workload": f"fp32 AdamW step over the parameters of {ADAMW_LAYERS} Llama-3-8B decoder "
+                     f"layers ({len(d['params'])} tensors, {n / 1e6:.1f} M elements) in one "
+                     "fo_adamw_step call",
+         "ms_isolated_median": round(ms, 4), "algorithmic_MB": round(byt / 1e6, 1),
+         "GBps": round(byt / (ms * 1e-3) / 1e9, 1),
+         "frac_hbm_peak": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if copy_gbs:
+        e["frac_measured_copy"] = round(e["GBps"] / copy_gbs, 4)
+    del d
+    print(f"# adamw: {ms:.3f} ms, {e['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+    return e
+
+
 def unaligned_lines(fo, synth, torch, stream, med):
     """The scalar (unaligned) paths at the Llama-3-8B token count, reported apart from
     the aligned per-op lines: RMSNorm with d = 4097 and SwiGLU with F = 14337 (rows not
@@ -356,6 +401,10 @@ def gpu_bench(args):
     same = (None if args.no_probes or not hbm_bytes
             else same_size_copies(fo, torch, stream, med, hbm_bytes, args.iso_reps))
     unaligned = None if args.no_probes or only else unaligned_lines(fo, synth, torch, stream, med)
+    next_ops = None
+    if not (args.no_next or only):
+        next_ops = {"adamw_step": adamw_line(fo, synth, torch, stream, med, 20,
+                                             peaks["copy_GBps"] if peaks else None)}
     traffic = measured_traffic()
     per_op = {}
     for i, (name, _, work, bound) in enumerate(wl.ops):
@@ -429,6 +478,8 @@ def gpu_bench(args):
         out["fwd_bwd"] = pairs
     if peaks is not None:
         out["measured_peaks"] = peaks
+    if next_ops is not None:
+        out["next_ops"] = next_ops
     if unaligned is not None:
         out["unaligned"] = unaligned
     # dominant op of the step: the fused linear cross-entropy (MFMA-bound)
