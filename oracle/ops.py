@@ -62,6 +62,38 @@ def rmsnorm_bwd(dy, x, w, eps):
 
 
 # ---------------------------------------------------------------------------
+# LayerNorm — [FastLLM] 三 技术架构, "Transformer Block 结构": the block normalisation is
+# LayerNorm or RMSNorm; the same page's environment section names Apex's
+# fast_layer_norm kernels.  No formula is printed; the reading is the textbook layer
+# normalisation over the last axis with a learned scale and bias, the biased (1/d)
+# variance, and eps inside the root (as for RMSNorm).
+# ---------------------------------------------------------------------------
+def layernorm_fwd(x, w, b, eps):
+    """y[t,j] = (x[t,j] - mu[t]) r[t] w[j] + b[j],  mu = mean_j x,
+    r = 1/sqrt(mean_j (x - mu)^2 + eps).  Returns (y, mu [T], rstd [T])."""
+    x, w, b = _f64(x), _f64(w), _f64(b)
+    mu = np.mean(x, axis=-1)
+    xc = x - mu[..., None]
+    rstd = 1.0 / np.sqrt(np.mean(xc * xc, axis=-1) + eps)
+    return xc * rstd[..., None] * w + b, mu, rstd
+
+
+def layernorm_bwd(dy, x, w, eps):
+    """Gradients of layernorm_fwd for upstream dy.  With xh = (x - mu) r and g = w dy,
+        dx = r (g - mean_j g - xh mean_j(g xh)),  dw = sum_t dy xh,  db = sum_t dy.
+    Returns (dx, dw, db)."""
+    dy, x, w = _f64(dy), _f64(x), _f64(w)
+    mu = np.mean(x, axis=-1, keepdims=True)
+    r = 1.0 / np.sqrt(np.mean((x - mu) ** 2, axis=-1, keepdims=True) + eps)
+    xh = (x - mu) * r
+    g = dy * w
+    dx = r * (g - np.mean(g, axis=-1, keepdims=True)
+              - xh * np.mean(g * xh, axis=-1, keepdims=True))
+    axes = tuple(range(x.ndim - 1))
+    return dx, np.sum(dy * xh, axis=axes), np.sum(dy, axis=axes)
+
+
+# ---------------------------------------------------------------------------
 # RoPE — [FastLLM] 三 技术架构, "Transformer Block 结构" (attention + RoPE) and
 # 训练配置示例 (rotary type default, theta; heads / head_groups / head_size);
 # [LF] npu_fused_rope; [HFK] "Liger" (rope).
