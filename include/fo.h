@@ -86,6 +86,31 @@ int fo_rmsnorm_bwd(int dtype, int64_t T, int64_t d, const void* dy, int64_t lddy
                    void* dx, int64_t lddx, float* dw, void* ws, size_t ws_bytes,
                    void* stream);
 
+/* ---- LayerNorm ([FastLLM] Transformer Block 结构: LayerNorm or RMSNorm as the block
+ * normalisation; the page's environment section names Apex fast_layer_norm) ----
+ * forward:  mu[t] = mean_j x[t,j];  r[t] = 1/sqrt(mean_j (x[t,j] - mu[t])^2 + eps);
+ *           y[t,j] = (x[t,j] - mu[t]) * r[t] * w[j] + b[j]
+ *   dtype, strides and aliasing as fo_rmsnorm_fwd; w [d] and b [d] of the same dtype;
+ *   mean [T] and rstd [T] fp32, each may be NULL (the saved statistics of the backward).
+ *   The row stays in registers between the mean and the centred variance (two sweeps
+ *   over registers, one read of x).
+ */
+int fo_layernorm_fwd(int dtype, int64_t T, int64_t d, const void* x, int64_t ldx,
+                     const void* w, const void* b, float eps, void* y, int64_t ldy,
+                     float* mean, float* rstd, void* stream);
+
+/* backward:  g = w*dy;  xh = (x - mu) r;
+ *            dx = r (g - mean_j g - xh mean_j(g xh));  dw[j] = sum_t dy xh;  db[j] = sum_t dy
+ *   mean and rstd: the forward's saved statistics (required).  dw, db [d] fp32,
+ *   overwritten, fixed-order sums.  dx may alias dy (same stride).
+ *   ws: fo_layernorm_bwd_workspace(T, d) bytes.
+ */
+size_t fo_layernorm_bwd_workspace(int64_t T, int64_t d);
+int fo_layernorm_bwd(int dtype, int64_t T, int64_t d, const void* dy, int64_t lddy,
+                     const void* x, int64_t ldx, const void* w, const float* mean,
+                     const float* rstd, void* dx, int64_t lddx, float* dw, float* db, void* ws,
+                     size_t ws_bytes, void* stream);
+
 /* ---- RoPE on Q and K, in place ([FastLLM] 训练配置示例 rotary theta, heads,
  * head_groups, head_size; [LF]; [HFK] Liger) ----
  * For token t with position p = positions[t] and pair i in [0, head_dim/2):

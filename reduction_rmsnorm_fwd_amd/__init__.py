@@ -18,6 +18,7 @@ __all__ = [
     "fo_rmsnorm_fwd", "fo_rmsnorm_bwd", "fo_rope_fwd", "fo_rope_bwd",
     "fo_swiglu_fwd", "fo_swiglu_bwd", "fo_xent_fwd_bwd", "fo_flce_fwd_bwd",
     "fo_rmsnorm_bwd_workspace", "fo_xent_workspace", "fo_flce_workspace", "fo_adamw_step",
+    "fo_layernorm_fwd", "fo_layernorm_bwd", "fo_layernorm_bwd_workspace",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfo.so")
@@ -40,6 +41,13 @@ SIGNATURES = {
     "fo_rmsnorm_bwd": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr,
                                       _c_i64, _c_ptr, _c_ptr, ctypes.c_float, _c_ptr, _c_i64,
                                       _c_ptr, _c_ptr, ctypes.c_size_t, _c_ptr]),
+    "fo_layernorm_fwd": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr,
+                                        _c_ptr, ctypes.c_float, _c_ptr, _c_i64, _c_ptr, _c_ptr,
+                                        _c_ptr]),
+    "fo_layernorm_bwd_workspace": (ctypes.c_size_t, [_c_i64, _c_i64]),
+    "fo_layernorm_bwd": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr,
+                                        _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_ptr,
+                                        _c_ptr, _c_ptr, ctypes.c_size_t, _c_ptr]),
     "fo_rope_fwd": (ctypes.c_int, [ctypes.c_int, _c_i64, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_int32, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr,
                                    ctypes.c_double, _c_ptr]),
@@ -177,6 +185,47 @@ def fo_rmsnorm_bwd(dy, x, w, rstd, eps, dx=None, dw=None, ws=None):
         _dt(x), T, d, _ptr(dy), _rows(dy, "dy"), _ptr(x), _rows(x, "x"), _ptr(w), _ptr(rstd),
         float(eps), _ptr(dx), _rows(dx, "dx"), _ptr(dw), _ptr(ws), ws.numel(), _stream()))
     return dx, dw
+
+
+# ----------------------------------------------------------------- LayerNorm
+def fo_layernorm_fwd(x, w, b, eps, y=None, mean=None, rstd=None, want_stats=True):
+    import torch
+    lib = load()
+    T, d = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    if want_stats:
+        if mean is None:
+            mean = torch.empty(T, dtype=torch.float32, device=x.device)
+        if rstd is None:
+            rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+    _check("fo_layernorm_fwd", lib.fo_layernorm_fwd(
+        _dt(x), T, d, _ptr(x), _rows(x, "x"), _ptr(w), _ptr(b), float(eps), _ptr(y),
+        _rows(y, "y"), _ptr(mean), _ptr(rstd), _stream()))
+    return y, mean, rstd
+
+
+def fo_layernorm_bwd_workspace(T, d):
+    return load_library().fo_layernorm_bwd_workspace(T, d)
+
+
+def fo_layernorm_bwd(dy, x, w, mean, rstd, dx=None, dw=None, db=None, ws=None):
+    import torch
+    lib = load()
+    T, d = x.shape
+    if dx is None:
+        dx = torch.empty_like(x)
+    if dw is None:
+        dw = torch.empty(d, dtype=torch.float32, device=x.device)
+    if db is None:
+        db = torch.empty(d, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = _ws(lib.fo_layernorm_bwd_workspace(T, d), x.device)
+    _check("fo_layernorm_bwd", lib.fo_layernorm_bwd(
+        _dt(x), T, d, _ptr(dy), _rows(dy, "dy"), _ptr(x), _rows(x, "x"), _ptr(w), _ptr(mean),
+        _ptr(rstd), _ptr(dx), _rows(dx, "dx"), _ptr(dw), _ptr(db), _ptr(ws), ws.numel(),
+        _stream()))
+    return dx, dw, db
 
 
 # ---------------------------------------------------------------------- RoPE

@@ -29,10 +29,13 @@ constexpr int kMaxPartials = 512;  // dw partial rows (workgroups of the backwar
 constexpr int kGenericThreads = 256;
 
 // ----------------------------------------------------------------- forward, fast
-template <typename T, int NV>
+// LN: LayerNorm (mean subtracted before the variance, bias added); the row is still
+// read once: mean and centred variance are two sweeps over the registers.
+template <typename T, int NV, bool LN>
 __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
     int64_t T_, int nvec, int d, const T* __restrict__ x, int64_t ldx,
-    const T* __restrict__ w, float eps, T* y, int64_t ldy, float* __restrict__ rstd) {
+    const T* __restrict__ w, const T* __restrict__ b, float eps, T* y, int64_t ldy,
+    float* __restrict__ mean, float* __restrict__ rstd) {
   constexpr int VEC = Vec<T>::N;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = (int64_t)blockIdx.x * kFwdWaves + (threadIdx.x / kWave);
@@ -45,13 +48,27 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
     if (v < nvec) xv[i] = load_pack(xr + (int64_t)v * VEC);
     else xv[i].raw = u32x4{0, 0, 0, 0};
   }
+  float mu = 0.f;
+  if constexpr (LN) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) s += to_f32(xv[i].v[j]);
+    mu = wave_sum(s) / (float)d;
+  }
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i)
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
-      const float f = to_f32(xv[i].v[j]);
-      ss = fmaf(f, f, ss);
+      if constexpr (LN) {
+        const float f = to_f32(xv[i].v[j]) - mu;
+        if (lane + i * kWave < nvec) ss = fmaf(f, f, ss);  // padding lanes hold 0, not mu
+      } else {
+        const float f = to_f32(xv[i].v[j]);
+        ss = fmaf(f, f, ss);
+      }
     }
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
@@ -66,12 +83,24 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
     if (v < nvec) {
       const Pack<T> wv = load_pack_cached(w + (int64_t)v * VEC);
       Pack<T> o;
+      if constexpr (LN) {
+        const Pack<T> bv = load_pack_cached(b + (int64_t)v * VEC);
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) o.v[j] = from_f32<T>(to_f32(xv[i].v[j]) * r * to_f32(wv.v[j]));
+        for (int j = 0; j < VEC; ++j)
+          o.v[j] = from_f32<T>(fmaf((to_f32(xv[i].v[j]) - mu) * r, to_f32(wv.v[j]), to_f32(bv.v[j])));
+      } else {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) o.v[j] = from_f32<T>(to_f32(xv[i].v[j]) * r * to_f32(wv.v[j]));
+      }
       store_pack(yr + (int64_t)v * VEC, o);
     }
   }
-  if (rstd != nullptr && lane == 0) rstd[row] = r;
+  if (lane == 0) {
+    if (rstd != nullptr) rstd[row] = r;
+    if constexpr (LN) {
+      if (mean != nullptr) mean[row] = mu;
+    }
+  }
 }
 
 // Workgroup sum with a fixed combination order; every thread gets the total.
@@ -89,24 +118,38 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
 }
 
 // -------------------------------------------------------------- forward, generic
-template <typename T>
+template <typename T, bool LN>
 __global__ __launch_bounds__(kGenericThreads) void rmsnorm_fwd_block(
-    int64_t T_, int64_t d, const T* x, int64_t ldx, const T* __restrict__ w, float eps,
-    T* y, int64_t ldy, float* __restrict__ rstd) {
+    int64_t T_, int64_t d, const T* x, int64_t ldx, const T* __restrict__ w,
+    const T* __restrict__ b, float eps, T* y, int64_t ldy, float* __restrict__ mean,
+    float* __restrict__ rstd) {
   __shared__ float sh[kGenericThreads / kWave];
   const int64_t row = blockIdx.x;
   const T* xr = x + row * ldx;
+  float mu = 0.f;
+  if constexpr (LN) {
+    float s = 0.f;
+    for (int64_t j = threadIdx.x; j < d; j += kGenericThreads) s += to_f32(xr[j]);
+    mu = block_sum<kGenericThreads>(s, sh) / (float)d;
+  }
   float ss = 0.f;
   for (int64_t j = threadIdx.x; j < d; j += kGenericThreads) {
-    const float f = to_f32(xr[j]);
+    const float f = to_f32(xr[j]) - mu;
     ss = fmaf(f, f, ss);
   }
   ss = block_sum<kGenericThreads>(ss, sh);
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
   T* yr = y + row * ldy;
-  for (int64_t j = threadIdx.x; j < d; j += kGenericThreads)
-    yr[j] = from_f32<T>(to_f32(xr[j]) * r * to_f32(w[j]));
-  if (rstd != nullptr && threadIdx.x == 0) rstd[row] = r;
+  for (int64_t j = threadIdx.x; j < d; j += kGenericThreads) {
+    if constexpr (LN) yr[j] = from_f32<T>(fmaf((to_f32(xr[j]) - mu) * r, to_f32(w[j]), to_f32(b[j])));
+    else yr[j] = from_f32<T>(to_f32(xr[j]) * r * to_f32(w[j]));
+  }
+  if (threadIdx.x == 0) {
+    if (rstd != nullptr) rstd[row] = r;
+    if constexpr (LN) {
+      if (mean != nullptr) mean[row] = mu;
+    }
+  }
 }
 
 // ----------------------------------------------------------------- backward, fast
@@ -119,21 +162,26 @@ __global__ __launch_bounds__(kGenericThreads) void rmsnorm_fwd_block(
 // so a round's cross-wave barrier never leaves the memory pipe empty.  At the end the
 // waves' column partials are folded through LDS in a fixed order into one fp32 partial
 // row per workgroup: partial[blockIdx.x, :].
-template <typename T, int NV, int RW>
+//
+// LN (LayerNorm, mean and rstd saved by the forward): with g = w*dy and xc = x - mean,
+//   dx = r g - r mean_j(g) - r^3 xc mean_j(g xc),  dw += dy xc r,  db += dy,
+// the db partials folded beside the dw partials (partial row of 2d floats).
+template <typename T, int NV, int RW, bool LN>
 __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
     int64_t T_, int nvec, int d, const T* dy, int64_t lddy, const T* x, int64_t ldx,
-    const T* __restrict__ w, const float* __restrict__ rstd, float eps, T* dx,
-    int64_t lddx, float* __restrict__ partial) {
+    const T* __restrict__ w, const float* __restrict__ mean, const float* __restrict__ rstd,
+    float eps, T* dx, int64_t lddx, float* __restrict__ partial) {
   constexpr int VEC = Vec<T>::N;
   constexpr int RG = kBwdWaves / RW;  // rows in flight per workgroup
-  extern __shared__ float fold[];     // [d]
+  constexpr int NB = LN ? NV : 1;     // db accumulators (LayerNorm only)
+  extern __shared__ float fold[];     // [d], or [2d] for LN
   __shared__ float xdot[kBwdWaves], xss[kBwdWaves];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rg = wave / RW, wr = wave % RW;
   const int vbase = wr * kWave + lane;
   Pack<T> wv[NV];
-  float acc[NV][VEC];
+  float acc[NV][VEC], accb[NB][VEC];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int v = vbase + i * RW * kWave;
@@ -142,15 +190,23 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
 #pragma unroll
     for (int j = 0; j < VEC; ++j) acc[i][j] = 0.f;
   }
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) accb[i][j] = 0.f;
   const float inv_d = 1.0f / (float)d;
   const int64_t stride = (int64_t)gridDim.x * RG;
   const int64_t rounds = ceil_div(T_ - (int64_t)blockIdx.x * RG, stride);
   Pack<T> gv[NV], xv[NV], gn[NV], xn[NV];
-  float rv = 0.f, rn = 0.f;  // the saved 1/rms of the row (loaded with the row)
-  auto load_round = [&](int64_t rd, Pack<T>* g, Pack<T>* xx, float& r) {
+  float rv = 0.f, rn = 0.f;  // the saved 1/rms (1/std) of the row (loaded with the row)
+  float mv = 0.f, mn = 0.f;  // LN: the saved mean of the row
+  auto load_round = [&](int64_t rd, Pack<T>* g, Pack<T>* xx, float& r, float& m) {
     const int64_t row = (int64_t)blockIdx.x * RG + rg + rd * stride;
     const bool live = rd < rounds && row < T_;
     if (rstd != nullptr && live) r = rstd[row];
+    if constexpr (LN) {
+      if (live) m = mean[row];
+    }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int v = vbase + i * RW * kWave;
@@ -163,19 +219,27 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
       }
     }
   };
-  load_round(0, gv, xv, rv);
+  load_round(0, gv, xv, rv, mv);
   for (int64_t rd = 0; rd < rounds; ++rd) {
     const int64_t row = (int64_t)blockIdx.x * RG + rg + rd * stride;
     const bool live = row < T_;
-    load_round(rd + 1, gn, xn, rn);
+    load_round(rd + 1, gn, xn, rn, mn);
+    // RMS: dot = sum g x, ss = sum x^2;  LN: dot = sum g (x - mean), ss = sum g
     float dot = 0.f, ss = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
       for (int j = 0; j < VEC; ++j) {
-        const float xf = to_f32(xv[i].v[j]);
-        dot = fmaf(to_f32(wv[i].v[j]) * to_f32(gv[i].v[j]), xf, dot);
-        ss = fmaf(xf, xf, ss);
+        const float gf = to_f32(wv[i].v[j]) * to_f32(gv[i].v[j]);
+        if constexpr (LN) {
+          // padding lanes hold zeros in w and dy, so gf = 0 there
+          dot = fmaf(gf, to_f32(xv[i].v[j]) - mv, dot);
+          ss += gf;
+        } else {
+          const float xf = to_f32(xv[i].v[j]);
+          dot = fmaf(gf, xf, dot);
+          ss = fmaf(xf, xf, ss);
+        }
       }
     dot = wave_sum(dot);
     ss = wave_sum(ss);
@@ -192,8 +256,15 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
       __syncthreads();  // slots are rewritten next round
     }
     if (live) {
-      const float r = rstd != nullptr ? rv : 1.0f / sqrtf(ss * inv_d + eps);
-      const float k = r * r * r * (dot * inv_d);
+      float r, k, c = 0.f;
+      if constexpr (LN) {
+        r = rv;
+        k = r * r * r * (dot * inv_d);
+        c = r * (ss * inv_d);
+      } else {
+        r = rstd != nullptr ? rv : 1.0f / sqrtf(ss * inv_d + eps);
+        k = r * r * r * (dot * inv_d);
+      }
       T* dxr = dx + row * lddx;
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
@@ -202,10 +273,17 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
           Pack<T> o;
 #pragma unroll
           for (int j = 0; j < VEC; ++j) {
-            const float xf = to_f32(xv[i].v[j]);
             const float gf = to_f32(gv[i].v[j]);
-            o.v[j] = from_f32<T>(r * (to_f32(wv[i].v[j]) * gf) - k * xf);
-            acc[i][j] = fmaf(gf * xf, r, acc[i][j]);
+            if constexpr (LN) {
+              const float xc = to_f32(xv[i].v[j]) - mv;
+              o.v[j] = from_f32<T>(r * (to_f32(wv[i].v[j]) * gf) - c - k * xc);
+              acc[i][j] = fmaf(gf * xc, r, acc[i][j]);
+              accb[i][j] += gf;
+            } else {
+              const float xf = to_f32(xv[i].v[j]);
+              o.v[j] = from_f32<T>(r * (to_f32(wv[i].v[j]) * gf) - k * xf);
+              acc[i][j] = fmaf(gf * xf, r, acc[i][j]);
+            }
           }
           store_pack(dxr + (int64_t)v * VEC, o);
         }
@@ -217,6 +295,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
       xv[i] = xn[i];
     }
     rv = rn;
+    mv = mn;
   }
   // fold the row groups' column partials in order 0,1,2,... (RW waves of a group own
   // disjoint columns, so they write their slots in the same step)
@@ -230,36 +309,52 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
           for (int j = 0; j < VEC; ++j) {
             float* p = &fold[v * VEC + j];
             *p = (s == 0) ? acc[i][j] : (*p + acc[i][j]);
+            if constexpr (LN) {
+              float* q = &fold[d + v * VEC + j];
+              *q = (s == 0) ? accb[i][j] : (*q + accb[i][j]);
+            }
           }
         }
       }
     }
     __syncthreads();
   }
-  float* out = partial + (int64_t)blockIdx.x * d;
-  for (int j = threadIdx.x; j < d; j += blockDim.x) out[j] = fold[j];
+  constexpr int kCols = LN ? 2 : 1;
+  float* out = partial + (int64_t)blockIdx.x * kCols * d;
+  for (int j = threadIdx.x; j < kCols * d; j += blockDim.x) out[j] = fold[j];
 }
 
 // -------------------------------------------------------------- backward, generic
-// One workgroup per row: dx, and r[t] saved for the dw pass.
-template <typename T>
+// One workgroup per row: dx, and (RMS) r[t] saved for the dw pass.  LN uses the saved
+// mean and rstd.
+template <typename T, bool LN>
 __global__ __launch_bounds__(kGenericThreads) void rmsnorm_bwd_dx_block(
     int64_t T_, int64_t d, const T* dy, int64_t lddy, const T* x, int64_t ldx,
-    const T* __restrict__ w, const float* __restrict__ rstd, float eps, T* dx,
-    int64_t lddx, float* __restrict__ r_out) {
+    const T* __restrict__ w, const float* __restrict__ mean, const float* __restrict__ rstd,
+    float eps, T* dx, int64_t lddx, float* __restrict__ r_out) {
   __shared__ float sh[kGenericThreads / kWave];
   const int64_t row = blockIdx.x;
   const T* dyr = dy + row * lddy;
   const T* xr = x + row * ldx;
+  const float mu = LN ? mean[row] : 0.f;
   float dot = 0.f, ss = 0.f;
   for (int64_t j = threadIdx.x; j < d; j += kGenericThreads) {
-    const float xf = to_f32(xr[j]);
-    dot = fmaf(to_f32(w[j]) * to_f32(dyr[j]), xf, dot);
-    ss = fmaf(xf, xf, ss);
+    const float gf = to_f32(w[j]) * to_f32(dyr[j]);
+    if constexpr (LN) {
+      dot = fmaf(gf, to_f32(xr[j]) - mu, dot);
+      ss += gf;
+    } else {
+      const float xf = to_f32(xr[j]);
+      dot = fmaf(gf, xf, dot);
+      ss = fmaf(xf, xf, ss);
+    }
   }
   dot = block_sum<kGenericThreads>(dot, sh);
-  float r;
-  if (rstd != nullptr) {
+  float r, c = 0.f;
+  if constexpr (LN) {
+    r = rstd[row];
+    c = r * (block_sum<kGenericThreads>(ss, sh) / (float)d);
+  } else if (rstd != nullptr) {
     r = rstd[row];
   } else {
     ss = block_sum<kGenericThreads>(ss, sh);
@@ -270,26 +365,42 @@ __global__ __launch_bounds__(kGenericThreads) void rmsnorm_bwd_dx_block(
   // dx may alias dy: every element is read (above) by the thread that writes it, and
   // the block_sum barriers separate all reads of the dot product from these writes.
   for (int64_t j = threadIdx.x; j < d; j += kGenericThreads) {
-    const float xf = to_f32(xr[j]);
-    dxr[j] = from_f32<T>(r * (to_f32(w[j]) * to_f32(dyr[j])) - k * xf);
+    const float xf = to_f32(xr[j]) - mu;
+    dxr[j] = from_f32<T>(r * (to_f32(w[j]) * to_f32(dyr[j])) - c - k * xf);
   }
-  if (threadIdx.x == 0) r_out[row] = r;
+  if constexpr (!LN) {
+    if (threadIdx.x == 0) r_out[row] = r;
+  }
 }
 
-// dw partial rows of the generic path: workgroup (g, column block) sums its row range.
-template <typename T>
+// dw (and, LN, db) partial rows of the generic path: workgroup (g, column block) sums
+// its row range; LN writes the db partial at column d + j.
+template <typename T, bool LN>
 __global__ __launch_bounds__(256) void rmsnorm_dw_partial_block(
     int64_t T_, int64_t d, const T* dy, int64_t lddy, const T* x, int64_t ldx,
-    const float* __restrict__ r, int64_t rows_per_group, float* __restrict__ partial) {
+    const float* __restrict__ mean, const float* __restrict__ r, int64_t rows_per_group,
+    float* __restrict__ partial) {
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t g = blockIdx.y;
   if (j >= d) return;
   const int64_t r0 = g * rows_per_group;
   const int64_t r1 = (r0 + rows_per_group < T_) ? r0 + rows_per_group : T_;
-  float acc = 0.f;
-  for (int64_t t = r0; t < r1; ++t)
-    acc = fmaf(to_f32(dy[t * lddy + j]) * to_f32(x[t * ldx + j]), r[t], acc);
-  partial[g * d + j] = acc;
+  float acc = 0.f, accb = 0.f;
+  for (int64_t t = r0; t < r1; ++t) {
+    const float gf = to_f32(dy[t * lddy + j]);
+    if constexpr (LN) {
+      acc = fmaf(gf * (to_f32(x[t * ldx + j]) - mean[t]), r[t], acc);
+      accb += gf;
+    } else {
+      acc = fmaf(gf * to_f32(x[t * ldx + j]), r[t], acc);
+    }
+  }
+  if constexpr (LN) {
+    partial[g * 2 * d + j] = acc;
+    partial[g * 2 * d + d + j] = accb;
+  } else {
+    partial[g * d + j] = acc;
+  }
 }
 
 // dw[j] = sum_g partial[g, j].  A workgroup covers 16 columns as 4 float4 lanes; its
@@ -299,7 +410,7 @@ __global__ __launch_bounds__(256) void rmsnorm_dw_partial_block(
 constexpr int kReducePhases = 64;
 constexpr int kReduceCols = 16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-__global__ __launch_bounds__(256) void rmsnorm_dw_reduce(int64_t G, int64_t d,
+__global__ __launch_bounds__(256) void rmsnorm_dw_reduce(int64_t G, int64_t d, int64_t ldp,
                                                         const float* __restrict__ partial,
                                                         float* __restrict__ dw) {
   __shared__ float sh[kReducePhases][kReduceCols + 1];
@@ -310,12 +421,12 @@ __global__ __launch_bounds__(256) void rmsnorm_dw_reduce(int64_t G, int64_t d,
   const int64_t g0 = ph * per;
   const int64_t g1 = (g0 + per < G) ? g0 + per : G;
   float a[4] = {0.f, 0.f, 0.f, 0.f};
-  if (j + 3 < d && d % 4 == 0 && (reinterpret_cast<uintptr_t>(partial) & 15) == 0) {
+  if (j + 3 < d && ldp % 4 == 0 && (reinterpret_cast<uintptr_t>(partial) & 15) == 0) {
     for (int64_t g = g0; g < g1; g += 8) {
       f32x4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (g + u < g1) v[u] = *reinterpret_cast<const f32x4*>(partial + (g + u) * d + j);
+        if (g + u < g1) v[u] = *reinterpret_cast<const f32x4*>(partial + (g + u) * ldp + j);
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (g + u < g1)
@@ -326,7 +437,7 @@ __global__ __launch_bounds__(256) void rmsnorm_dw_reduce(int64_t G, int64_t d,
     for (int64_t g = g0; g < g1; ++g)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        if (j + c < d) a[c] += partial[g * d + j + c];
+        if (j + c < d) a[c] += partial[g * ldp + j + c];
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c) sh[ph][q * 4 + c] = a[c];
@@ -362,26 +473,30 @@ int nv_for(int64_t d) {
   return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
 }
 
-template <typename T>
-int fwd_impl(int64_t T_, int64_t d, const void* x, int64_t ldx, const void* w, float eps,
-             void* y, int64_t ldy, float* rstd, hipStream_t st) {
+template <typename T, bool LN>
+int fwd_impl(int64_t T_, int64_t d, const void* x, int64_t ldx, const void* w, const void* b,
+             float eps, void* y, int64_t ldy, float* mean, float* rstd, hipStream_t st) {
   const T* xp = static_cast<const T*>(x);
   const T* wp = static_cast<const T*>(w);
+  const T* bp = static_cast<const T*>(b);
   T* yp = static_cast<T*>(y);
-  if (vector_ok<T>(d, x, ldx, y, ldy, x, ldx, w)) {
+  if (vector_ok<T>(d, x, ldx, y, ldy, x, ldx, w) && (!LN || aligned16(b))) {
     const int nvec = (int)(d / Vec<T>::N);
     const dim3 grid((unsigned)ceil_div(T_, kFwdWaves));
     const dim3 block(kFwdWaves * kWave);
+#define FO_FWD(NV_) \
+  rmsnorm_fwd_wave<T, NV_, LN><<<grid, block, 0, st>>>(T_, nvec, (int)d, xp, ldx, wp, bp, eps, yp, ldy, mean, rstd)
     switch (nv_for<T>(d)) {
-      case 1: rmsnorm_fwd_wave<T, 1><<<grid, block, 0, st>>>(T_, nvec, (int)d, xp, ldx, wp, eps, yp, ldy, rstd); break;
-      case 2: rmsnorm_fwd_wave<T, 2><<<grid, block, 0, st>>>(T_, nvec, (int)d, xp, ldx, wp, eps, yp, ldy, rstd); break;
-      case 4: rmsnorm_fwd_wave<T, 4><<<grid, block, 0, st>>>(T_, nvec, (int)d, xp, ldx, wp, eps, yp, ldy, rstd); break;
-      case 8: rmsnorm_fwd_wave<T, 8><<<grid, block, 0, st>>>(T_, nvec, (int)d, xp, ldx, wp, eps, yp, ldy, rstd); break;
-      default: rmsnorm_fwd_wave<T, 16><<<grid, block, 0, st>>>(T_, nvec, (int)d, xp, ldx, wp, eps, yp, ldy, rstd); break;
+      case 1: FO_FWD(1); break;
+      case 2: FO_FWD(2); break;
+      case 4: FO_FWD(4); break;
+      case 8: FO_FWD(8); break;
+      default: FO_FWD(16); break;
     }
+#undef FO_FWD
   } else {
-    rmsnorm_fwd_block<T><<<dim3((unsigned)T_), dim3(kGenericThreads), 0, st>>>(
-        T_, d, xp, ldx, wp, eps, yp, ldy, rstd);
+    rmsnorm_fwd_block<T, LN><<<dim3((unsigned)T_), dim3(kGenericThreads), 0, st>>>(
+        T_, d, xp, ldx, wp, bp, eps, yp, ldy, mean, rstd);
   }
   return launch_status();
 }
@@ -410,24 +525,27 @@ BwdPlan bwd_plan(int64_t T_, int nvec) {
   return p;
 }
 
-template <typename T, int NV, int RW>
+template <typename T, int NV, int RW, bool LN>
 void launch_bwd(const BwdPlan& p, int64_t T_, int nvec, int d, const T* dy, int64_t lddy,
-                const T* x, int64_t ldx, const T* w, const float* rstd, float eps, T* dx,
-                int64_t lddx, float* partial, hipStream_t st) {
-  rmsnorm_bwd_wave<T, NV, RW>
-      <<<dim3((unsigned)p.groups), dim3(kBwdWaves * kWave), (size_t)d * sizeof(float), st>>>(
-          T_, nvec, d, dy, lddy, x, ldx, w, rstd, eps, dx, lddx, partial);
+                const T* x, int64_t ldx, const T* w, const float* mean, const float* rstd,
+                float eps, T* dx, int64_t lddx, float* partial, hipStream_t st) {
+  rmsnorm_bwd_wave<T, NV, RW, LN>
+      <<<dim3((unsigned)p.groups), dim3(kBwdWaves * kWave), (size_t)(LN ? 2 : 1) * d * sizeof(float),
+         st>>>(T_, nvec, d, dy, lddy, x, ldx, w, mean, rstd, eps, dx, lddx, partial);
 }
 
-template <typename T>
+// LN: mean and rstd are the forward's saved statistics (required); db receives the
+// bias gradient.  RMS: mean and db unused, rstd optional.
+template <typename T, bool LN>
 int bwd_impl(int64_t T_, int64_t d, const void* dy, int64_t lddy, const void* x,
-             int64_t ldx, const void* w, const float* rstd, float eps, void* dx,
-             int64_t lddx, float* dw, void* ws, hipStream_t st) {
+             int64_t ldx, const void* w, const float* mean, const float* rstd, float eps,
+             void* dx, int64_t lddx, float* dw, float* db, void* ws, hipStream_t st) {
   const T* dyp = static_cast<const T*>(dy);
   const T* xp = static_cast<const T*>(x);
   const T* wp = static_cast<const T*>(w);
   T* dxp = static_cast<T*>(dx);
   float* partial = static_cast<float*>(ws);
+  constexpr int64_t kCols = LN ? 2 : 1;  // partial row: dw (and db) columns
   int64_t G;
   if (vector_ok<T>(d, dy, lddy, x, ldx, dx, lddx, w)) {
     const int nvec = (int)(d / Vec<T>::N);
@@ -435,8 +553,8 @@ int bwd_impl(int64_t T_, int64_t d, const void* dy, int64_t lddy, const void* x,
     G = p.groups;
     constexpr int kMaxNV = 16 / Vec<T>::N;
     auto go = [&](auto nv_c, auto rw_c) {
-      launch_bwd<T, decltype(nv_c)::value, decltype(rw_c)::value>(
-          p, T_, nvec, (int)d, dyp, lddy, xp, ldx, wp, rstd, eps, dxp, lddx, partial, st);
+      launch_bwd<T, decltype(nv_c)::value, decltype(rw_c)::value, LN>(
+          p, T_, nvec, (int)d, dyp, lddy, xp, ldx, wp, mean, rstd, eps, dxp, lddx, partial, st);
     };
     auto go_rw = [&](auto rw_c) {
       if (p.nv == 1) go(std::integral_constant<int, 1>{}, rw_c);
@@ -450,17 +568,21 @@ int bwd_impl(int64_t T_, int64_t d, const void* dy, int64_t lddy, const void* x,
       default: go_rw(std::integral_constant<int, 8>{}); break;
     }
   } else {
-    // r[t] after the partials in the workspace
+    // RMS: r[t] after the partials in the workspace; LN uses the saved rstd
     G = bwd_groups(T_);
-    float* r = partial + align_up((size_t)G * (size_t)d, 64);
-    rmsnorm_bwd_dx_block<T><<<dim3((unsigned)T_), dim3(kGenericThreads), 0, st>>>(
-        T_, d, dyp, lddy, xp, ldx, wp, rstd, eps, dxp, lddx, r);
+    float* r = partial + align_up((size_t)G * (size_t)(kCols * d), 64);
+    rmsnorm_bwd_dx_block<T, LN><<<dim3((unsigned)T_), dim3(kGenericThreads), 0, st>>>(
+        T_, d, dyp, lddy, xp, ldx, wp, mean, rstd, eps, dxp, lddx, r);
     const int64_t rows_per_group = ceil_div(T_, G);
     G = ceil_div(T_, rows_per_group);
-    rmsnorm_dw_partial_block<T><<<dim3((unsigned)ceil_div(d, 256), (unsigned)G), dim3(256), 0, st>>>(
-        T_, d, dyp, lddy, xp, ldx, r, rows_per_group, partial);
+    rmsnorm_dw_partial_block<T, LN><<<dim3((unsigned)ceil_div(d, 256), (unsigned)G), dim3(256), 0, st>>>(
+        T_, d, dyp, lddy, xp, ldx, mean, LN ? rstd : r, rows_per_group, partial);
   }
-  rmsnorm_dw_reduce<<<dim3((unsigned)ceil_div(d, kReduceCols)), dim3(256), 0, st>>>(G, d, partial, dw);
+  rmsnorm_dw_reduce<<<dim3((unsigned)ceil_div(d, kReduceCols)), dim3(256), 0, st>>>(
+      G, d, kCols * d, partial, dw);
+  if constexpr (LN)
+    rmsnorm_dw_reduce<<<dim3((unsigned)ceil_div(d, kReduceCols)), dim3(256), 0, st>>>(
+        G, d, kCols * d, partial + d, db);
   return launch_status();
 }
 
@@ -484,8 +606,9 @@ extern "C" int fo_rmsnorm_fwd(int dtype, int64_t T, int64_t d, const void* x, in
   if (T == 0) return FO_OK;
   if (!x || !w || !y) return FO_ERR_NULL;
   hipStream_t st = as_stream(stream);
-  return dtype == FO_F32 ? fwd_impl<float>(T, d, x, ldx, w, eps, y, ldy, rstd, st)
-                         : fwd_impl<bf16>(T, d, x, ldx, w, eps, y, ldy, rstd, st);
+  return dtype == FO_F32
+             ? fwd_impl<float, false>(T, d, x, ldx, w, nullptr, eps, y, ldy, nullptr, rstd, st)
+             : fwd_impl<bf16, false>(T, d, x, ldx, w, nullptr, eps, y, ldy, nullptr, rstd, st);
 }
 
 extern "C" int fo_rmsnorm_bwd(int dtype, int64_t T, int64_t d, const void* dy, int64_t lddy,
@@ -504,6 +627,50 @@ extern "C" int fo_rmsnorm_bwd(int dtype, int64_t T, int64_t d, const void* dy, i
   if (!dy || !x || !w || !dx) return FO_ERR_NULL;
   if (!ws || ws_bytes < fo_rmsnorm_bwd_workspace(T, d)) return FO_ERR_WORKSPACE;
   return dtype == FO_F32
-             ? bwd_impl<float>(T, d, dy, lddy, x, ldx, w, rstd, eps, dx, lddx, dw, ws, st)
-             : bwd_impl<bf16>(T, d, dy, lddy, x, ldx, w, rstd, eps, dx, lddx, dw, ws, st);
+             ? bwd_impl<float, false>(T, d, dy, lddy, x, ldx, w, nullptr, rstd, eps, dx, lddx, dw,
+                                      nullptr, ws, st)
+             : bwd_impl<bf16, false>(T, d, dy, lddy, x, ldx, w, nullptr, rstd, eps, dx, lddx, dw,
+                                     nullptr, ws, st);
+}
+
+extern "C" int fo_layernorm_fwd(int dtype, int64_t T, int64_t d, const void* x, int64_t ldx,
+                                const void* w, const void* b, float eps, void* y, int64_t ldy,
+                                float* mean, float* rstd, void* stream) {
+  if (dtype != FO_F32 && dtype != FO_BF16) return FO_ERR_DTYPE;
+  if (T < 0 || d < 1 || T > INT32_MAX) return FO_ERR_SHAPE;
+  if (ldx < d || ldy < d) return FO_ERR_STRIDE;
+  if (T == 0) return FO_OK;
+  if (!x || !w || !b || !y) return FO_ERR_NULL;
+  hipStream_t st = as_stream(stream);
+  return dtype == FO_F32 ? fwd_impl<float, true>(T, d, x, ldx, w, b, eps, y, ldy, mean, rstd, st)
+                         : fwd_impl<bf16, true>(T, d, x, ldx, w, b, eps, y, ldy, mean, rstd, st);
+}
+
+extern "C" size_t fo_layernorm_bwd_workspace(int64_t T, int64_t d) {
+  if (T < 0 || d < 1) return 0;
+  const int64_t G = T > 0 ? bwd_groups(T) : 1;
+  return align_up((size_t)G * (size_t)(2 * d), 64) * sizeof(float) + 256;
+}
+
+extern "C" int fo_layernorm_bwd(int dtype, int64_t T, int64_t d, const void* dy, int64_t lddy,
+                                const void* x, int64_t ldx, const void* w, const float* mean,
+                                const float* rstd, void* dx, int64_t lddx, float* dw, float* db,
+                                void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != FO_F32 && dtype != FO_BF16) return FO_ERR_DTYPE;
+  if (T < 0 || d < 1 || T > INT32_MAX) return FO_ERR_SHAPE;
+  if (lddy < d || ldx < d || lddx < d) return FO_ERR_STRIDE;
+  if (!dw || !db) return FO_ERR_NULL;
+  hipStream_t st = as_stream(stream);
+  if (T == 0) {
+    fill_f32<<<dim3((unsigned)ceil_div(d, 256)), dim3(256), 0, st>>>(dw, d, 0.f);
+    fill_f32<<<dim3((unsigned)ceil_div(d, 256)), dim3(256), 0, st>>>(db, d, 0.f);
+    return launch_status();
+  }
+  if (!dy || !x || !w || !dx || !mean || !rstd) return FO_ERR_NULL;
+  if (!ws || ws_bytes < fo_layernorm_bwd_workspace(T, d)) return FO_ERR_WORKSPACE;
+  return dtype == FO_F32
+             ? bwd_impl<float, true>(T, d, dy, lddy, x, ldx, w, mean, rstd, 0.f, dx, lddx, dw, db,
+                                     ws, st)
+             : bwd_impl<bf16, true>(T, d, dy, lddy, x, ldx, w, mean, rstd, 0.f, dx, lddx, dw, db,
+                                    ws, st);
 }

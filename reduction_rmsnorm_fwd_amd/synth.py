@@ -34,7 +34,7 @@ TID = {
     "x": 1, "dy": 2, "w": 3, "q": 4, "k": 5, "dq": 6, "dk": 7,
     "gate": 8, "up": 9, "dh": 10, "logits": 11, "targets": 12, "ignore": 13,
     "docs": 14, "hidden": 15, "weight": 16,
-    "param": 17, "grad": 18, "exp_avg": 19, "exp_avg_sq": 20,
+    "param": 17, "grad": 18, "exp_avg": 19, "exp_avg_sq": 20, "bias": 21,
 }
 
 
@@ -177,6 +177,17 @@ def rmsnorm_inputs(cfg: Config):
     w = _as_torch(normal_f32(s, TID["w"], d, std=0.1, mean=1.0), cfg.dtype, (d,))
     dy = _as_torch(normal_f32(s, TID["dy"], T * d), cfg.dtype, (T, d))
     return dict(x=x, w=w, dy=dy, eps=cfg.eps)
+
+
+def layernorm_inputs(cfg: Config):
+    """LayerNorm: as RMSNorm's inputs but with rows of nonzero mean (x ~ N(1, 1)) and a
+    bias N(0, 0.1^2)."""
+    T, d, s = cfg.T, cfg.d, cfg.seed
+    x = _as_torch(normal_f32(s, TID["x"], T * d, mean=1.0), cfg.dtype, (T, d))
+    w = _as_torch(normal_f32(s, TID["w"], d, std=0.1, mean=1.0), cfg.dtype, (d,))
+    b = _as_torch(normal_f32(s, TID["bias"], d, std=0.1), cfg.dtype, (d,))
+    dy = _as_torch(normal_f32(s, TID["dy"], T * d), cfg.dtype, (T, d))
+    return dict(x=x, w=w, b=b, dy=dy, eps=cfg.eps)
 
 
 def rope_inputs(cfg: Config):

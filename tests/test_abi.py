@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared()
-    assert len(names) == 17, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in fo.SIGNATURES, f"binding lacks {n}"
@@ -72,6 +72,22 @@ def test_rmsnorm_validation(lib):
     assert b(BF16, 100, 64, P, 64, P, 64, P, N, 1e-5, P, 64, P, N, ws, N) == WS
     assert b(BF16, 100, 64, P, 63, P, 64, P, N, 1e-5, P, 64, P, P, ws, N) == STRIDE
     assert b(BF16, 100, 64, N, 64, P, 64, P, N, 1e-5, P, 64, P, P, ws, N) == NULL
+
+
+def test_layernorm_validation(lib):
+    f = lib.fo_layernorm_fwd
+    assert f(BF16, 4, 8, P, 8, P, N, 1e-5, P, 8, N, N, N) == NULL       # bias required
+    assert f(BF16, 4, 8, P, 7, P, P, 1e-5, P, 8, N, N, N) == STRIDE
+    assert f(5, 4, 8, P, 8, P, P, 1e-5, P, 8, N, N, N) == DTYPE
+    assert f(BF16, 0, 8, N, 8, N, N, 1e-5, N, 8, N, N, N) == OK         # empty
+    b = lib.fo_layernorm_bwd
+    ws = lib.fo_layernorm_bwd_workspace(100, 64)
+    assert ws >= 2 * 64 * 100 * 4  # a dw and a db partial row per row group
+    assert b(BF16, 100, 64, P, 64, P, 64, P, N, P, P, 64, P, P, P, ws, N) == NULL  # mean
+    assert b(BF16, 100, 64, P, 64, P, 64, P, P, N, P, 64, P, P, P, ws, N) == NULL  # rstd
+    assert b(BF16, 100, 64, P, 64, P, 64, P, P, P, P, 64, P, N, P, ws, N) == NULL  # db
+    assert b(BF16, 100, 64, P, 64, P, 64, P, P, P, P, 64, P, P, P, ws - 1, N) == WS
+    assert b(BF16, 100, 64, P, 63, P, 64, P, P, P, P, 64, P, P, P, ws, N) == STRIDE
 
 
 def test_rope_validation(lib):

@@ -1,0 +1,134 @@
+"""GPU parity of fo_layernorm_fwd / fo_layernorm_bwd against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from reduction_rmsnorm_fwd_amd import synth
+from tolerance import check
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run(fo, x, w, b, dy, eps):
+    xg, wg, bg, dyg = x.to(DEV), w.to(DEV), b.to(DEV), dy.to(DEV)
+    y, mean, rstd = fo.fo_layernorm_fwd(xg, wg, bg, eps)
+    dx, dw, db = fo.fo_layernorm_bwd(dyg, xg, wg, mean, rstd)
+    torch.cuda.synchronize()
+    return y.cpu(), mean.cpu(), rstd.cpu(), dx.cpu(), dw.cpu(), db.cpu()
+
+
+def compare(x, w, b, dy, eps, dt, got):
+    y, mean, rstd, dx, dw, db = got
+    ry, rm, rr = oracle.layernorm_fwd(x, w, b, eps)
+    rdx, rdw, rdb = oracle.layernorm_bwd(dy, x, w, eps)
+    check(y, ry, dt, "y", single_rounding=True)
+    check(mean, rm, "f32", "mean")
+    check(rstd, rr, "f32", "rstd")
+    check(dx, rdx, dt, "dx", single_rounding=True)
+    check(dw, rdw, "f32", "dw")
+    check(db, rdb, "f32", "db")
+
+
+def small_cfg(dtype, T, d, seed=11):
+    return synth.Config(0, "ln", dtype, T=T, d=d, n_q=1, n_kv=1, head_dim=2, F=1, V=2,
+                        eps=1e-5, theta=1e4, logit_std=1, z_loss=0, ignore_frac=0,
+                        packed=False, doc_lengths=(T,), seed=seed)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+@pytest.mark.parametrize("T", [1, 67])
+def test_configs_small(gpu, cid, T):
+    cfg = synth.scaled(synth.CONFIGS[cid], T)
+    i = synth.layernorm_inputs(cfg)
+    got = run(gpu, i["x"], i["w"], i["b"], i["dy"], cfg.eps)
+    compare(i["x"], i["w"], i["b"], i["dy"], cfg.eps, cfg.dtype, got)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [13, 1000, 1025, 4097, 8, 8192, 12288])
+def test_unaligned_and_wide_rows(gpu, dtype, d):
+    cfg = small_cfg(dtype, 37, d)
+    i = synth.layernorm_inputs(cfg)
+    got = run(gpu, i["x"], i["w"], i["b"], i["dy"], cfg.eps)
+    compare(i["x"], i["w"], i["b"], i["dy"], cfg.eps, dtype, got)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_strided_and_misaligned_rows(gpu, dtype):
+    td = synth.torch_dtype(dtype)
+    T, d, ld = 50, 256, 264
+    g = torch.Generator().manual_seed(4)
+    base = (torch.randn(T, ld, generator=g) + 2).to(td)
+    w = (1 + 0.1 * torch.randn(d, generator=g)).to(td)
+    b = (0.1 * torch.randn(d, generator=g)).to(td)
+    dy = torch.randn(T, d, generator=g).to(td)
+    for off in (0, 1):  # off=1: base pointer not 16-byte aligned
+        xs = base[:, off:off + d]
+        xg = base.to(DEV)[:, off:off + d]
+        y, mean, rstd = gpu.fo_layernorm_fwd(xg, w.to(DEV), b.to(DEV), 1e-5)
+        dx, dw, db = gpu.fo_layernorm_bwd(dy.to(DEV), xg, w.to(DEV), mean, rstd)
+        torch.cuda.synchronize()
+        compare(xs, w, b, dy, 1e-5, dtype,
+                (y.cpu(), mean.cpu(), rstd.cpu(), dx.cpu(), dw.cpu(), db.cpu()))
+
+
+def test_in_place_forward_and_backward(gpu):
+    cfg = synth.scaled(synth.CONFIGS[3], 40)
+    i = synth.layernorm_inputs(cfg)
+    xg, wg, bg = i["x"].to(DEV), i["w"].to(DEV), i["b"].to(DEV)
+    ref_y, mean, rstd = gpu.fo_layernorm_fwd(xg, wg, bg, cfg.eps)
+    x2 = xg.clone()
+    gpu.fo_layernorm_fwd(x2, wg, bg, cfg.eps, y=x2, want_stats=False)
+    dyg = i["dy"].to(DEV)
+    ref_dx, ref_dw, ref_db = gpu.fo_layernorm_bwd(dyg, xg, wg, mean, rstd)
+    dy2 = dyg.clone()
+    _, dw2, db2 = gpu.fo_layernorm_bwd(dy2, xg, wg, mean, rstd, dx=dy2)
+    torch.cuda.synchronize()
+    assert torch.equal(x2, ref_y) and torch.equal(dy2, ref_dx)
+    assert torch.equal(dw2, ref_dw) and torch.equal(db2, ref_db)
+
+
+def test_empty_batch_zeroes_dw_db(gpu):
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(64, dtype=torch.bfloat16, device=DEV)
+    dw = torch.full((64,), 7.0, device=DEV)
+    db = torch.full((64,), 7.0, device=DEV)
+    st = torch.empty(0, device=DEV)
+    gpu.fo_layernorm_bwd(x, x, w, st, st, dx=x, dw=dw, db=db)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0) and torch.all(db == 0)
+
+
+def test_deterministic(gpu):
+    cfg = synth.scaled(synth.CONFIGS[4], 3000)
+    i = synth.layernorm_inputs(cfg)
+    a = run(gpu, i["x"], i["w"], i["b"], i["dy"], cfg.eps)
+    b = run(gpu, i["x"], i["w"], i["b"], i["dy"], cfg.eps)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("cid", [3, 4])
+def test_full_size_sampled(gpu, cid):
+    cfg = synth.CONFIGS[cid]
+    i = synth.layernorm_inputs(cfg)
+    y, mean, rstd, dx, dw, db = run(gpu, i["x"], i["w"], i["b"], i["dy"], cfg.eps)
+    rows = np.unique(np.concatenate([[0, 1, cfg.T - 1],
+                                     np.random.default_rng(cid).integers(0, cfg.T, 29)]))
+    x, w, b, dy = i["x"][rows], i["w"], i["b"], i["dy"][rows]
+    ry, rm, rr = oracle.layernorm_fwd(x, w, b, cfg.eps)
+    rdx, _, _ = oracle.layernorm_bwd(dy, x, w, cfg.eps)
+    check(y[rows], ry, cfg.dtype, "y", single_rounding=True)
+    check(mean[rows], rm, "f32", "mean")
+    check(rstd[rows], rr, "f32", "rstd")
+    check(dx[rows], rdx, cfg.dtype, "dx", single_rounding=True)
+    # dw and db need every row: oracle over all T in row blocks
+    rdw, rdb = np.zeros(cfg.d), np.zeros(cfg.d)
+    for r0 in range(0, cfg.T, 2048):
+        _, a, c = oracle.layernorm_bwd(i["dy"][r0:r0 + 2048], i["x"][r0:r0 + 2048], w, cfg.eps)
+        rdw += a
+        rdb += c
+    check(dw, rdw, "f32", "dw")
+    check(db, rdb, "f32", "db")
