@@ -71,7 +71,8 @@ def parse():
     p.add_argument("--no-probes", action="store_true",
                    help="skip the copy / MFMA ceiling probes and the unaligned-shape lines")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-next", action="store_true", help="skip the rows after the step (AdamW)")
+    p.add_argument("--no-next", action="store_true",
+                   help="skip the rows after the step (AdamW, LayerNorm)")
     p.add_argument("--no-isolated", action="store_true")
     p.add_argument("--only", default="", help="comma list of ops to run (profiling)")
     p.add_argument("--calib-copy", action="store_true",
@@ -276,6 +277,51 @@ def adamw_line(fo, synth, torch, stream, med, reps, copy_gbs):
     return e
 
 
+def layernorm_lines(fo, synth, torch, stream, med, reps, copy_gbs):
+    """LayerNorm forward and backward (a row after the step's ops, reported apart from
+    the step) at the Llama-3-8B layer shape, isolated with caches flushed.  Algorithmic
+    bytes: forward 2Tdb + 2db + 8T (x in, y out, w and b, mean and rstd out); backward
+    3Tdb + db + 8T + 8d (dy and x in, dx out, w, the saved statistics, dw and db out)."""
+    c3 = synth.CONFIGS[3]
+    i = synth.layernorm_inputs(c3)
+    x, w, b, dy = (i[k].to("cuda") for k in ("x", "w", "b", "dy"))
+    T, d = x.shape
+    el = x.element_size()
+    y, mean, rstd = fo.fo_layernorm_fwd(x, w, b, c3.eps)
+    dx = torch.empty_like(x)
+    dw = torch.empty(d, dtype=torch.float32, device="cuda")
+    db = torch.empty_like(dw)
+    ws = torch.empty(fo.fo_layernorm_bwd_workspace(T, d), dtype=torch.uint8, device="cuda")
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    lines = {}
+    for name, fn, byt in (
+            ("layernorm_fwd", lambda: fo.fo_layernorm_fwd(x, w, b, c3.eps, y=y, mean=mean, rstd=rstd),
+             2 * T * d * el + 2 * d * el + 8 * T),
+            ("layernorm_bwd", lambda: fo.fo_layernorm_bwd(dy, x, w, mean, rstd, dx=dx, dw=dw, db=db, ws=ws),
+             3 * T * d * el + d * el + 8 * T + 8 * d)):
+        ts = []
+        for r in range(reps + 2):
+            scratch.fill_(1.0)
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            e.record(stream)
+            e.synchronize()
+            if r >= 2:
+                ts.append(a.elapsed_time(e))
+        ms = med(ts)
+        ent = {"workload": f"T {T}, d {d}, bf16 (Llama-3-8B layer shape)",
+               "ms_isolated_median": round(ms, 4), "algorithmic_MB": round(byt / 1e6, 3),
+               "GBps": round(byt / (ms * 1e-3) / 1e9, 1),
+               "frac_hbm_peak": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if copy_gbs:
+            ent["frac_measured_copy"] = round(ent["GBps"] / copy_gbs, 4)
+        lines[name] = ent
+    del scratch
+    print("# layernorm lines done", file=sys.stderr, flush=True)
+    return lines
+
+
 def unaligned_lines(fo, synth, torch, stream, med):
     """The scalar (unaligned) paths at the Llama-3-8B token count, reported apart from
     the aligned per-op lines: RMSNorm with d = 4097 and SwiGLU with F = 14337 (rows not
@@ -403,8 +449,9 @@ def gpu_bench(args):
     unaligned = None if args.no_probes or only else unaligned_lines(fo, synth, torch, stream, med)
     next_ops = None
     if not (args.no_next or only):
-        next_ops = {"adamw_step": adamw_line(fo, synth, torch, stream, med, 20,
-                                             peaks["copy_GBps"] if peaks else None)}
+        cg = peaks["copy_GBps"] if peaks else None
+        next_ops = {"adamw_step": adamw_line(fo, synth, torch, stream, med, 20, cg)}
+        next_ops.update(layernorm_lines(fo, synth, torch, stream, med, args.iso_reps, cg))
     traffic = measured_traffic()
     per_op = {}
     for i, (name, _, work, bound) in enumerate(wl.ops):

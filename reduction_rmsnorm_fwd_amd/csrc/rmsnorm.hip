@@ -56,6 +56,9 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
 #pragma unroll
       for (int j = 0; j < VEC; ++j) s += to_f32(xv[i].v[j]);
     mu = wave_sum(s) / (float)d;
+    // re-widen for the variance sweep instead of holding fp32 copies (as below)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(xv[i].raw));
   }
   float ss = 0.f;
 #pragma unroll
@@ -410,9 +413,12 @@ __global__ __launch_bounds__(256) void rmsnorm_dw_partial_block(
 constexpr int kReducePhases = 64;
 constexpr int kReduceCols = 16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Columns [0, split) go to out0, columns [split, d) to out1 (LayerNorm: dw then db from
+// one launch over the 2d-wide partial rows).
 __global__ __launch_bounds__(256) void rmsnorm_dw_reduce(int64_t G, int64_t d, int64_t ldp,
                                                         const float* __restrict__ partial,
-                                                        float* __restrict__ dw) {
+                                                        float* __restrict__ out0, int64_t split,
+                                                        float* __restrict__ out1) {
   __shared__ float sh[kReducePhases][kReduceCols + 1];
   const int q = threadIdx.x & 3;  // column quad
   const int ph = threadIdx.x >> 2;
@@ -446,7 +452,8 @@ __global__ __launch_bounds__(256) void rmsnorm_dw_reduce(int64_t G, int64_t d, i
     const int64_t jc = (int64_t)blockIdx.x * kReduceCols + threadIdx.x;
     float t = sh[0][threadIdx.x];
     for (int p = 1; p < kReducePhases; ++p) t += sh[p][threadIdx.x];
-    if (jc < d) dw[jc] = t;
+    if (jc < split) out0[jc] = t;
+    else if (jc < d) out1[jc - split] = t;
   }
 }
 
@@ -578,11 +585,8 @@ int bwd_impl(int64_t T_, int64_t d, const void* dy, int64_t lddy, const void* x,
     rmsnorm_dw_partial_block<T, LN><<<dim3((unsigned)ceil_div(d, 256), (unsigned)G), dim3(256), 0, st>>>(
         T_, d, dyp, lddy, xp, ldx, mean, LN ? rstd : r, rows_per_group, partial);
   }
-  rmsnorm_dw_reduce<<<dim3((unsigned)ceil_div(d, kReduceCols)), dim3(256), 0, st>>>(
-      G, d, kCols * d, partial, dw);
-  if constexpr (LN)
-    rmsnorm_dw_reduce<<<dim3((unsigned)ceil_div(d, kReduceCols)), dim3(256), 0, st>>>(
-        G, d, kCols * d, partial + d, db);
+  rmsnorm_dw_reduce<<<dim3((unsigned)ceil_div(kCols * d, kReduceCols)), dim3(256), 0, st>>>(
+      G, kCols * d, kCols * d, partial, dw, d, db);
   return launch_status();
 }
 
