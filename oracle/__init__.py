@@ -21,13 +21,15 @@ forms, invariants, finite differences and independent library routines.  Parity
 unpinned by the pages themselves (fixed by a stated reading, pinned only against
 that reading): the RoPE pairing convention, the z-loss formula, the position
 of eps inside the RMSNorm and LayerNorm roots, the LayerNorm form (biased variance,
-scale and bias), and the AdamW formula behind the Adam kernel's printed signature.
+scale and bias), the exact (erf) GeLU, and the AdamW formula behind the Adam kernel's
+printed signature.
 """
 from .ops import (  # noqa: F401
     rmsnorm_fwd, rmsnorm_bwd,
     layernorm_fwd, layernorm_bwd,
     rope_angles, rope_fwd, rope_bwd,
     silu, swiglu_fwd, swiglu_bwd,
+    ACTS, act_value, act_deriv, glu_fwd, glu_bwd, act_fwd, act_bwd,
     xent_fwd_bwd, xent_rows,
     flce_fwd_bwd,
     adamw_scalars, adamw_step,

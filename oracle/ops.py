@@ -173,6 +173,66 @@ def swiglu_bwd(dh, gate, up):
 
 
 # ---------------------------------------------------------------------------
+# Other MLP activations — [FastLLM] 三 技术架构, "支持的 MLP 变体": dense MLPs, gated or
+# not, with SiLU, GeLU or ReLU.  Readings: GeLU is the exact form x Phi(x) (Phi the
+# standard normal CDF, via erf), not the tanh approximation; a gated MLP computes
+# act(gate) * up as SwiGLU does; the derivative of ReLU at 0 is taken as 0.
+# ---------------------------------------------------------------------------
+ACTS = ("silu", "gelu", "relu")
+
+
+def _erf(x):
+    from scipy.special import erf  # the error function, double precision
+    return erf(x)
+
+
+def act_value(x, act):
+    """act(x) elementwise for act in ACTS."""
+    x = _f64(x)
+    if act == "silu":
+        return silu(x)
+    if act == "gelu":
+        return x * 0.5 * (1.0 + _erf(x / np.sqrt(2.0)))
+    if act == "relu":
+        return np.maximum(x, 0.0)
+    raise ValueError(act)
+
+
+def act_deriv(x, act):
+    """d act(x) / dx elementwise."""
+    x = _f64(x)
+    if act == "silu":
+        s = _sigmoid(x)
+        return s * (1.0 + x * (1.0 - s))
+    if act == "gelu":
+        return 0.5 * (1.0 + _erf(x / np.sqrt(2.0))) + x * np.exp(-0.5 * x * x) / np.sqrt(2.0 * np.pi)
+    if act == "relu":
+        return (x > 0.0).astype(np.float64)
+    raise ValueError(act)
+
+
+def glu_fwd(gate, up, act):
+    """h = act(gate) * up."""
+    return act_value(gate, act) * _f64(up)
+
+
+def glu_bwd(dh, gate, up, act):
+    """(dgate, dup) = (dh * up * act'(gate), dh * act(gate))."""
+    dh, up = _f64(dh), _f64(up)
+    return dh * up * act_deriv(gate, act), dh * act_value(gate, act)
+
+
+def act_fwd(x, act):
+    """y = act(x) (non-gated MLP activation)."""
+    return act_value(x, act)
+
+
+def act_bwd(dy, x, act):
+    """dx = dy * act'(x)."""
+    return _f64(dy) * act_deriv(x, act)
+
+
+# ---------------------------------------------------------------------------
 # Cross-entropy with ignore_index and z-loss — [FastLLM] 三 技术架构, "损失函数体系"
 # (Cross-Entropy; Z-Loss "prevents over-confidence"), and the Triton kernel list of
 # 整体框架结构 (entropy_loss.py, z_loss.py); [HFK] "Liger" (cross_entropy).
