@@ -58,6 +58,10 @@ enum {
 
 enum { FO_F32 = 0, FO_BF16 = 1 };
 
+/* MLP activations: SiLU x s(x); GeLU x Phi(x) (exact, via erf); ReLU max(x, 0), whose
+ * derivative at 0 is taken as 0. */
+enum { FO_ACT_SILU = 0, FO_ACT_GELU = 1, FO_ACT_RELU = 2 };
+
 #define FO_ABI_VERSION 1
 
 const char* fo_status_str(int status);
@@ -145,6 +149,25 @@ int fo_swiglu_fwd(int dtype, int64_t T, int64_t F, const void* gate, int64_t ldg
 int fo_swiglu_bwd(int dtype, int64_t T, int64_t F, const void* dh, int64_t lddh,
                   const void* gate, int64_t ldg, const void* up, int64_t ldu,
                   void* dgate, int64_t lddg, void* dup, int64_t lddu, void* stream);
+
+/* ---- Other MLP activations ([FastLLM] 三 技术架构, 支持的 MLP 变体: dense MLPs, gated or
+ * not, with SiLU, GeLU or ReLU) ----
+ * fo_glu_fwd/bwd: the gated form h = act(gate) * up, arguments and layout exactly as
+ *   fo_swiglu_fwd/bwd (which are fo_glu_* with FO_ACT_SILU):
+ *   dgate = dh * up * act'(gate), dup = dh * act(gate).
+ * fo_act_fwd/bwd: the plain form y = act(x), dx = dy * act'(x); x, y, dy, dx [T,F] with
+ *   row strides; y may alias x and dx may alias dy.
+ * act: FO_ACT_SILU, FO_ACT_GELU or FO_ACT_RELU (anything else: FO_ERR_SHAPE).
+ */
+int fo_glu_fwd(int dtype, int act, int64_t T, int64_t F, const void* gate, int64_t ldg,
+               const void* up, int64_t ldu, void* h, int64_t ldh, void* stream);
+int fo_glu_bwd(int dtype, int act, int64_t T, int64_t F, const void* dh, int64_t lddh,
+               const void* gate, int64_t ldg, const void* up, int64_t ldu, void* dgate,
+               int64_t lddg, void* dup, int64_t lddu, void* stream);
+int fo_act_fwd(int dtype, int act, int64_t T, int64_t F, const void* x, int64_t ldx, void* y,
+               int64_t ldy, void* stream);
+int fo_act_bwd(int dtype, int act, int64_t T, int64_t F, const void* dy, int64_t lddy,
+               const void* x, int64_t ldx, void* dx, int64_t lddx, void* stream);
 
 /* ---- Cross-entropy with ignore_index and z-loss, forward and backward in one call
  * ([FastLLM] 损失函数体系: Cross-Entropy, Z-Loss; kernel list entropy_loss / z_loss;

@@ -19,6 +19,7 @@ __all__ = [
     "fo_swiglu_fwd", "fo_swiglu_bwd", "fo_xent_fwd_bwd", "fo_flce_fwd_bwd",
     "fo_rmsnorm_bwd_workspace", "fo_xent_workspace", "fo_flce_workspace", "fo_adamw_step",
     "fo_layernorm_fwd", "fo_layernorm_bwd", "fo_layernorm_bwd_workspace",
+    "fo_glu_fwd", "fo_glu_bwd", "fo_act_fwd", "fo_act_bwd", "ACTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfo.so")
@@ -59,6 +60,15 @@ SIGNATURES = {
     "fo_swiglu_bwd": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr,
                                      _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64,
                                      _c_ptr]),
+    "fo_glu_fwd": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_i64,
+                                  _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr]),
+    "fo_glu_bwd": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_i64,
+                                  _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr,
+                                  _c_i64, _c_ptr]),
+    "fo_act_fwd": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_i64,
+                                  _c_ptr, _c_i64, _c_ptr]),
+    "fo_act_bwd": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_i64,
+                                  _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr]),
     "fo_xent_workspace": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "fo_xent_fwd_bwd": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr,
                                        _c_i64, ctypes.c_float, ctypes.c_float, _c_ptr, _c_i64,
@@ -279,6 +289,60 @@ def fo_swiglu_bwd(dh, gate, up, dgate=None, dup=None):
         _rows(up, "up"), _ptr(dgate), _rows(dgate, "dgate"), _ptr(dup), _rows(dup, "dup"),
         _stream()))
     return dgate, dup
+
+
+ACTS = {"silu": 0, "gelu": 1, "relu": 2}  # FO_ACT_SILU, FO_ACT_GELU, FO_ACT_RELU
+
+
+def fo_glu_fwd(act, gate, up, h=None):
+    """h = act(gate) * up, act in ACTS."""
+    import torch
+    lib = load()
+    T, F = gate.shape
+    if h is None:
+        h = torch.empty((T, F), dtype=gate.dtype, device=gate.device)
+    _check("fo_glu_fwd", lib.fo_glu_fwd(_dt(gate), ACTS[act], T, F, _ptr(gate), _rows(gate, "gate"),
+                                        _ptr(up), _rows(up, "up"), _ptr(h), _rows(h, "h"),
+                                        _stream()))
+    return h
+
+
+def fo_glu_bwd(act, dh, gate, up, dgate=None, dup=None):
+    import torch
+    lib = load()
+    T, F = gate.shape
+    if dgate is None:
+        dgate = torch.empty((T, F), dtype=gate.dtype, device=gate.device)
+    if dup is None:
+        dup = torch.empty((T, F), dtype=gate.dtype, device=gate.device)
+    _check("fo_glu_bwd", lib.fo_glu_bwd(
+        _dt(gate), ACTS[act], T, F, _ptr(dh), _rows(dh, "dh"), _ptr(gate), _rows(gate, "gate"),
+        _ptr(up), _rows(up, "up"), _ptr(dgate), _rows(dgate, "dgate"), _ptr(dup),
+        _rows(dup, "dup"), _stream()))
+    return dgate, dup
+
+
+def fo_act_fwd(act, x, y=None):
+    """y = act(x), act in ACTS."""
+    import torch
+    lib = load()
+    T, F = x.shape
+    if y is None:
+        y = torch.empty((T, F), dtype=x.dtype, device=x.device)
+    _check("fo_act_fwd", lib.fo_act_fwd(_dt(x), ACTS[act], T, F, _ptr(x), _rows(x, "x"), _ptr(y),
+                                        _rows(y, "y"), _stream()))
+    return y
+
+
+def fo_act_bwd(act, dy, x, dx=None):
+    import torch
+    lib = load()
+    T, F = x.shape
+    if dx is None:
+        dx = torch.empty((T, F), dtype=x.dtype, device=x.device)
+    _check("fo_act_bwd", lib.fo_act_bwd(_dt(x), ACTS[act], T, F, _ptr(dy), _rows(dy, "dy"), _ptr(x),
+                                        _rows(x, "x"), _ptr(dx), _rows(dx, "dx"), _stream()))
+    return dx
 
 
 # ------------------------------------------------------------- cross-entropy

@@ -1,4 +1,6 @@
-// SwiGLU forward and backward for gfx950.
+// SwiGLU forward and backward for gfx950, and the other MLP activations of the same
+// page: gated or plain, SiLU / GeLU / ReLU ("支持的 MLP 变体": dense MLPs gated or not,
+// with SiLU, GeLU or ReLU; GeLU taken as the exact x Phi(x)).
 //
 // Definition ("Fast-LLM: 高效大语言模型训练框架", 三 技术架构: gated MLP with SiLU in the
 // Transformer Block 结构 table, and mlp gated: true / activation: silu in 训练配置示例;
@@ -23,15 +25,39 @@ __device__ __forceinline__ float sigmoid_f(float g) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
+// Activations of the MLP variants: SiLU, GeLU (exact: x Phi(x)), ReLU; value and
+// derivative in fp32.
+enum Act { kSilu = FO_ACT_SILU, kGelu = FO_ACT_GELU, kRelu = FO_ACT_RELU };
+
+template <int ACT>
+__device__ __forceinline__ float act_f(float x) {
+  if constexpr (ACT == kSilu) return x * sigmoid_f(x);
+  else if constexpr (ACT == kGelu) return x * (0.5f * (1.0f + erff(x * 0.70710678118654752f)));
+  else return x > 0.f ? x : 0.f;
+}
+template <int ACT>
+__device__ __forceinline__ float act_d(float x) {
+  if constexpr (ACT == kSilu) {
+    const float s = sigmoid_f(x);
+    return s * fmaf(x, 1.0f - s, 1.0f);
+  } else if constexpr (ACT == kGelu) {
+    return fmaf(x * 0.39894228040143268f, __expf(-0.5f * x * x),
+                0.5f * (1.0f + erff(x * 0.70710678118654752f)));
+  } else {
+    return x > 0.f ? 1.f : 0.f;
+  }
+}
+
 // Index space: rows x nvr vectors (VEC elements each); nb column blocks per row.
-template <typename T, int VEC>
+// GATED: h = act(g) u; otherwise h = act(g) (u unused).
+template <typename T, int VEC, int ACT, bool GATED>
 __global__ __launch_bounds__(kThreads) void swiglu_fwd_k(int64_t nvr, int64_t nb,
                                                          const T* g, int64_t ldg, const T* u,
                                                          int64_t ldu, T* h, int64_t ldh) {
   const int64_t row = blockIdx.x / nb;
   const int64_t cb = blockIdx.x - row * nb;
   const T* gr = g + row * ldg;
-  const T* ur = u + row * ldu;
+  const T* ur = GATED ? u + row * ldu : nullptr;
   T* hr = h + row * ldh;
   const int64_t v0 = cb * (kThreads * kUnroll) + threadIdx.x;
   if constexpr (VEC > 1) {
@@ -41,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_fwd_k(int64_t nvr, int64_t nb
       const int64_t v = v0 + i * kThreads;
       if (v < nvr) {
         gv[i] = load_pack(gr + v * VEC);
-        uv[i] = load_pack(ur + v * VEC);
+        if constexpr (GATED) uv[i] = load_pack(ur + v * VEC);
       }
     }
 #pragma unroll
@@ -52,7 +78,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_fwd_k(int64_t nvr, int64_t nb
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
           const float gf = to_f32(gv[i].v[j]);
-          o.v[j] = from_f32<T>(gf * sigmoid_f(gf) * to_f32(uv[i].v[j]));
+          if constexpr (GATED) o.v[j] = from_f32<T>(act_f<ACT>(gf) * to_f32(uv[i].v[j]));
+          else o.v[j] = from_f32<T>(act_f<ACT>(gf));
         }
         store_pack(hr + v * VEC, o);
       }
@@ -63,13 +90,15 @@ __global__ __launch_bounds__(kThreads) void swiglu_fwd_k(int64_t nvr, int64_t nb
       const int64_t v = v0 + i * kThreads;
       if (v < nvr) {
         const float gf = to_f32(gr[v]);
-        hr[v] = from_f32<T>(gf * sigmoid_f(gf) * to_f32(ur[v]));
+        if constexpr (GATED) hr[v] = from_f32<T>(act_f<ACT>(gf) * to_f32(ur[v]));
+        else hr[v] = from_f32<T>(act_f<ACT>(gf));
       }
     }
   }
 }
 
-template <typename T, int VEC>
+// GATED: dg = dh u act'(g), du = dh act(g); otherwise dg = dh act'(g) (u, du unused).
+template <typename T, int VEC, int ACT, bool GATED>
 __global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t nvr, int64_t nb,
                                                          const T* dh, int64_t lddh,
                                                          const T* g, int64_t ldg, const T* u,
@@ -79,9 +108,9 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t nvr, int64_t nb
   const int64_t cb = blockIdx.x - row * nb;
   const T* dhr = dh + row * lddh;
   const T* gr = g + row * ldg;
-  const T* ur = u + row * ldu;
+  const T* ur = GATED ? u + row * ldu : nullptr;
   T* dgr = dg + row * lddg;
-  T* dur = du + row * lddu;
+  T* dur = GATED ? du + row * lddu : nullptr;
   const int64_t v0 = cb * (kThreads * kUnroll) + threadIdx.x;
   if constexpr (VEC > 1) {
     Pack<T> hv[kUnroll], gv[kUnroll], uv[kUnroll];
@@ -91,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t nvr, int64_t nb
       if (v < nvr) {
         hv[i] = load_pack(dhr + v * VEC);
         gv[i] = load_pack(gr + v * VEC);
-        uv[i] = load_pack(ur + v * VEC);
+        if constexpr (GATED) uv[i] = load_pack(ur + v * VEC);
       }
     }
 #pragma unroll
@@ -102,14 +131,23 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t nvr, int64_t nb
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
           const float gf = to_f32(gv[i].v[j]);
-          const float uf = to_f32(uv[i].v[j]);
           const float hf = to_f32(hv[i].v[j]);
-          const float s = sigmoid_f(gf);
-          og.v[j] = from_f32<T>(hf * uf * s * fmaf(gf, 1.0f - s, 1.0f));
-          ou.v[j] = from_f32<T>(hf * gf * s);
+          if constexpr (GATED && ACT == kSilu) {
+            // one sigmoid for both outputs
+            const float uf = to_f32(uv[i].v[j]);
+            const float s = sigmoid_f(gf);
+            og.v[j] = from_f32<T>(hf * uf * s * fmaf(gf, 1.0f - s, 1.0f));
+            ou.v[j] = from_f32<T>(hf * gf * s);
+          } else if constexpr (GATED) {
+            const float uf = to_f32(uv[i].v[j]);
+            og.v[j] = from_f32<T>(hf * uf * act_d<ACT>(gf));
+            ou.v[j] = from_f32<T>(hf * act_f<ACT>(gf));
+          } else {
+            og.v[j] = from_f32<T>(hf * act_d<ACT>(gf));
+          }
         }
         store_pack(dgr + v * VEC, og);
-        store_pack(dur + v * VEC, ou);
+        if constexpr (GATED) store_pack(dur + v * VEC, ou);
       }
     }
   } else {
@@ -117,10 +155,19 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t nvr, int64_t nb
     for (int i = 0; i < kUnroll; ++i) {
       const int64_t v = v0 + i * kThreads;
       if (v < nvr) {
-        const float gf = to_f32(gr[v]), uf = to_f32(ur[v]), hf = to_f32(dhr[v]);
-        const float s = sigmoid_f(gf);
-        dgr[v] = from_f32<T>(hf * uf * s * fmaf(gf, 1.0f - s, 1.0f));
-        dur[v] = from_f32<T>(hf * gf * s);
+        const float gf = to_f32(gr[v]), hf = to_f32(dhr[v]);
+        if constexpr (GATED && ACT == kSilu) {
+          const float uf = to_f32(ur[v]);
+          const float s = sigmoid_f(gf);
+          dgr[v] = from_f32<T>(hf * uf * s * fmaf(gf, 1.0f - s, 1.0f));
+          dur[v] = from_f32<T>(hf * gf * s);
+        } else if constexpr (GATED) {
+          const float uf = to_f32(ur[v]);
+          dgr[v] = from_f32<T>(hf * uf * act_d<ACT>(gf));
+          dur[v] = from_f32<T>(hf * act_f<ACT>(gf));
+        } else {
+          dgr[v] = from_f32<T>(hf * act_d<ACT>(gf));
+        }
       }
     }
   }
@@ -151,30 +198,31 @@ Geo plan(int64_t T_, int64_t F, int n, const void* const* ptr, const int64_t* ld
   return g;
 }
 
-template <typename T>
+// GATED = false: u, du (and their strides) are ignored.
+template <typename T, int ACT, bool GATED>
 int fwd_impl(int64_t T_, int64_t F, const void* g, int64_t ldg, const void* u, int64_t ldu,
              void* h, int64_t ldh, hipStream_t st) {
-  const void* p[3] = {g, u, h};
-  const int64_t l[3] = {ldg, ldu, ldh};
-  const Geo geo = plan<T>(T_, F, 3, p, l);
+  const void* p[3] = {g, h, u};
+  const int64_t l[3] = {ldg, ldh, ldu};
+  const Geo geo = plan<T>(T_, F, GATED ? 3 : 2, p, l);
   const dim3 grid((unsigned)(geo.rows * geo.nb)), block(kThreads);
   const T* gp = static_cast<const T*>(g);
   const T* up = static_cast<const T*>(u);
   T* hp = static_cast<T*>(h);
   if (geo.vec)
-    swiglu_fwd_k<T, Vec<T>::N><<<grid, block, 0, st>>>(geo.nvr, geo.nb, gp, ldg, up, ldu, hp, ldh);
+    swiglu_fwd_k<T, Vec<T>::N, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, gp, ldg, up, ldu, hp, ldh);
   else
-    swiglu_fwd_k<T, 1><<<grid, block, 0, st>>>(geo.nvr, geo.nb, gp, ldg, up, ldu, hp, ldh);
+    swiglu_fwd_k<T, 1, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, gp, ldg, up, ldu, hp, ldh);
   return launch_status();
 }
 
-template <typename T>
+template <typename T, int ACT, bool GATED>
 int bwd_impl(int64_t T_, int64_t F, const void* dh, int64_t lddh, const void* g, int64_t ldg,
              const void* u, int64_t ldu, void* dg, int64_t lddg, void* du, int64_t lddu,
              hipStream_t st) {
-  const void* p[5] = {dh, g, u, dg, du};
-  const int64_t l[5] = {lddh, ldg, ldu, lddg, lddu};
-  const Geo geo = plan<T>(T_, F, 5, p, l);
+  const void* p[5] = {dh, g, dg, u, du};
+  const int64_t l[5] = {lddh, ldg, lddg, ldu, lddu};
+  const Geo geo = plan<T>(T_, F, GATED ? 5 : 3, p, l);
   const dim3 grid((unsigned)(geo.rows * geo.nb)), block(kThreads);
   const T* dhp = static_cast<const T*>(dh);
   const T* gp = static_cast<const T*>(g);
@@ -182,12 +230,45 @@ int bwd_impl(int64_t T_, int64_t F, const void* dh, int64_t lddh, const void* g,
   T* dgp = static_cast<T*>(dg);
   T* dup = static_cast<T*>(du);
   if (geo.vec)
-    swiglu_bwd_k<T, Vec<T>::N><<<grid, block, 0, st>>>(geo.nvr, geo.nb, dhp, lddh, gp, ldg, up,
-                                                       ldu, dgp, lddg, dup, lddu);
+    swiglu_bwd_k<T, Vec<T>::N, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, dhp, lddh, gp, ldg, up,
+                                                                   ldu, dgp, lddg, dup, lddu);
   else
-    swiglu_bwd_k<T, 1><<<grid, block, 0, st>>>(geo.nvr, geo.nb, dhp, lddh, gp, ldg, up, ldu,
-                                               dgp, lddg, dup, lddu);
+    swiglu_bwd_k<T, 1, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, dhp, lddh, gp, ldg, up, ldu,
+                                                           dgp, lddg, dup, lddu);
   return launch_status();
+}
+
+// dtype x activation dispatch
+template <bool GATED>
+int fwd_dispatch(int dtype, int act, int64_t T_, int64_t F, const void* g, int64_t ldg,
+                 const void* u, int64_t ldu, void* h, int64_t ldh, hipStream_t st) {
+#define FO_F(TY, A) return fwd_impl<TY, A, GATED>(T_, F, g, ldg, u, ldu, h, ldh, st)
+  if (dtype == FO_F32) {
+    if (act == kSilu) FO_F(float, kSilu);
+    if (act == kGelu) FO_F(float, kGelu);
+    FO_F(float, kRelu);
+  }
+  if (act == kSilu) FO_F(bf16, kSilu);
+  if (act == kGelu) FO_F(bf16, kGelu);
+  FO_F(bf16, kRelu);
+#undef FO_F
+}
+
+template <bool GATED>
+int bwd_dispatch(int dtype, int act, int64_t T_, int64_t F, const void* dh, int64_t lddh,
+                 const void* g, int64_t ldg, const void* u, int64_t ldu, void* dg, int64_t lddg,
+                 void* du, int64_t lddu, hipStream_t st) {
+#define FO_B(TY, A) \
+  return bwd_impl<TY, A, GATED>(T_, F, dh, lddh, g, ldg, u, ldu, dg, lddg, du, lddu, st)
+  if (dtype == FO_F32) {
+    if (act == kSilu) FO_B(float, kSilu);
+    if (act == kGelu) FO_B(float, kGelu);
+    FO_B(float, kRelu);
+  }
+  if (act == kSilu) FO_B(bf16, kSilu);
+  if (act == kGelu) FO_B(bf16, kGelu);
+  FO_B(bf16, kRelu);
+#undef FO_B
 }
 
 bool grid_fits(int64_t T_, int64_t F) {
@@ -201,28 +282,66 @@ bool grid_fits(int64_t T_, int64_t F) {
 
 using namespace fo;
 
-extern "C" int fo_swiglu_fwd(int dtype, int64_t T, int64_t F, const void* gate, int64_t ldg,
-                             const void* up, int64_t ldu, void* h, int64_t ldh, void* stream) {
+static bool act_ok(int act) { return act == FO_ACT_SILU || act == FO_ACT_GELU || act == FO_ACT_RELU; }
+
+extern "C" int fo_glu_fwd(int dtype, int act, int64_t T, int64_t F, const void* gate,
+                          int64_t ldg, const void* up, int64_t ldu, void* h, int64_t ldh,
+                          void* stream) {
   if (dtype != FO_F32 && dtype != FO_BF16) return FO_ERR_DTYPE;
+  if (!act_ok(act)) return FO_ERR_SHAPE;
   if (T < 0 || F < 1 || !grid_fits(T, F)) return FO_ERR_SHAPE;
   if (ldg < F || ldu < F || ldh < F) return FO_ERR_STRIDE;
   if (T == 0) return FO_OK;
   if (!gate || !up || !h) return FO_ERR_NULL;
-  hipStream_t st = as_stream(stream);
-  return dtype == FO_F32 ? fwd_impl<float>(T, F, gate, ldg, up, ldu, h, ldh, st)
-                         : fwd_impl<bf16>(T, F, gate, ldg, up, ldu, h, ldh, st);
+  return fwd_dispatch<true>(dtype, act, T, F, gate, ldg, up, ldu, h, ldh, as_stream(stream));
+}
+
+extern "C" int fo_glu_bwd(int dtype, int act, int64_t T, int64_t F, const void* dh,
+                          int64_t lddh, const void* gate, int64_t ldg, const void* up,
+                          int64_t ldu, void* dgate, int64_t lddg, void* dup, int64_t lddu,
+                          void* stream) {
+  if (dtype != FO_F32 && dtype != FO_BF16) return FO_ERR_DTYPE;
+  if (!act_ok(act)) return FO_ERR_SHAPE;
+  if (T < 0 || F < 1 || !grid_fits(T, F)) return FO_ERR_SHAPE;
+  if (lddh < F || ldg < F || ldu < F || lddg < F || lddu < F) return FO_ERR_STRIDE;
+  if (T == 0) return FO_OK;
+  if (!dh || !gate || !up || !dgate || !dup) return FO_ERR_NULL;
+  return bwd_dispatch<true>(dtype, act, T, F, dh, lddh, gate, ldg, up, ldu, dgate, lddg, dup,
+                            lddu, as_stream(stream));
+}
+
+extern "C" int fo_swiglu_fwd(int dtype, int64_t T, int64_t F, const void* gate, int64_t ldg,
+                             const void* up, int64_t ldu, void* h, int64_t ldh, void* stream) {
+  return fo_glu_fwd(dtype, FO_ACT_SILU, T, F, gate, ldg, up, ldu, h, ldh, stream);
 }
 
 extern "C" int fo_swiglu_bwd(int dtype, int64_t T, int64_t F, const void* dh, int64_t lddh,
                              const void* gate, int64_t ldg, const void* up, int64_t ldu,
                              void* dgate, int64_t lddg, void* dup, int64_t lddu, void* stream) {
+  return fo_glu_bwd(dtype, FO_ACT_SILU, T, F, dh, lddh, gate, ldg, up, ldu, dgate, lddg, dup,
+                    lddu, stream);
+}
+
+extern "C" int fo_act_fwd(int dtype, int act, int64_t T, int64_t F, const void* x,
+                          int64_t ldx, void* y, int64_t ldy, void* stream) {
   if (dtype != FO_F32 && dtype != FO_BF16) return FO_ERR_DTYPE;
+  if (!act_ok(act)) return FO_ERR_SHAPE;
   if (T < 0 || F < 1 || !grid_fits(T, F)) return FO_ERR_SHAPE;
-  if (lddh < F || ldg < F || ldu < F || lddg < F || lddu < F) return FO_ERR_STRIDE;
+  if (ldx < F || ldy < F) return FO_ERR_STRIDE;
   if (T == 0) return FO_OK;
-  if (!dh || !gate || !up || !dgate || !dup) return FO_ERR_NULL;
-  hipStream_t st = as_stream(stream);
-  return dtype == FO_F32
-             ? bwd_impl<float>(T, F, dh, lddh, gate, ldg, up, ldu, dgate, lddg, dup, lddu, st)
-             : bwd_impl<bf16>(T, F, dh, lddh, gate, ldg, up, ldu, dgate, lddg, dup, lddu, st);
+  if (!x || !y) return FO_ERR_NULL;
+  return fwd_dispatch<false>(dtype, act, T, F, x, ldx, nullptr, F, y, ldy, as_stream(stream));
+}
+
+extern "C" int fo_act_bwd(int dtype, int act, int64_t T, int64_t F, const void* dy,
+                          int64_t lddy, const void* x, int64_t ldx, void* dx, int64_t lddx,
+                          void* stream) {
+  if (dtype != FO_F32 && dtype != FO_BF16) return FO_ERR_DTYPE;
+  if (!act_ok(act)) return FO_ERR_SHAPE;
+  if (T < 0 || F < 1 || !grid_fits(T, F)) return FO_ERR_SHAPE;
+  if (lddy < F || ldx < F || lddx < F) return FO_ERR_STRIDE;
+  if (T == 0) return FO_OK;
+  if (!dy || !x || !dx) return FO_ERR_NULL;
+  return bwd_dispatch<false>(dtype, act, T, F, dy, lddy, x, ldx, nullptr, F, dx, lddx, nullptr, F,
+                             as_stream(stream));
 }

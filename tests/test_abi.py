@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared()
-    assert len(names) == 20, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in fo.SIGNATURES, f"binding lacks {n}"
@@ -113,6 +113,23 @@ def test_swiglu_validation(lib):
     assert b(BF16, 4, 8, P, 8, P, 8, P, 8, P, 8, P, 7, N) == STRIDE
     assert b(BF16, 4, 8, P, 8, P, 8, P, 8, N, 8, P, 8, N) == NULL
     assert b(2, 4, 8, P, 8, P, 8, P, 8, P, 8, P, 8, N) == DTYPE
+
+
+def test_activation_validation(lib):
+    g, a = lib.fo_glu_fwd, lib.fo_act_fwd
+    assert g(BF16, 3, 4, 8, P, 8, P, 8, P, 8, N) == SHAPE      # unknown activation
+    assert g(BF16, 1, 4, 8, P, 8, P, 7, P, 8, N) == STRIDE
+    assert g(BF16, 2, 4, 8, P, 8, N, 8, P, 8, N) == NULL
+    assert g(BF16, 1, 0, 8, N, 8, N, 8, N, 8, N) == OK         # empty
+    assert a(BF16, -1, 4, 8, P, 8, P, 8, N) == SHAPE
+    assert a(BF16, 1, 4, 8, P, 8, P, 7, N) == STRIDE
+    assert a(BF16, 2, 4, 8, N, 8, P, 8, N) == NULL
+    assert a(7, 1, 4, 8, P, 8, P, 8, N) == DTYPE
+    gb, ab = lib.fo_glu_bwd, lib.fo_act_bwd
+    assert gb(BF16, 1, 4, 8, P, 8, P, 8, P, 8, P, 8, N, 8, N) == NULL
+    assert gb(BF16, 5, 4, 8, P, 8, P, 8, P, 8, P, 8, P, 8, N) == SHAPE
+    assert ab(BF16, 1, 4, 8, P, 8, P, 8, N, 8, N) == NULL
+    assert ab(BF16, 1, 4, 0, P, 8, P, 8, P, 8, N) == SHAPE
 
 
 def test_xent_validation(lib):
