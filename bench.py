@@ -72,7 +72,7 @@ def parse():
                    help="skip the copy / MFMA ceiling probes and the unaligned-shape lines")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-next", action="store_true",
-                   help="skip the rows after the step (AdamW, LayerNorm)")
+                   help="skip the rows after the step (AdamW, LayerNorm, GeLU MLP activations)")
     p.add_argument("--no-isolated", action="store_true")
     p.add_argument("--only", default="", help="comma list of ops to run (profiling)")
     p.add_argument("--calib-copy", action="store_true",
@@ -322,6 +322,47 @@ def layernorm_lines(fo, synth, torch, stream, med, reps, copy_gbs):
     return lines
 
 
+def activation_lines(fo, synth, torch, stream, med, reps, copy_gbs):
+    """GeLU-gated and plain GeLU MLP activations (rows after the step's ops, reported apart
+    from the step) at the Llama-3-8B MLP width (T 8192, F 14336, bf16), isolated with
+    caches flushed.  Bytes: gated 3TFb forward, 5TFb backward; plain 2TFb, 3TFb."""
+    c3 = synth.CONFIGS[3]
+    i = synth.swiglu_inputs(c3)
+    g, u, dh = (i[k].to("cuda") for k in ("gate", "up", "dh"))
+    T, F = g.shape
+    b = g.element_size()
+    h = torch.empty_like(g)
+    dg, du = torch.empty_like(g), torch.empty_like(g)
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    lines = {}
+    for name, fn, byt in (
+            ("geglu_fwd", lambda: fo.fo_glu_fwd("gelu", g, u, h=h), 3 * T * F * b),
+            ("geglu_bwd", lambda: fo.fo_glu_bwd("gelu", dh, g, u, dgate=dg, dup=du), 5 * T * F * b),
+            ("gelu_fwd", lambda: fo.fo_act_fwd("gelu", g, y=h), 2 * T * F * b),
+            ("gelu_bwd", lambda: fo.fo_act_bwd("gelu", dh, g, dx=dg), 3 * T * F * b)):
+        ts = []
+        for r in range(reps + 2):
+            scratch.fill_(1.0)
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            e.record(stream)
+            e.synchronize()
+            if r >= 2:
+                ts.append(a.elapsed_time(e))
+        ms = med(ts)
+        ent = {"workload": f"T {T}, F {F}, bf16 (Llama-3-8B MLP width)",
+               "ms_isolated_median": round(ms, 4), "algorithmic_MB": round(byt / 1e6, 3),
+               "GBps": round(byt / (ms * 1e-3) / 1e9, 1),
+               "frac_hbm_peak": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if copy_gbs:
+            ent["frac_measured_copy"] = round(ent["GBps"] / copy_gbs, 4)
+        lines[name] = ent
+    del scratch
+    print("# activation lines done", file=sys.stderr, flush=True)
+    return lines
+
+
 def unaligned_lines(fo, synth, torch, stream, med):
     """The scalar (unaligned) paths at the Llama-3-8B token count, reported apart from
     the aligned per-op lines: RMSNorm with d = 4097 and SwiGLU with F = 14337 (rows not
@@ -452,6 +493,7 @@ def gpu_bench(args):
         cg = peaks["copy_GBps"] if peaks else None
         next_ops = {"adamw_step": adamw_line(fo, synth, torch, stream, med, 20, cg)}
         next_ops.update(layernorm_lines(fo, synth, torch, stream, med, args.iso_reps, cg))
+        next_ops.update(activation_lines(fo, synth, torch, stream, med, args.iso_reps, cg))
     traffic = measured_traffic()
     per_op = {}
     for i, (name, _, work, bound) in enumerate(wl.ops):
