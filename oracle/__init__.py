@@ -21,7 +21,8 @@ forms, invariants, finite differences and independent library routines.  Parity
 unpinned by the pages themselves (fixed by a stated reading, pinned only against
 that reading): the RoPE pairing convention, the z-loss formula, the position
 of eps inside the RMSNorm and LayerNorm roots, the LayerNorm form (biased variance,
-scale and bias), the exact (erf) GeLU, and the AdamW formula behind the Adam kernel's
+scale and bias), the exact (erf) GeLU, the soft-target (distillation) cross-entropy form, and the AdamW
+formula behind the Adam kernel's
 printed signature.
 """
 from .ops import (  # noqa: F401
@@ -30,7 +31,7 @@ from .ops import (  # noqa: F401
     rope_angles, rope_fwd, rope_bwd,
     silu, swiglu_fwd, swiglu_bwd,
     ACTS, act_value, act_deriv, glu_fwd, glu_bwd, act_fwd, act_bwd,
-    xent_fwd_bwd, xent_rows,
+    xent_fwd_bwd, xent_rows, distill_fwd_bwd,
     flce_fwd_bwd,
     adamw_scalars, adamw_step,
 )

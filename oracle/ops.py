@@ -291,6 +291,39 @@ def xent_fwd_bwd(logits, targets, ignore_index=-100, z_loss=0.0, dloss=1.0):
 
 
 # ---------------------------------------------------------------------------
+# Soft-target cross-entropy (distillation) — [FastLLM] 三 技术架构, "损失函数体系": label
+# entropy and distillation losses next to the hard-label cross-entropy, computed by the
+# framework's fused entropy-loss kernel.  No formula is printed; the reading is the
+# cross-entropy of the student's softmax against the teacher's softmax (temperature 1),
+# averaged over the rows a mask keeps; the KL divergence (cross-entropy minus the
+# teacher's entropy, same gradient) is returned beside it.
+# ---------------------------------------------------------------------------
+def _log_softmax(z):
+    m = np.max(z, axis=-1, keepdims=True)
+    return z - m - np.log(np.sum(np.exp(z - m), axis=-1, keepdims=True))
+
+
+def distill_fwd_bwd(logits, teacher, row_mask=None, dloss=1.0):
+    """p = softmax(teacher), q = softmax(logits) per row; over the N rows with a
+    nonzero mask (all rows if None):
+        loss = (1/N) sum_t -sum_v p log q,   kl = (1/N) sum_t sum_v p (log p - log q),
+        dlogits = dloss (q - p) / N  (zero rows where the mask is 0; N = 0: all zero)."""
+    z, zt = _f64(logits), _f64(teacher)
+    T = z.shape[0]
+    keep = np.ones(T, dtype=bool) if row_mask is None else (_i64(row_mask) != 0)
+    n = int(keep.sum())
+    lq, lp = _log_softmax(z), _log_softmax(zt)
+    p = np.exp(lp)
+    ce = -np.sum(p * lq, axis=-1)
+    kl = np.sum(p * (lp - lq), axis=-1)
+    d = np.zeros_like(z)
+    if n:
+        d[keep] = dloss * (np.exp(lq[keep]) - p[keep]) / n
+    return dict(loss=float(ce[keep].sum() / n) if n else 0.0,
+                kl=float(kl[keep].sum() / n) if n else 0.0, n_valid=n, dlogits=d)
+
+
+# ---------------------------------------------------------------------------
 # Fused linear cross-entropy — [HFK] "Liger" (fused_linear_cross_entropy: the lm-head
 # projection and the loss fused so that large vocabularies stay feasible in memory).
 # Definition: the composition xent(H W^T) with dH = dZ W and dW = dZ^T H, where dZ
