@@ -191,6 +191,25 @@ int fo_xent_fwd_bwd(int dtype, int64_t T, int64_t V, const void* logits, int64_t
                     int64_t* n_valid, int32_t* status, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* ---- Soft-target cross-entropy / distillation ([FastLLM] 损失函数体系: label-entropy and
+ * distillation losses beside the hard-label cross-entropy; read as the cross-entropy
+ * of the student's softmax against the teacher's, temperature 1) ----
+ *   q = softmax(logits[t]), p = softmax(teacher[t]) over V;  over the N rows whose
+ *   row_mask byte is nonzero (row_mask: device uint8 [T], or NULL = every row):
+ *   *loss = (1/N) sum_t -sum_v p log q;   *kl = (1/N) sum_t sum_v p (log p - log q)
+ *   dlogits = dloss (q - p) / N, zero rows where the mask is 0 (N = 0: all zero).
+ *   logits, teacher, dlogits [T,V] of dtype (FO_F32 or FO_BF16) with row strides ldl,
+ *   ldt, ldd; dlogits may be NULL (forward only) or the logits memory itself (same
+ *   stride).  loss, kl (may be NULL), n_valid (may be NULL): device scalars.
+ *   ws: fo_distill_workspace(T, V) bytes.  HBM traffic: both rows read once and dlogits
+ *   written once for rows of up to 16 K vectors (131072 bf16 / 65536 fp32 values).
+ */
+size_t fo_distill_workspace(int64_t T, int64_t V);
+int fo_distill_fwd_bwd(int dtype, int64_t T, int64_t V, const void* logits, int64_t ldl,
+                       const void* teacher, int64_t ldt, const uint8_t* row_mask, float dloss,
+                       void* dlogits, int64_t ldd, float* loss, float* kl, int64_t* n_valid,
+                       void* ws, size_t ws_bytes, void* stream);
+
 /* ---- Fused linear cross-entropy ([HFK] Liger FusedLinearCrossEntropy: the lm-head
  * projection fused with the loss so the full logits never exist) ----
  * Computes the cross-entropy above on Z = hidden * weight^T without materialising Z:

@@ -20,6 +20,7 @@ __all__ = [
     "fo_rmsnorm_bwd_workspace", "fo_xent_workspace", "fo_flce_workspace", "fo_adamw_step",
     "fo_layernorm_fwd", "fo_layernorm_bwd", "fo_layernorm_bwd_workspace",
     "fo_glu_fwd", "fo_glu_bwd", "fo_act_fwd", "fo_act_bwd", "ACTS",
+    "fo_distill_fwd_bwd", "fo_distill_workspace",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfo.so")
@@ -74,6 +75,10 @@ SIGNATURES = {
                                        _c_i64, ctypes.c_float, ctypes.c_float, _c_ptr, _c_i64,
                                        _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_size_t,
                                        _c_ptr]),
+    "fo_distill_workspace": (ctypes.c_size_t, [_c_i64, _c_i64]),
+    "fo_distill_fwd_bwd": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr,
+                                          _c_i64, _c_ptr, ctypes.c_float, _c_ptr, _c_i64, _c_ptr,
+                                          _c_ptr, _c_ptr, _c_ptr, ctypes.c_size_t, _c_ptr]),
     "fo_flce_workspace": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int]),
     "fo_adamw_step": (ctypes.c_int, [ctypes.c_int32, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                      _c_ptr, _c_ptr, ctypes.c_float, ctypes.c_float,
@@ -383,6 +388,36 @@ def fo_xent_fwd_bwd(logits, targets, ignore_index=-100, z_loss=0.0, dloss=1.0, d
 
 
 # ------------------------------------------------ fused linear cross-entropy
+def fo_distill_workspace(T, V):
+    return load_library().fo_distill_workspace(T, V)
+
+
+def fo_distill_fwd_bwd(logits, teacher, row_mask=None, dloss=1.0, dlogits=None, want_grad=True,
+                       ws=None, out=None):
+    """Soft-target cross-entropy of logits against softmax(teacher); returns dict(loss,
+    kl, n_valid, dlogits).  row_mask: optional uint8 device tensor [T]."""
+    import torch
+    lib = load()
+    T, V = logits.shape
+    if want_grad and dlogits is None:
+        dlogits = torch.empty_like(logits)
+    if out is None:
+        out = dict(loss=torch.empty((), dtype=torch.float32, device=logits.device),
+                   kl=torch.empty((), dtype=torch.float32, device=logits.device),
+                   n_valid=torch.empty((), dtype=torch.int64, device=logits.device))
+    if ws is None:
+        ws = _ws(lib.fo_distill_workspace(T, V), logits.device)
+    if row_mask is not None and row_mask.dtype != torch.uint8:
+        raise ValueError("row_mask must be uint8")
+    _check("fo_distill_fwd_bwd", lib.fo_distill_fwd_bwd(
+        _dt(logits), T, V, _ptr(logits), _rows(logits, "logits"), _ptr(teacher),
+        _rows(teacher, "teacher"), _ptr(row_mask), float(dloss), _ptr(dlogits),
+        _rows(dlogits, "dlogits") if dlogits is not None else V, _ptr(out["loss"]),
+        _ptr(out["kl"]), _ptr(out["n_valid"]), _ptr(ws), ws.numel(), _stream()))
+    out["dlogits"] = dlogits
+    return out
+
+
 def fo_flce_workspace(T, H, V, chunk_tokens=0, dweight_dtype=FO_F32):
     return load_library().fo_flce_workspace(T, H, V, chunk_tokens, dweight_dtype)
 

@@ -1,0 +1,361 @@
+// Soft-target cross-entropy (distillation) forward+backward for gfx950.
+//
+// Definition ("Fast-LLM: 高效大语言模型训练框架", 三 技术架构, 损失函数体系: label-entropy
+// and distillation losses beside the hard-label cross-entropy, computed by the
+// framework's fused entropy-loss kernel), read as the cross-entropy of the student's
+// softmax against the teacher's (temperature 1), over the rows a mask keeps:
+//   q = softmax(z), p = softmax(zt) per row;  loss = (1/N) sum_t -sum_v p log q,
+//   kl = (1/N) sum_t sum_v p (log p - log q),  dz = dloss (q - p) / N.
+// Per row, one sweep gives both online logsumexps and the two p-weighted sums
+//   A = sum_v exp(zt - m_t) z,  B = sum_v exp(zt - m_t) zt   (rescaled with m_t),
+// so -sum p log q = lse_z - A/s_t and -sum p log p = lse_t - B/s_t; a second sweep over
+// the same values writes dz.  For rows of up to 16 K vectors both rows stay on chip
+// between the sweeps: the student row in VGPRs, the teacher row in VGPRs and (for the
+// longest rows) LDS, filled by buffer loads that write LDS directly; so HBM sees each
+// input once and dz once (3 T V b).  Longer or unaligned rows re-read both rows in the
+// second sweep (from L2 / MALL).
+#include "xent_kernels.hpp"
+
+namespace fo {
+namespace {
+
+using xent::Counters;
+
+constexpr int kRowThreads = 1024;
+typedef __attribute__((address_space(3))) void* lds_vptr;
+constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
+
+// Per-thread (then per-row) state of the sweep: student (ms, ss), teacher (mt, st) and
+// the teacher-weighted sums A (of z) and B (of zt), all relative to mt.
+struct Stats {
+  float ms, ss, mt, st, a, b;
+};
+
+__device__ __forceinline__ void stats_init(Stats& s) {
+  s.ms = -INFINITY; s.ss = 0.f; s.mt = -INFINITY; s.st = 0.f; s.a = 0.f; s.b = 0.f;
+}
+
+__device__ __forceinline__ void stats_merge(Stats& s, const Stats& o) {
+  lse_merge(s.ms, s.ss, o.ms, o.ss);
+  const float m = fmaxf(s.mt, o.mt);
+  if (m == -INFINITY) return;
+  const float f1 = __expf(s.mt - m), f2 = __expf(o.mt - m);
+  s.st = s.st * f1 + o.st * f2;
+  s.a = s.a * f1 + o.a * f2;
+  s.b = s.b * f1 + o.b * f2;
+  s.mt = m;
+}
+
+// VEC values of the student (z) and teacher (t)
+// (exponentials: accurate for fp32 rows, the hardware path for bf16 rows, as the
+// hard-label kernels)
+template <typename T, int VEC>
+__device__ __forceinline__ void stats_add(Stats& s, const float* z, const float* t) {
+  float vz = z[0], vt = t[0];
+#pragma unroll
+  for (int j = 1; j < VEC; ++j) { vz = fmaxf(vz, z[j]); vt = fmaxf(vt, t[j]); }
+  if (vz > s.ms) { s.ss *= xent::ex<T>(s.ms - vz); s.ms = vz; }
+  if (vt > s.mt) {
+    const float f = xent::ex<T>(s.mt - vt);
+    s.st *= f; s.a *= f; s.b *= f; s.mt = vt;
+  }
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    s.ss += xent::ex<T>(z[j] - s.ms);
+    const float e = xent::ex<T>(t[j] - s.mt);
+    s.st += e;
+    s.a = fmaf(e, z[j], s.a);
+    s.b = fmaf(e, t[j], s.b);
+  }
+}
+
+// Fixed-order workgroup merge: every thread gets the row's totals.
+template <int NT>
+__device__ __forceinline__ Stats block_stats(Stats s, Stats* sh) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    Stats q;
+    q.ms = __shfl_xor(s.ms, o, kWave); q.ss = __shfl_xor(s.ss, o, kWave);
+    q.mt = __shfl_xor(s.mt, o, kWave); q.st = __shfl_xor(s.st, o, kWave);
+    q.a = __shfl_xor(s.a, o, kWave); q.b = __shfl_xor(s.b, o, kWave);
+    stats_merge(s, q);
+  }
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) sh[w] = s;
+  __syncthreads();
+  Stats r = sh[0];
+#pragma unroll
+  for (int i = 1; i < NT / kWave; ++i) stats_merge(r, sh[i]);
+  return r;
+}
+
+struct DistillArgs {
+  int64_t T, V, ldz, ldt, ldd;
+  const uint8_t* mask;  // null: every row kept
+  float dloss;
+  const Counters* cnt;
+  float* row_ce;  // [T]
+  float* row_kl;  // [T]
+};
+
+// The row's loss terms from its totals (thread 0), and the logsumexps for the gradient.
+__device__ __forceinline__ void row_terms(const DistillArgs& a, int64_t row, const Stats& r,
+                                          float& lse_z, float& lse_t) {
+  lse_z = r.ms + __logf(r.ss);
+  lse_t = r.mt + __logf(r.st);
+  if (threadIdx.x == 0) {
+    const float ce = lse_z - r.a / r.st;   // -sum p log q
+    const float h = lse_t - r.b / r.st;    // -sum p log p
+    a.row_ce[row] = ce;
+    a.row_kl[row] = ce - h;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void masked_row(const DistillArgs& a, int64_t row, T* dz) {
+  if (dz != nullptr) {
+    T* dr = dz + row * a.ldd;
+    for (int64_t e = threadIdx.x; e < a.V; e += kRowThreads) dr[e] = from_f32<T>(0.f);
+  }
+  if (threadIdx.x == 0) { a.row_ce[row] = 0.f; a.row_kl[row] = 0.f; }
+}
+
+// On-chip rows: NS vectors per thread of the student in VGPRs; of the teacher, the first
+// NL in LDS and the rest in VGPRs.  Requires V % VEC == 0, aligned rows and strides,
+// V/VEC <= kRowThreads * NS.  dz may alias z (the whole row is loaded before any write).
+template <typename T, int NS, int NL>
+__global__ __launch_bounds__(kRowThreads) void soft_row(DistillArgs a, const T* z, const T* zt,
+                                                       T* dz) {
+  constexpr int VEC = Vec<T>::N;
+  constexpr int NR = NS - NL;  // teacher vectors per thread in VGPRs
+  __shared__ __attribute__((aligned(16))) u32x4 stage[NL > 0 ? NL * kRowThreads : 1];
+  __shared__ Stats sh[kRowThreads / kWave];
+  const int64_t row = blockIdx.x;
+  if (a.mask != nullptr && a.mask[row] == 0) {
+    masked_row<T>(a, row, dz);
+    return;
+  }
+  const int tid = threadIdx.x;
+  const int64_t nvec = a.V / VEC;
+  const T* zr = z + row * a.ldz;
+  const T* tr = zt + row * a.ldt;
+  if constexpr (NL > 0) {
+    // teacher vectors tid + i*1024 (i < NL) into LDS slot i*1024 + tid; the buffer covers
+    // the row only, so vectors past it read as zeros (and are never used)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)tr, (short)0, (int)(nvec * 16), kBufFlags);
+    const int wbase = tid & ~(kWave - 1);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const uint32_t off = (uint32_t)(i * kRowThreads + tid) * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_vptr)(stage + i * kRowThreads + wbase), 16,
+                                               off, 0, 0, 0);
+    }
+  }
+  Pack<T> zv[NS], tv[NR > 0 ? NR : 1];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int64_t v = tid + (int64_t)i * kRowThreads;
+    if (v < nvec) zv[i] = load_pack(zr + v * VEC);
+    else zv[i].raw = u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int64_t v = tid + (int64_t)(NL + i) * kRowThreads;
+    if (v < nvec) tv[i] = load_pack(tr + v * VEC);
+    else tv[i].raw = u32x4{0, 0, 0, 0};
+  }
+  // each lane reads back only the LDS slots its own DMA lane wrote: its own wait suffices
+  if constexpr (NL > 0) __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0) (lgkm, exp at max)
+  auto teacher = [&](int i) -> Pack<T> {
+    Pack<T> p;
+    if (i < NL) p.raw = stage[i * kRowThreads + tid];
+    else p = tv[i - NL];
+    return p;
+  };
+  Stats s;
+  stats_init(s);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int64_t v = tid + (int64_t)i * kRowThreads;
+    if (v < nvec) {
+      const Pack<T> tp = teacher(i);
+      float zf[VEC], tf[VEC];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) { zf[j] = to_f32(zv[i].v[j]); tf[j] = to_f32(tp.v[j]); }
+      stats_add<T, VEC>(s, zf, tf);
+    }
+  }
+  const Stats r = block_stats<kRowThreads>(s, sh);
+  float lse_z, lse_t;
+  row_terms(a, row, r, lse_z, lse_t);
+  if (dz == nullptr) return;
+  const float scale = a.dloss / (float)a.cnt->n_valid;
+  // keep both rows packed between the sweeps (re-widened below)
+#pragma unroll
+  for (int i = 0; i < NS; ++i) asm volatile("" : "+v"(zv[i].raw));
+#pragma unroll
+  for (int i = 0; i < NR; ++i) asm volatile("" : "+v"(tv[i].raw));
+  T* dr = dz + row * a.ldd;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int64_t v = tid + (int64_t)i * kRowThreads;
+    if (v < nvec) {
+      const Pack<T> tp = teacher(i);
+      Pack<T> o;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j)
+        o.v[j] = from_f32<T>(scale * (xent::ex<T>(to_f32(zv[i].v[j]) - lse_z) -
+                                      xent::ex<T>(to_f32(tp.v[j]) - lse_t)));
+      store_pack(dr + v * VEC, o);
+    }
+  }
+}
+
+// Any row length and alignment: the second sweep re-reads both rows.  dz may alias z
+// (each element is read by the thread that writes it; the merge barrier separates the
+// first sweep's reads from the writes).
+template <typename T, int VEC>
+__global__ __launch_bounds__(kRowThreads) void soft_stream(DistillArgs a, const T* z,
+                                                          const T* zt, T* dz) {
+  __shared__ Stats sh[kRowThreads / kWave];
+  const int64_t row = blockIdx.x;
+  if (a.mask != nullptr && a.mask[row] == 0) {
+    masked_row<T>(a, row, dz);
+    return;
+  }
+  const int64_t n = a.V / VEC;  // vectors (VEC = 1: elements)
+  const T* zr = z + row * a.ldz;
+  const T* tr = zt + row * a.ldt;
+  Stats s;
+  stats_init(s);
+  for (int64_t v = threadIdx.x; v < n; v += kRowThreads) {
+    float zf[VEC], tf[VEC];
+    if constexpr (VEC > 1) {
+      const Pack<T> zp = load_pack_cached(zr + v * VEC), tp = load_pack_cached(tr + v * VEC);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) { zf[j] = to_f32(zp.v[j]); tf[j] = to_f32(tp.v[j]); }
+    } else {
+      zf[0] = to_f32(zr[v]);
+      tf[0] = to_f32(tr[v]);
+    }
+    stats_add<T, VEC>(s, zf, tf);
+  }
+  const Stats r = block_stats<kRowThreads>(s, sh);
+  float lse_z, lse_t;
+  row_terms(a, row, r, lse_z, lse_t);
+  if (dz == nullptr) return;
+  const float scale = a.dloss / (float)a.cnt->n_valid;
+  T* dr = dz + row * a.ldd;
+  for (int64_t v = threadIdx.x; v < n; v += kRowThreads) {
+    if constexpr (VEC > 1) {
+      const Pack<T> zp = load_pack(zr + v * VEC), tp = load_pack(tr + v * VEC);
+      Pack<T> o;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j)
+        o.v[j] = from_f32<T>(scale * (xent::ex<T>(to_f32(zp.v[j]) - lse_z) -
+                                      xent::ex<T>(to_f32(tp.v[j]) - lse_t)));
+      store_pack(dr + v * VEC, o);
+    } else {
+      dr[v] = from_f32<T>(scale * (xent::ex<T>(to_f32(zr[v]) - lse_z) -
+                                   xent::ex<T>(to_f32(tr[v]) - lse_t)));
+    }
+  }
+}
+
+// N = rows the mask keeps (all T without a mask), into cnt.  One workgroup.
+__global__ __launch_bounds__(1024) void count_mask(int64_t T_, const uint8_t* __restrict__ mask,
+                                                   Counters* cnt) {
+  __shared__ long long sh[16];
+  long long c = 0;
+  for (int64_t t = threadIdx.x; t < T_; t += 1024) c += (mask == nullptr || mask[t] != 0) ? 1 : 0;
+  c = wave_sum_i64(c);
+  if ((threadIdx.x & (kWave - 1)) == 0) sh[threadIdx.x / kWave] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long n = 0;
+    for (int i = 0; i < 16; ++i) n += sh[i];
+    cnt->n_valid = n;
+    cnt->n_bad = 0;
+    cnt->pad = 0;
+  }
+}
+
+struct Ws {
+  size_t off_cnt, off_ce, off_kl, total;
+};
+Ws ws_layout(int64_t T_) {
+  Ws w;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
+  w.off_cnt = take(sizeof(Counters));
+  w.off_ce = take((size_t)(T_ > 0 ? T_ : 1) * 4);
+  w.off_kl = take((size_t)(T_ > 0 ? T_ : 1) * 4);
+  w.total = o;
+  return w;
+}
+
+template <typename T>
+int distill_impl(const DistillArgs& a0, const T* z, const T* zt, T* dz, float* loss, float* kl,
+                 int64_t* n_valid, char* ws, hipStream_t st) {
+  const Ws w = ws_layout(a0.T);
+  DistillArgs a = a0;
+  Counters* cnt = reinterpret_cast<Counters*>(ws + w.off_cnt);
+  a.cnt = cnt;
+  a.row_ce = reinterpret_cast<float*>(ws + w.off_ce);
+  a.row_kl = reinterpret_cast<float*>(ws + w.off_kl);
+  count_mask<<<1, 1024, 0, st>>>(a.T, a.mask, cnt);
+  if (a.T > 0) {
+    constexpr int VEC = Vec<T>::N;
+    const bool vec = a.V % VEC == 0 && a.ldz % VEC == 0 && a.ldt % VEC == 0 && aligned16(z) &&
+                     aligned16(zt) && (dz == nullptr || (a.ldd % VEC == 0 && aligned16(dz)));
+    const int64_t nvec = a.V / VEC;
+    const dim3 grid((unsigned)a.T), block(kRowThreads);
+    if (vec && nvec <= 16 * kRowThreads) {
+      const int64_t per = ceil_div(nvec, kRowThreads);
+      if (per <= 4) soft_row<T, 4, 0><<<grid, block, 0, st>>>(a, z, zt, dz);
+      else if (per <= 8) soft_row<T, 8, 0><<<grid, block, 0, st>>>(a, z, zt, dz);
+      else if (per <= 12) soft_row<T, 12, 5><<<grid, block, 0, st>>>(a, z, zt, dz);
+      else soft_row<T, 16, 9><<<grid, block, 0, st>>>(a, z, zt, dz);
+    } else if (vec) {
+      soft_stream<T, VEC><<<grid, block, 0, st>>>(a, z, zt, dz);
+    } else {
+      soft_stream<T, 1><<<grid, block, 0, st>>>(a, z, zt, dz);
+    }
+  }
+  xent::finalize<<<1, 1024, 0, st>>>(a.T, a.row_ce, a.row_kl, cnt, loss, kl, n_valid, nullptr);
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace fo
+
+using namespace fo;
+
+extern "C" size_t fo_distill_workspace(int64_t T, int64_t V) {
+  if (T < 0 || V < 1) return 0;
+  return ws_layout(T).total;
+}
+
+extern "C" int fo_distill_fwd_bwd(int dtype, int64_t T, int64_t V, const void* logits,
+                                  int64_t ldl, const void* teacher, int64_t ldt,
+                                  const uint8_t* row_mask, float dloss, void* dlogits,
+                                  int64_t ldd, float* loss, float* kl, int64_t* n_valid,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != FO_F32 && dtype != FO_BF16) return FO_ERR_DTYPE;
+  if (T < 0 || V < 1 || T > INT32_MAX) return FO_ERR_SHAPE;
+  if (ldl < V || ldt < V || (dlogits && ldd < V)) return FO_ERR_STRIDE;
+  if (!loss) return FO_ERR_NULL;
+  if (T > 0 && (!logits || !teacher)) return FO_ERR_NULL;
+  if (!ws || ws_bytes < fo_distill_workspace(T, V)) return FO_ERR_WORKSPACE;
+  DistillArgs a{};
+  a.T = T; a.V = V; a.ldz = ldl; a.ldt = ldt; a.ldd = ldd;
+  a.mask = row_mask;
+  a.dloss = dloss;
+  hipStream_t st = as_stream(stream);
+  if (dtype == FO_F32)
+    return distill_impl<float>(a, static_cast<const float*>(logits), static_cast<const float*>(teacher),
+                               static_cast<float*>(dlogits), loss, kl, n_valid, static_cast<char*>(ws), st);
+  return distill_impl<bf16>(a, static_cast<const bf16*>(logits), static_cast<const bf16*>(teacher),
+                            static_cast<bf16*>(dlogits), loss, kl, n_valid, static_cast<char*>(ws), st);
+}

@@ -35,6 +35,7 @@ TID = {
     "gate": 8, "up": 9, "dh": 10, "logits": 11, "targets": 12, "ignore": 13,
     "docs": 14, "hidden": 15, "weight": 16,
     "param": 17, "grad": 18, "exp_avg": 19, "exp_avg_sq": 20, "bias": 21,
+    "teacher": 22, "row_mask": 23,
 }
 
 
@@ -255,3 +256,16 @@ def adamw_inputs(sizes, seed: int):
         out["exp_avg_sqs"].append(
             torch.from_numpy(np.abs(normal_f32(key, TID["exp_avg_sq"], n, std=1e-3))))
     return out
+
+
+def distill_inputs(cfg: Config, mask_frac: float = 0.1, teacher_std: float = 2.0):
+    """Soft-target cross-entropy: the config's student logits (as for cross-entropy), a
+    teacher's logits N(0, teacher_std^2) of the same shape and dtype, and a row mask that
+    drops round(mask_frac * T) rows chosen by a seeded permutation."""
+    T, V, s = cfg.T, cfg.V, cfg.seed
+    z = _as_torch(normal_f32(s, TID["logits"], T * V, std=cfg.logit_std), cfg.dtype, (T, V))
+    zt = _as_torch(normal_f32(s, TID["teacher"], T * V, std=teacher_std), cfg.dtype, (T, V))
+    mask = np.ones(T, dtype=np.uint8)
+    drop = np.random.default_rng([s, TID["row_mask"]]).permutation(T)[:int(round(mask_frac * T))]
+    mask[drop] = 0
+    return dict(logits=z, teacher=zt, row_mask=torch.from_numpy(mask), dloss=1.0)

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared()
-    assert len(names) == 24, names
+    assert len(names) == 26, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in fo.SIGNATURES, f"binding lacks {n}"
@@ -143,6 +143,29 @@ def test_xent_validation(lib):
     assert f(BF16, 16, 0, P, 100, P, -100, 0.0, 1.0, P, 100, P, N, N, N, P, ws, N) == SHAPE
     assert f(BF16, 16, 100, N, 100, P, -100, 0.0, 1.0, P, 100, P, N, N, N, P, ws, N) == NULL
     assert f(3, 16, 100, P, 100, P, -100, 0.0, 1.0, P, 100, P, N, N, N, P, ws, N) == DTYPE
+
+
+def test_distill_validation(lib):
+    f = lib.fo_distill_fwd_bwd
+    ws = lib.fo_distill_workspace(16, 100)
+    assert ws >= 2 * 16 * 4
+    args = [BF16, 16, 100, P, 100, P, 100, N, 1.0, P, 100, P, N, N, P, ws, N]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return f(*a)
+
+    assert call(a0=4) == DTYPE
+    assert call(a2=0) == SHAPE
+    assert call(a4=99) == STRIDE                 # logits stride
+    assert call(a6=99) == STRIDE                 # teacher stride
+    assert call(a10=99) == STRIDE                # dlogits stride
+    assert call(a11=N) == NULL                   # loss
+    assert call(a5=N) == NULL                    # teacher
+    assert call(a15=ws - 1) == WS
+    assert call(a14=N) == WS
 
 
 def test_flce_validation(lib):

@@ -1,0 +1,101 @@
+"""GPU parity of fo_distill_fwd_bwd (soft-target cross-entropy) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from reduction_rmsnorm_fwd_amd import synth
+from tolerance import check, check_loss
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run(fo, z, zt, mask, dloss=1.0, want_grad=True):
+    o = fo.fo_distill_fwd_bwd(z.to(DEV), zt.to(DEV), None if mask is None else mask.to(DEV),
+                              dloss, want_grad=want_grad)
+    torch.cuda.synchronize()
+    return {k: (v.cpu() if v is not None else None) for k, v in o.items()}
+
+
+def compare(z, zt, mask, o, dt, dloss=1.0):
+    r = oracle.distill_fwd_bwd(z, zt, mask, dloss)
+    assert o["n_valid"].item() == r["n_valid"]
+    check_loss(o["loss"].item(), r["loss"])
+    check_loss(o["kl"].item(), r["kl"], "kl", rel=5e-4)
+    if o["dlogits"] is not None:
+        check(o["dlogits"], r["dlogits"], dt, "dlogits")
+        if mask is not None:
+            dropped = (mask == 0).nonzero().flatten()
+            assert torch.all(o["dlogits"][dropped].float() == 0)
+
+
+def cfg_of(dtype, T, V, seed=31, logit_std=3.0):
+    return synth.Config(0, "kd", dtype, T=T, d=8, n_q=1, n_kv=1, head_dim=2, F=1, V=V,
+                        eps=1e-5, theta=1e4, logit_std=logit_std, z_loss=0, ignore_frac=0,
+                        packed=False, doc_lengths=(T,), seed=seed)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [100, 1000, 4096, 49152, 128256, 151936])
+def test_vocab_paths(gpu, dtype, V):
+    # V 100 (unaligned: element path), 1000/4096 (4 vectors), 49152 (8), 128256 (16 with
+    # the teacher partly in LDS), 151936 (beyond on-chip rows: streaming)
+    T = 6 if V > 50000 else 23
+    i = synth.distill_inputs(cfg_of(dtype, T, V))
+    o = run(gpu, i["logits"], i["teacher"], i["row_mask"])
+    compare(i["logits"], i["teacher"], i["row_mask"], o, dtype)
+
+
+def test_no_mask_forward_only_and_dloss(gpu):
+    i = synth.distill_inputs(cfg_of("bf16", 40, 32000, seed=5))
+    o = run(gpu, i["logits"], i["teacher"], None, dloss=0.5)
+    compare(i["logits"], i["teacher"], None, o, "bf16", dloss=0.5)
+    f = run(gpu, i["logits"], i["teacher"], None, want_grad=False)
+    assert f["dlogits"] is None and f["loss"].item() == o["loss"].item()
+
+
+def test_all_masked(gpu):
+    i = synth.distill_inputs(cfg_of("bf16", 12, 5000, seed=6), mask_frac=1.0)
+    o = run(gpu, i["logits"], i["teacher"], i["row_mask"])
+    assert o["loss"].item() == 0.0 and o["kl"].item() == 0.0 and o["n_valid"].item() == 0
+    assert torch.all(o["dlogits"].float() == 0)
+
+
+def test_teacher_equals_student(gpu):
+    i = synth.distill_inputs(cfg_of("f32", 9, 8192, seed=7))
+    o = run(gpu, i["logits"], i["logits"].clone(), None)
+    assert abs(o["kl"].item()) < 1e-5
+    assert o["dlogits"].abs().max().item() < 1e-9
+
+
+def test_in_place_gradient(gpu):
+    i = synth.distill_inputs(cfg_of("bf16", 16, 128256, seed=8))
+    zg, tg, mg = i["logits"].to(DEV), i["teacher"].to(DEV), i["row_mask"].to(DEV)
+    ref = gpu.fo_distill_fwd_bwd(zg, tg, mg)
+    z2 = zg.clone()
+    o = gpu.fo_distill_fwd_bwd(z2, tg, mg, dlogits=z2)
+    torch.cuda.synchronize()
+    assert torch.equal(z2, ref["dlogits"]) and o["loss"].item() == ref["loss"].item()
+
+
+def test_full_size_sampled(gpu):
+    """T 8192 x V 128256 bf16 (the Llama-3-8B lm-head logits) in one call: gradient rows
+    sampled against the oracle, the loss against a row-block oracle sum."""
+    cfg = synth.scaled(synth.CONFIGS[3], 8192)
+    i = synth.distill_inputs(cfg)
+    z, zt, mask = i["logits"], i["teacher"], i["row_mask"]
+    o = run(gpu, z, zt, mask)
+    n = int((mask != 0).sum())
+    assert o["n_valid"].item() == n
+    rows = np.unique(np.concatenate([[0, cfg.T - 1], np.random.default_rng(9).integers(0, cfg.T, 12)]))
+    keep = [r for r in rows if mask[r] != 0]
+    rr = oracle.distill_fwd_bwd(z[keep], zt[keep], None, dloss=len(keep) / n)
+    check(o["dlogits"][keep], rr["dlogits"], "bf16", "dlogits rows")
+    ce = kl = 0.0
+    for r0 in range(0, cfg.T, 1024):
+        b = oracle.distill_fwd_bwd(z[r0:r0 + 1024], zt[r0:r0 + 1024], mask[r0:r0 + 1024])
+        ce += b["loss"] * b["n_valid"]
+        kl += b["kl"] * b["n_valid"]
+    check_loss(o["loss"].item(), ce / n)
+    check_loss(o["kl"].item(), kl / n, "kl", rel=5e-4)
