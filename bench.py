@@ -72,7 +72,8 @@ def parse():
                    help="skip the copy / MFMA ceiling probes and the unaligned-shape lines")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-next", action="store_true",
-                   help="skip the rows after the step (AdamW, LayerNorm, GeLU MLP activations)")
+                   help="skip the rows after the step (AdamW, LayerNorm, GeLU MLP "
+                        "activations, soft-target cross-entropy)")
     p.add_argument("--no-isolated", action="store_true")
     p.add_argument("--only", default="", help="comma list of ops to run (profiling)")
     p.add_argument("--calib-copy", action="store_true",
@@ -363,6 +364,43 @@ def activation_lines(fo, synth, torch, stream, med, reps, copy_gbs):
     return lines
 
 
+def distill_line(fo, synth, torch, stream, med, reps, copy_gbs):
+    """Soft-target cross-entropy (a row after the step's ops, reported apart from the
+    step) on the Llama-3-8B lm-head logits shape (T 8192, V 128256, bf16, 10% of rows
+    masked), isolated with caches flushed.  Bytes 3TVb (student and teacher read,
+    dlogits written) + T (mask)."""
+    cfg = synth.scaled(synth.CONFIGS[3], 8192)
+    i = synth.distill_inputs(cfg)
+    z, zt, mask = (i[k].to("cuda") for k in ("logits", "teacher", "row_mask"))
+    T, V = z.shape
+    dz = torch.empty_like(z)
+    ws = torch.empty(fo.fo_distill_workspace(T, V), dtype=torch.uint8, device="cuda")
+    out = None
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    ts = []
+    for r in range(reps + 2):
+        scratch.fill_(1.0)
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        out = fo.fo_distill_fwd_bwd(z, zt, mask, dlogits=dz, ws=ws, out=out)
+        e.record(stream)
+        e.synchronize()
+        if r >= 2:
+            ts.append(a.elapsed_time(e))
+    del scratch
+    ms = med(ts)
+    byt = 3 * T * V * z.element_size() + T
+    ent = {"workload": f"T {T}, V {V}, bf16, 10% of rows masked (Llama-3-8B lm-head logits shape)",
+           "ms_isolated_median": round(ms, 4), "algorithmic_MB": round(byt / 1e6, 1),
+           "GBps": round(byt / (ms * 1e-3) / 1e9, 1),
+           "frac_hbm_peak": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "tokens_per_s": round(T / (ms * 1e-3), 1)}
+    if copy_gbs:
+        ent["frac_measured_copy"] = round(ent["GBps"] / copy_gbs, 4)
+    print(f"# distill: {ms:.3f} ms", file=sys.stderr, flush=True)
+    return ent
+
+
 def unaligned_lines(fo, synth, torch, stream, med):
     """The scalar (unaligned) paths at the Llama-3-8B token count, reported apart from
     the aligned per-op lines: RMSNorm with d = 4097 and SwiGLU with F = 14337 (rows not
@@ -494,6 +532,7 @@ def gpu_bench(args):
         next_ops = {"adamw_step": adamw_line(fo, synth, torch, stream, med, 20, cg)}
         next_ops.update(layernorm_lines(fo, synth, torch, stream, med, args.iso_reps, cg))
         next_ops.update(activation_lines(fo, synth, torch, stream, med, args.iso_reps, cg))
+        next_ops["distill_fwd_bwd"] = distill_line(fo, synth, torch, stream, med, 10, cg)
     traffic = measured_traffic()
     per_op = {}
     for i, (name, _, work, bound) in enumerate(wl.ops):
