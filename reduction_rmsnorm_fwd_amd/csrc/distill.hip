@@ -23,6 +23,7 @@ using xent::Counters;
 
 constexpr int kRowThreads = 1024;
 typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef unsigned int v4u32_t __attribute__((ext_vector_type(4)));
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
 
 // Per-thread (then per-row) state of the sweep: student (ms, ss), teacher (mt, st) and
@@ -122,7 +123,12 @@ __device__ __forceinline__ void masked_row(const DistillArgs& a, int64_t row, T*
 
 // On-chip rows: NS vectors per thread of the student in VGPRs; of the teacher, the first
 // NL in LDS and the rest in VGPRs.  Requires V % VEC == 0, aligned rows and strides,
-// V/VEC <= kRowThreads * NS.  dz may alias z (the whole row is loaded before any write).
+// V/VEC <= kRowThreads * NS.  Persistent: workgroup b walks rows b, b + gridDim.x, ...;
+// the loads of a row are issued as soon as the previous row's gradient stores are (and,
+// for its LDS part, once every wave has finished reading the previous row there), so a
+// CU streams the next row in while the current one drains.  dz may alias z (a row is
+// wholly loaded before any of its writes, and a row's writes come before the next
+// row's loads only in program order of the same threads that load it).
 template <typename T, int NS, int NL>
 __global__ __launch_bounds__(kRowThreads) void soft_row(DistillArgs a, const T* z, const T* zt,
                                                        T* dz) {
@@ -130,85 +136,97 @@ __global__ __launch_bounds__(kRowThreads) void soft_row(DistillArgs a, const T* 
   constexpr int NR = NS - NL;  // teacher vectors per thread in VGPRs
   __shared__ __attribute__((aligned(16))) u32x4 stage[NL > 0 ? NL * kRowThreads : 1];
   __shared__ Stats sh[kRowThreads / kWave];
-  const int64_t row = blockIdx.x;
-  if (a.mask != nullptr && a.mask[row] == 0) {
-    masked_row<T>(a, row, dz);
-    return;
-  }
   const int tid = threadIdx.x;
   const int64_t nvec = a.V / VEC;
-  const T* zr = z + row * a.ldz;
-  const T* tr = zt + row * a.ldt;
-  if constexpr (NL > 0) {
-    // teacher vectors tid + i*1024 (i < NL) into LDS slot i*1024 + tid; the buffer covers
-    // the row only, so vectors past it read as zeros (and are never used)
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)tr, (short)0, (int)(nvec * 16), kBufFlags);
-    const int wbase = tid & ~(kWave - 1);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const uint32_t off = (uint32_t)(i * kRowThreads + tid) * 16u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_vptr)(stage + i * kRowThreads + wbase), 16,
-                                               off, 0, 0, 0);
-    }
-  }
   Pack<T> zv[NS], tv[NR > 0 ? NR : 1];
+  auto kept = [&](int64_t row) { return row < a.T && (a.mask == nullptr || a.mask[row] != 0); };
+  // issue every load of `row` (nothing for a dropped or missing row).  Buffer accesses
+  // over the row: one 32-bit lane offset, the vector index in the scalar offset, and
+  // vectors past the row read as zeros (no per-vector address registers or branches).
+  const uint32_t lane_off = (uint32_t)tid * 16u;
+  auto row_rsrc = [&](const T* base, int64_t row, int64_t ld) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row * ld), (short)0,
+                                             (int)(nvec * 16), kBufFlags);
+  };
+  auto issue = [&](int64_t row) {
+    if (!kept(row)) return;
+    const __amdgpu_buffer_rsrc_t rz = row_rsrc(z, row, a.ldz);
+    const __amdgpu_buffer_rsrc_t rt = row_rsrc(zt, row, a.ldt);
+    if constexpr (NL > 0) {
+      // teacher vectors tid + i*1024 (i < NL) into LDS slot i*1024 + tid
+      const int wbase = tid & ~(kWave - 1);
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int64_t v = tid + (int64_t)i * kRowThreads;
-    if (v < nvec) zv[i] = load_pack(zr + v * VEC);
-    else zv[i].raw = u32x4{0, 0, 0, 0};
-  }
+      for (int i = 0; i < NL; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (lds_vptr)(stage + i * kRowThreads + wbase),
+                                                 16, lane_off, i * kRowThreads * 16, 0, 0);
+    }
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int64_t v = tid + (int64_t)(NL + i) * kRowThreads;
-    if (v < nvec) tv[i] = load_pack(tr + v * VEC);
-    else tv[i].raw = u32x4{0, 0, 0, 0};
-  }
-  // each lane reads back only the LDS slots its own DMA lane wrote: its own wait suffices
-  if constexpr (NL > 0) __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0) (lgkm, exp at max)
+    for (int i = 0; i < NS; ++i)
+      zv[i].raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rz, lane_off, i * kRowThreads * 16, 0));
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      tv[i].raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rt, lane_off, (NL + i) * kRowThreads * 16, 0));
+  };
   auto teacher = [&](int i) -> Pack<T> {
     Pack<T> p;
     if (i < NL) p.raw = stage[i * kRowThreads + tid];
     else p = tv[i - NL];
     return p;
   };
-  Stats s;
-  stats_init(s);
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int64_t v = tid + (int64_t)i * kRowThreads;
-    if (v < nvec) {
-      const Pack<T> tp = teacher(i);
-      float zf[VEC], tf[VEC];
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) { zf[j] = to_f32(zv[i].v[j]); tf[j] = to_f32(tp.v[j]); }
-      stats_add<T, VEC>(s, zf, tf);
+  issue(blockIdx.x);
+  for (int64_t row = blockIdx.x; row < a.T; row += gridDim.x) {
+    const int64_t next = row + gridDim.x;
+    if (!kept(row)) {
+      masked_row<T>(a, row, dz);
+      issue(next);
+      continue;
     }
-  }
-  const Stats r = block_stats<kRowThreads>(s, sh);
-  float lse_z, lse_t;
-  row_terms(a, row, r, lse_z, lse_t);
-  if (dz == nullptr) return;
-  const float scale = a.dloss / (float)a.cnt->n_valid;
-  // keep both rows packed between the sweeps (re-widened below)
+    // each lane reads back only the LDS slots its own DMA lane wrote: its own wait
+    // suffices (it also covers the previous row's stores, which drain meanwhile)
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0) (lgkm, exp at max)
+    Stats s;
+    stats_init(s);
 #pragma unroll
-  for (int i = 0; i < NS; ++i) asm volatile("" : "+v"(zv[i].raw));
+    for (int i = 0; i < NS; ++i) {
+      const int64_t v = tid + (int64_t)i * kRowThreads;
+      if (v < nvec) {
+        const Pack<T> tp = teacher(i);
+        float zf[VEC], tf[VEC];
 #pragma unroll
-  for (int i = 0; i < NR; ++i) asm volatile("" : "+v"(tv[i].raw));
-  T* dr = dz + row * a.ldd;
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int64_t v = tid + (int64_t)i * kRowThreads;
-    if (v < nvec) {
-      const Pack<T> tp = teacher(i);
-      Pack<T> o;
-#pragma unroll
-      for (int j = 0; j < VEC; ++j)
-        o.v[j] = from_f32<T>(scale * (xent::ex<T>(to_f32(zv[i].v[j]) - lse_z) -
-                                      xent::ex<T>(to_f32(tp.v[j]) - lse_t)));
-      store_pack(dr + v * VEC, o);
+        for (int j = 0; j < VEC; ++j) { zf[j] = to_f32(zv[i].v[j]); tf[j] = to_f32(tp.v[j]); }
+        stats_add<T, VEC>(s, zf, tf);
+      }
     }
+    const Stats r = block_stats<kRowThreads>(s, sh);
+    float lse_z, lse_t;
+    row_terms(a, row, r, lse_z, lse_t);
+    if (dz != nullptr) {
+      const float scale = a.dloss / (float)a.cnt->n_valid;
+      // keep both rows packed between the sweeps (re-widened below)
+#pragma unroll
+      for (int i = 0; i < NS; ++i) asm volatile("" : "+v"(zv[i].raw));
+#pragma unroll
+      for (int i = 0; i < NR; ++i) asm volatile("" : "+v"(tv[i].raw));
+      // stores past the row fall outside the buffer and are dropped
+      const __amdgpu_buffer_rsrc_t rd = row_rsrc(dz, row, a.ldd);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const Pack<T> tp = teacher(i);
+        Pack<T> o;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+          o.v[j] = from_f32<T>(scale * (xent::ex<T>(to_f32(zv[i].v[j]) - lse_z) -
+                                        xent::ex<T>(to_f32(tp.v[j]) - lse_t)));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, o.raw), rd, lane_off,
+                                               i * kRowThreads * 16, 0);
+      }
+    }
+    // every wave is done with this row's LDS part (and with sh) before the next row's
+    // copy lands there
+    __syncthreads();
+    issue(next);
   }
 }
 
@@ -298,6 +316,11 @@ Ws ws_layout(int64_t T_) {
 template <typename T>
 int distill_impl(const DistillArgs& a0, const T* z, const T* zt, T* dz, float* loss, float* kl,
                  int64_t* n_valid, char* ws, hipStream_t st) {
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n_cu < 1)
+    return FO_ERR_HIP;
   const Ws w = ws_layout(a0.T);
   DistillArgs a = a0;
   Counters* cnt = reinterpret_cast<Counters*>(ws + w.off_cnt);
@@ -312,11 +335,13 @@ int distill_impl(const DistillArgs& a0, const T* z, const T* zt, T* dz, float* l
     const int64_t nvec = a.V / VEC;
     const dim3 grid((unsigned)a.T), block(kRowThreads);
     if (vec && nvec <= 16 * kRowThreads) {
+      // persistent: one workgroup per CU (a row pair fills a CU's registers)
+      const dim3 pgrid((unsigned)(a.T < n_cu ? a.T : n_cu));
       const int64_t per = ceil_div(nvec, kRowThreads);
-      if (per <= 4) soft_row<T, 4, 0><<<grid, block, 0, st>>>(a, z, zt, dz);
-      else if (per <= 8) soft_row<T, 8, 0><<<grid, block, 0, st>>>(a, z, zt, dz);
-      else if (per <= 12) soft_row<T, 12, 5><<<grid, block, 0, st>>>(a, z, zt, dz);
-      else soft_row<T, 16, 9><<<grid, block, 0, st>>>(a, z, zt, dz);
+      if (per <= 4) soft_row<T, 4, 0><<<pgrid, block, 0, st>>>(a, z, zt, dz);
+      else if (per <= 8) soft_row<T, 8, 0><<<pgrid, block, 0, st>>>(a, z, zt, dz);
+      else if (per <= 12) soft_row<T, 12, 5><<<pgrid, block, 0, st>>>(a, z, zt, dz);
+      else soft_row<T, 16, 9><<<pgrid, block, 0, st>>>(a, z, zt, dz);
     } else if (vec) {
       soft_stream<T, VEC><<<grid, block, 0, st>>>(a, z, zt, dz);
     } else {
