@@ -14,8 +14,12 @@
 // across all the rows its workgroup visits.  The waves of a workgroup are folded
 // through LDS in a fixed order into one fp32 partial row per workgroup (at most 512
 // workgroups, so the partials stay a few MB), and a second small kernel sums the
-// partial rows in a fixed order.  Any other shape takes a workgroup-per-row path that
-// reads the row twice (the second read from L2).
+// partial rows in a fixed order.  Rows that start off a 16-byte boundary or whose
+// length is not a multiple of the vector take the same kernels (template flag UA):
+// their full vectors are still moved as 16-byte accesses at element-aligned addresses,
+// their last partial vector element by element.  Rows too long for the registers take a
+// workgroup-per-row path that reads the row twice (the second read from L2).
+#include <initializer_list>
 #include <type_traits>
 
 #include "fo_common.hpp"
@@ -28,10 +32,39 @@ constexpr int kBwdWaves = 8;     // waves per workgroup, backward
 constexpr int kMaxPartials = 512;  // dw partial rows (workgroups of the backward)
 constexpr int kGenericThreads = 256;
 
+// ------------------------------------------------------- vectors of a row, any alignment
+// UA = false: the row (or w, b) starts on 16 bytes and d is a multiple of the vector.
+// UA = true: it starts on any element and d is any length.  The full vectors of the row
+// are still moved as 16-byte accesses at their element-aligned addresses (gfx950 runs
+// global memory in unaligned mode: such loads cost nothing extra, stores ~12%, measured
+// against aligned ones), so every byte read or written is one of the row's; only the
+// last, partial vector goes element by element, with zeros past the row.
+template <typename T, bool UA, bool NT>
+__device__ __forceinline__ Pack<T> ld_vec(const T* p, int v, int d) {
+  constexpr int VEC = Vec<T>::N;
+  if (!UA || (v + 1) * VEC <= d) return NT ? load_pack(p + (int64_t)v * VEC) : load_pack_cached(p + (int64_t)v * VEC);
+  Pack<T> r;
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) r.v[j] = v * VEC + j < d ? p[(int64_t)v * VEC + j] : from_f32<T>(0.f);
+  return r;
+}
+template <typename T, bool UA>
+__device__ __forceinline__ void st_vec(T* p, int v, int d, const Pack<T>& o) {
+  constexpr int VEC = Vec<T>::N;
+  if (!UA || (v + 1) * VEC <= d) {
+    store_pack(p + (int64_t)v * VEC, o);
+  } else {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+      if (v * VEC + j < d) p[(int64_t)v * VEC + j] = o.v[j];
+  }
+}
+
 // ----------------------------------------------------------------- forward, fast
 // LN: LayerNorm (mean subtracted before the variance, bias added); the row is still
 // read once: mean and centred variance are two sweeps over the registers.
-template <typename T, int NV, bool LN>
+// nvec: vectors per row, the last one partial when UA and d is not a multiple of VEC.
+template <typename T, int NV, bool LN, bool UA>
 __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
     int64_t T_, int nvec, int d, const T* __restrict__ x, int64_t ldx,
     const T* __restrict__ w, const T* __restrict__ b, float eps, T* y, int64_t ldy,
@@ -45,7 +78,7 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int v = lane + i * kWave;
-    if (v < nvec) xv[i] = load_pack(xr + (int64_t)v * VEC);
+    if (v < nvec) xv[i] = ld_vec<T, UA, true>(xr, v, d);
     else xv[i].raw = u32x4{0, 0, 0, 0};
   }
   float mu = 0.f;
@@ -67,7 +100,8 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
     for (int j = 0; j < VEC; ++j) {
       if constexpr (LN) {
         const float f = to_f32(xv[i].v[j]) - mu;
-        if (lane + i * kWave < nvec) ss = fmaf(f, f, ss);  // padding lanes hold 0, not mu
+        // padding holds 0, not mu
+        if ((lane + i * kWave) * VEC + j < d) ss = fmaf(f, f, ss);
       } else {
         const float f = to_f32(xv[i].v[j]);
         ss = fmaf(f, f, ss);
@@ -84,10 +118,10 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
   for (int i = 0; i < NV; ++i) {
     const int v = lane + i * kWave;
     if (v < nvec) {
-      const Pack<T> wv = load_pack_cached(w + (int64_t)v * VEC);
+      const Pack<T> wv = ld_vec<T, UA, false>(w, v, d);
       Pack<T> o;
       if constexpr (LN) {
-        const Pack<T> bv = load_pack_cached(b + (int64_t)v * VEC);
+        const Pack<T> bv = ld_vec<T, UA, false>(b, v, d);
 #pragma unroll
         for (int j = 0; j < VEC; ++j)
           o.v[j] = from_f32<T>(fmaf((to_f32(xv[i].v[j]) - mu) * r, to_f32(wv.v[j]), to_f32(bv.v[j])));
@@ -95,7 +129,7 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
 #pragma unroll
         for (int j = 0; j < VEC; ++j) o.v[j] = from_f32<T>(to_f32(xv[i].v[j]) * r * to_f32(wv.v[j]));
       }
-      store_pack(yr + (int64_t)v * VEC, o);
+      st_vec<T, UA>(yr, v, d, o);
     }
   }
   if (lane == 0) {
@@ -169,7 +203,7 @@ __global__ __launch_bounds__(kGenericThreads) void rmsnorm_fwd_block(
 // LN (LayerNorm, mean and rstd saved by the forward): with g = w*dy and xc = x - mean,
 //   dx = r g - r mean_j(g) - r^3 xc mean_j(g xc),  dw += dy xc r,  db += dy,
 // the db partials folded beside the dw partials (partial row of 2d floats).
-template <typename T, int NV, int RW, bool LN>
+template <typename T, int NV, int RW, bool LN, bool UA>
 __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
     int64_t T_, int nvec, int d, const T* dy, int64_t lddy, const T* x, int64_t ldx,
     const T* __restrict__ w, const float* __restrict__ mean, const float* __restrict__ rstd,
@@ -188,7 +222,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int v = vbase + i * RW * kWave;
-    if (v < nvec) wv[i] = load_pack_cached(w + (int64_t)v * VEC);
+    if (v < nvec) wv[i] = ld_vec<T, UA, false>(w, v, d);
     else wv[i].raw = u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < VEC; ++j) acc[i][j] = 0.f;
@@ -214,8 +248,8 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
     for (int i = 0; i < NV; ++i) {
       const int v = vbase + i * RW * kWave;
       if (live && v < nvec) {
-        g[i] = load_pack(dy + row * lddy + (int64_t)v * VEC);
-        xx[i] = load_pack(x + row * ldx + (int64_t)v * VEC);
+        g[i] = ld_vec<T, UA, true>(dy + row * lddy, v, d);
+        xx[i] = ld_vec<T, UA, true>(x + row * ldx, v, d);
       } else {
         g[i].raw = u32x4{0, 0, 0, 0};
         xx[i].raw = u32x4{0, 0, 0, 0};
@@ -288,7 +322,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
               acc[i][j] = fmaf(gf * xf, r, acc[i][j]);
             }
           }
-          store_pack(dxr + (int64_t)v * VEC, o);
+          st_vec<T, UA>(dxr, v, d, o);
         }
       }
     }
@@ -310,6 +344,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
         if (v < nvec) {
 #pragma unroll
           for (int j = 0; j < VEC; ++j) {
+            if (UA && v * VEC + j >= d) continue;  // past the row (fold holds d columns)
             float* p = &fold[v * VEC + j];
             *p = (s == 0) ? acc[i][j] : (*p + acc[i][j]);
             if constexpr (LN) {
@@ -473,9 +508,17 @@ bool vector_ok(int64_t d, const void* a, int64_t lda, const void* b, int64_t ldb
          d <= 16 * kWave * VEC;
 }
 
+// Rows of any alignment and length that still fit the registers of the wave kernels
+// (UA = true there): element-aligned pointers, at most 16 vectors per lane.
 template <typename T>
-int nv_for(int64_t d) {
-  const int64_t nvec = d / Vec<T>::N;
+bool unaligned_ok(int64_t d, std::initializer_list<const void*> ptrs) {
+  bool ok = ceil_div(d, (int64_t)Vec<T>::N) <= 16 * kWave;
+  for (const void* p : ptrs) ok = ok && reinterpret_cast<uintptr_t>(p) % sizeof(T) == 0;
+  return ok;
+}
+
+// vectors per lane of the forward wave kernel for rows of nvec vectors
+inline int nv_for(int64_t nvec) {
   const int64_t per = ceil_div(nvec, kWave);
   return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
 }
@@ -487,20 +530,26 @@ int fwd_impl(int64_t T_, int64_t d, const void* x, int64_t ldx, const void* w, c
   const T* wp = static_cast<const T*>(w);
   const T* bp = static_cast<const T*>(b);
   T* yp = static_cast<T*>(y);
-  if (vector_ok<T>(d, x, ldx, y, ldy, x, ldx, w) && (!LN || aligned16(b))) {
-    const int nvec = (int)(d / Vec<T>::N);
+  const bool aligned = vector_ok<T>(d, x, ldx, y, ldy, x, ldx, w) && (!LN || aligned16(b));
+  if (aligned || unaligned_ok<T>(d, {x, y, w, LN ? b : x})) {
+    const int nvec = (int)ceil_div(d, (int64_t)Vec<T>::N);
     const dim3 grid((unsigned)ceil_div(T_, kFwdWaves));
     const dim3 block(kFwdWaves * kWave);
+    auto go = [&](auto ua) {
+      constexpr bool UA = decltype(ua)::value;
 #define FO_FWD(NV_) \
-  rmsnorm_fwd_wave<T, NV_, LN><<<grid, block, 0, st>>>(T_, nvec, (int)d, xp, ldx, wp, bp, eps, yp, ldy, mean, rstd)
-    switch (nv_for<T>(d)) {
-      case 1: FO_FWD(1); break;
-      case 2: FO_FWD(2); break;
-      case 4: FO_FWD(4); break;
-      case 8: FO_FWD(8); break;
-      default: FO_FWD(16); break;
-    }
+  rmsnorm_fwd_wave<T, NV_, LN, UA><<<grid, block, 0, st>>>(T_, nvec, (int)d, xp, ldx, wp, bp, eps, yp, ldy, mean, rstd)
+      switch (nv_for(nvec)) {
+        case 1: FO_FWD(1); break;
+        case 2: FO_FWD(2); break;
+        case 4: FO_FWD(4); break;
+        case 8: FO_FWD(8); break;
+        default: FO_FWD(16); break;
+      }
 #undef FO_FWD
+    };
+    if (aligned) go(std::false_type{});
+    else go(std::true_type{});
   } else {
     rmsnorm_fwd_block<T, LN><<<dim3((unsigned)T_), dim3(kGenericThreads), 0, st>>>(
         T_, d, xp, ldx, wp, bp, eps, yp, ldy, mean, rstd);
@@ -532,11 +581,11 @@ BwdPlan bwd_plan(int64_t T_, int nvec) {
   return p;
 }
 
-template <typename T, int NV, int RW, bool LN>
+template <typename T, int NV, int RW, bool LN, bool UA>
 void launch_bwd(const BwdPlan& p, int64_t T_, int nvec, int d, const T* dy, int64_t lddy,
                 const T* x, int64_t ldx, const T* w, const float* mean, const float* rstd,
                 float eps, T* dx, int64_t lddx, float* partial, hipStream_t st) {
-  rmsnorm_bwd_wave<T, NV, RW, LN>
+  rmsnorm_bwd_wave<T, NV, RW, LN, UA>
       <<<dim3((unsigned)p.groups), dim3(kBwdWaves * kWave), (size_t)(LN ? 2 : 1) * d * sizeof(float),
          st>>>(T_, nvec, d, dy, lddy, x, ldx, w, mean, rstd, eps, dx, lddx, partial);
 }
@@ -554,26 +603,31 @@ int bwd_impl(int64_t T_, int64_t d, const void* dy, int64_t lddy, const void* x,
   float* partial = static_cast<float*>(ws);
   constexpr int64_t kCols = LN ? 2 : 1;  // partial row: dw (and db) columns
   int64_t G;
-  if (vector_ok<T>(d, dy, lddy, x, ldx, dx, lddx, w)) {
-    const int nvec = (int)(d / Vec<T>::N);
+  const bool aligned = vector_ok<T>(d, dy, lddy, x, ldx, dx, lddx, w);
+  if (aligned || unaligned_ok<T>(d, {dy, x, dx, w})) {
+    const int nvec = (int)ceil_div(d, (int64_t)Vec<T>::N);
     const BwdPlan p = bwd_plan<T>(T_, nvec);
     G = p.groups;
     constexpr int kMaxNV = 16 / Vec<T>::N;
-    auto go = [&](auto nv_c, auto rw_c) {
-      launch_bwd<T, decltype(nv_c)::value, decltype(rw_c)::value, LN>(
+    auto go = [&](auto nv_c, auto rw_c, auto ua) {
+      launch_bwd<T, decltype(nv_c)::value, decltype(rw_c)::value, LN, decltype(ua)::value>(
           p, T_, nvec, (int)d, dyp, lddy, xp, ldx, wp, mean, rstd, eps, dxp, lddx, partial, st);
     };
-    auto go_rw = [&](auto rw_c) {
-      if (p.nv == 1) go(std::integral_constant<int, 1>{}, rw_c);
-      else if (p.nv == 2 || kMaxNV == 2) go(std::integral_constant<int, 2>{}, rw_c);
-      else go(std::integral_constant<int, kMaxNV>{}, rw_c);
+    auto go_nv = [&](auto rw_c, auto ua) {
+      if (p.nv == 1) go(std::integral_constant<int, 1>{}, rw_c, ua);
+      else if (p.nv == 2 || kMaxNV == 2) go(std::integral_constant<int, 2>{}, rw_c, ua);
+      else go(std::integral_constant<int, kMaxNV>{}, rw_c, ua);
     };
-    switch (p.rw) {
-      case 1: go_rw(std::integral_constant<int, 1>{}); break;
-      case 2: go_rw(std::integral_constant<int, 2>{}); break;
-      case 4: go_rw(std::integral_constant<int, 4>{}); break;
-      default: go_rw(std::integral_constant<int, 8>{}); break;
-    }
+    auto go_rw = [&](auto ua) {
+      switch (p.rw) {
+        case 1: go_nv(std::integral_constant<int, 1>{}, ua); break;
+        case 2: go_nv(std::integral_constant<int, 2>{}, ua); break;
+        case 4: go_nv(std::integral_constant<int, 4>{}, ua); break;
+        default: go_nv(std::integral_constant<int, 8>{}, ua); break;
+      }
+    };
+    if (aligned) go_rw(std::false_type{});
+    else go_rw(std::true_type{});
   } else {
     // RMS: r[t] after the partials in the workspace; LN uses the saved rstd
     G = bwd_groups(T_);
