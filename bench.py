@@ -402,9 +402,9 @@ def distill_line(fo, synth, torch, stream, med, reps, copy_gbs):
 
 
 def unaligned_lines(fo, synth, torch, stream, med):
-    """The scalar (unaligned) paths at the Llama-3-8B token count, reported apart from
-    the aligned per-op lines: RMSNorm with d = 4097 and SwiGLU with F = 14337 (rows not
-    a multiple of the 16-byte vector)."""
+    """Rows that are not a multiple of the 16-byte vector, at the Llama-3-8B token count,
+    reported apart from the aligned per-op lines: RMSNorm with d = 4097, SwiGLU with
+    F = 14337 and cross-entropy over a 50257-entry vocabulary (GPT-2's)."""
     import dataclasses
     c3 = synth.CONFIGS[3]
     cu = dataclasses.replace(c3, d=4097, F=14337)
@@ -421,12 +421,23 @@ def unaligned_lines(fo, synth, torch, stream, med):
     h = torch.empty_like(g)
     F = g.shape[1]
     b = 2
+    cv = dataclasses.replace(c3, V=50257)
+    xe = synth.xent_inputs(cv)
+    lg, tg = xe["logits"].to("cuda"), xe["targets"].to("cuda")
+    dlg = torch.empty_like(lg)
+    V = lg.shape[1]
+    n_ign = int((xe["targets"] == synth.IGNORE_INDEX).sum())
+    xws = torch.empty(fo.fo_xent_workspace(T, V), dtype=torch.uint8, device="cuda")
+    xo = fo._scalars("cuda")
     cases = [
         ("rmsnorm_fwd_d4097", lambda: fo.fo_rmsnorm_fwd(x, w, cu.eps, y=y, rstd=rstd),
          2 * T * d * b + d * b + 4 * T),
         ("rmsnorm_bwd_d4097", lambda: fo.fo_rmsnorm_bwd(dy, x, w, rstd, cu.eps, dx=dx, dw=dw, ws=ws),
          3 * T * d * b + d * b + 4 * T + 4 * d),
         ("swiglu_fwd_F14337", lambda: fo.fo_swiglu_fwd(g, u, h=h), 3 * T * F * b),
+        ("xent_fwd_bwd_V50257", lambda: fo.fo_xent_fwd_bwd(lg, tg, -100, cv.z_loss, 1.0, dlogits=dlg,
+                                                           ws=xws, out=xo),
+         (2 * (T - n_ign) + n_ign) * V * b + 8 * T),
     ]
     scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     res = {}

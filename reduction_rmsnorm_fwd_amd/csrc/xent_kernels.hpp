@@ -15,9 +15,10 @@
 // NV 16-byte vectors of the row into registers, folding each into a running
 // (max, sum of exp) pair as it arrives (online logsumexp); the pairs are merged across
 // the workgroup in a fixed order; the gradient is then formed from the registers and
-// written.  The row is read from HBM once.  Rows too long for the registers (or not
-// vector-aligned) take the streaming form, which makes the same online pass and then
-// reads the row a second time for the gradient.
+// written.  The row is read from HBM once, also when it starts off the 16-byte grid or
+// its length is not a multiple of the vector (full vectors are still 16-byte accesses).
+// Rows too long for the registers take the streaming form, which makes the same online
+// pass and then reads the row a second time for the gradient.
 #pragma once
 
 #include <type_traits>
@@ -155,21 +156,45 @@ struct RowArgs {
   float* row_z;     // [T] c lse^2 (0 for invalid rows)
 };
 
-// Register-resident row kernel.  Requires V % VEC == 0, aligned rows, nvec <= NT*NV.
-template <typename Tin, typename Tout, int NV, int NT>
+// Vector v of a row of n elements.  UA (rows of any element alignment and length): a
+// full vector is one 16-byte load at its element-aligned address (gfx950 serves global
+// memory in unaligned mode), the last, partial vector is read element by element and
+// padded with -inf, which drops out of the maximum and the sum of exponentials.
+template <typename T, bool UA>
+__device__ __forceinline__ Pack<T> row_vec(const T* p, int64_t v, int64_t n) {
+  constexpr int VEC = Vec<T>::N;
+  if (!UA || (v + 1) * VEC <= n) return load_pack(p + v * VEC);
+  Pack<T> r;
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) r.v[j] = v * VEC + j < n ? p[v * VEC + j] : from_f32<T>(-INFINITY);
+  return r;
+}
+
+// Register-resident row kernel.  Requires nvec <= NT*NV and, unless UA, V % VEC == 0 and
+// 16-byte aligned rows.  UA: rows of any element alignment and length (same element
+// type in and out): full vectors are still 16-byte accesses, the partial last vector of
+// each row goes element by element, so no access touches a neighbouring row.
+template <typename Tin, typename Tout, int NV, int NT, bool UA = false>
 __global__ __launch_bounds__(NT) void row_reg(RowArgs a, const Tin* z, Tout* dz) {
   constexpr int VEC = Vec<Tin>::N;
   static_assert(Vec<Tout>::N == VEC || Vec<Tout>::N == 2 * VEC, "vector widths");
+  static_assert(!UA || Vec<Tout>::N == VEC, "unaligned rows: one element type");
   __shared__ float shm[NT / kWave], shs[NT / kWave];
   __shared__ float sh_zy;
   const int64_t row = blockIdx.x;
   const long long y = a.tg[row];
-  const int64_t nvec = a.V / VEC;
+  const int64_t nvec = UA ? ceil_div(a.V, (int64_t)VEC) : a.V / VEC;
   if (!row_valid(y, a.V, a.ignore)) {
     if (dz != nullptr) {
       Tout* dr = dz + row * a.ldd;
-      if constexpr (Vec<Tout>::N == VEC) zero_row<Tout, VEC, NT>(dr, nvec);
-      else for (int64_t e = threadIdx.x; e < a.V; e += NT) dr[e] = from_f32<Tout>(0.f);
+      if constexpr (UA) {
+        zero_row<Tout, VEC, NT>(dr, a.V / VEC);
+        for (int64_t e = a.V / VEC * VEC + threadIdx.x; e < a.V; e += NT) dr[e] = from_f32<Tout>(0.f);
+      } else if constexpr (Vec<Tout>::N == VEC) {
+        zero_row<Tout, VEC, NT>(dr, nvec);
+      } else {
+        for (int64_t e = threadIdx.x; e < a.V; e += NT) dr[e] = from_f32<Tout>(0.f);
+      }
     }
     if (threadIdx.x == 0) { a.row_loss[row] = 0.f; a.row_z[row] = 0.f; }
     return;
@@ -180,7 +205,7 @@ __global__ __launch_bounds__(NT) void row_reg(RowArgs a, const Tin* z, Tout* dz)
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int64_t v = threadIdx.x + (int64_t)i * NT;
-    if (v < nvec) xv[i] = load_pack(zr + v * VEC);
+    if (v < nvec) xv[i] = row_vec<Tin, UA>(zr, v, a.V);
   }
   float m = -INFINITY, s = 0.f;
 #pragma unroll
@@ -227,7 +252,13 @@ __global__ __launch_bounds__(NT) void row_reg(RowArgs a, const Tin* z, Tout* dz)
         Pack<Tout> o;
 #pragma unroll
         for (int j = 0; j < VEC; ++j) o.v[j] = from_f32<Tout>(g[j]);
-        store_pack(dr + v * VEC, o);
+        if (!UA || (v + 1) * VEC <= a.V) {
+          store_pack(dr + v * VEC, o);
+        } else {
+#pragma unroll
+          for (int j = 0; j < VEC; ++j)
+            if (v * VEC + j < a.V) dr[v * VEC + j] = o.v[j];
+        }
       } else {
         // fp32 in, bf16 out: VEC outputs fill half a 16-byte vector
         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -519,6 +550,11 @@ hipError_t launch_rows(const RowArgs& a, const Tin* z, Tout* dz, hipStream_t st,
   constexpr int VEC = Vec<Tin>::N;
   const bool vec = a.V % VEC == 0 && a.ldz % VEC == 0 && aligned16(z) &&
                    (dz == nullptr || (a.ldd % VEC == 0 && aligned16(dz)));
+  // otherwise: element-aligned rows of one element type that fit the registers
+  const bool ua_ok = std::is_same<Tin, Tout>::value &&
+                     reinterpret_cast<uintptr_t>(z) % sizeof(Tin) == 0 &&
+                     reinterpret_cast<uintptr_t>(dz) % sizeof(Tout) == 0 &&
+                     ceil_div(a.V, (int64_t)VEC) <= 16 * 1024;
   const dim3 grid((unsigned)a.T);
   if (vec) {
     const int64_t nvec = a.V / VEC;
@@ -546,6 +582,24 @@ hipError_t launch_rows(const RowArgs& a, const Tin* z, Tout* dz, hipStream_t st,
         }
         break;
       default: row_stream<Tin, Tout, VEC, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
+    }
+  } else if (ua_ok) {
+    // rows of any element alignment and length that fit the registers
+    const int64_t nvec = ceil_div(a.V, (int64_t)VEC);
+    if (nvec <= 256 * 4) {
+      const int64_t per = ceil_div(nvec, 256);
+      if (per <= 1) row_reg<Tin, Tout, 1, 256, true><<<grid, 256, 0, st>>>(a, z, dz);
+      else if (per <= 2) row_reg<Tin, Tout, 2, 256, true><<<grid, 256, 0, st>>>(a, z, dz);
+      else row_reg<Tin, Tout, 4, 256, true><<<grid, 256, 0, st>>>(a, z, dz);
+      return hipGetLastError();
+    }
+    switch (ceil_div(nvec, 1024)) {
+      case 1: row_reg<Tin, Tout, 1, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      case 2: row_reg<Tin, Tout, 2, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      case 3: case 4: row_reg<Tin, Tout, 4, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      case 5: case 6: case 7: case 8: row_reg<Tin, Tout, 8, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      case 9: case 10: case 11: case 12: row_reg<Tin, Tout, 12, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      default: row_reg<Tin, Tout, 16, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
     }
   } else {
     row_stream<Tin, Tout, 1, 1024><<<grid, 1024, 0, st>>>(a, z, dz);

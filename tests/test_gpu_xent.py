@@ -44,9 +44,10 @@ def test_configs_small(gpu, cid, T):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("V", [4097, 7, 8, 1000, 131072, 151936, 200000])
+@pytest.mark.parametrize("V", [4097, 7, 8, 1000, 32001, 50257, 131072, 151936, 200000])
 def test_vocab_sizes(gpu, dtype, V):
-    # unaligned (scalar path), tiny, register-resident and streaming rows
+    # rows off the 16-byte grid (4097, 7, 32001, 50257: every row starts at another
+    # alignment), tiny, register-resident and streaming rows
     g = torch.Generator().manual_seed(V)
     T = 9
     z = (2 * torch.randn(T, V, generator=g)).to(synth.torch_dtype(dtype))
@@ -68,6 +69,27 @@ def test_ignored_rows_exact_zero_and_garbage_invariance(gpu):
     z2[ign] = 1234.0  # finite garbage in ignored rows changes nothing
     b = run(gpu, z2, t, 0.0)
     assert torch.equal(a["loss"], b["loss"]) and torch.equal(a["dlogits"], b["dlogits"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unaligned_rows_in_place_and_strided(gpu, dtype):
+    # a 50257-wide vocabulary (rows start at every alignment) in place, and the same rows
+    # as a view with a row stride of 50263 and a misaligned base: the same bits
+    g = torch.Generator().manual_seed(50257)
+    T, V = 12, 50257
+    z = (2 * torch.randn(T, V, generator=g)).to(synth.torch_dtype(dtype))
+    t = torch.randint(0, V, (T,), generator=g)
+    t[5] = IGN
+    a = run(gpu, z, t, 1e-4)
+    compare(z, t, 1e-4, dtype, a)
+    b = run(gpu, z, t, 1e-4, inplace=True)
+    assert torch.equal(a["dlogits"], b["dlogits"]) and torch.equal(a["loss"], b["loss"])
+    wide = torch.zeros(T, V + 6, dtype=z.dtype)
+    wide[:, 3:3 + V] = z
+    zs = wide.to(DEV)[:, 3:3 + V]  # base 6 bytes (bf16) / 12 bytes (fp32) off, ld = V + 6
+    c = gpu.fo_xent_fwd_bwd(zs, t.to(DEV), IGN, 1e-4, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(c["dlogits"].cpu(), a["dlogits"]) and torch.equal(c["loss"].cpu(), a["loss"])
 
 
 def test_in_place_matches_out_of_place(gpu):
