@@ -13,7 +13,8 @@
 // between the sweeps: the student row in VGPRs, the teacher row in VGPRs and (for the
 // longest rows) LDS, filled by buffer loads that write LDS directly; so HBM sees each
 // input once and dz once (3 T V b).  Longer or unaligned rows re-read both rows in the
-// second sweep (from L2 / MALL).
+// second sweep (from L2 / MALL); unaligned rows still move their full vectors as
+// 16-byte accesses.
 #include "xent_kernels.hpp"
 
 namespace fo {
@@ -50,7 +51,9 @@ __device__ __forceinline__ void stats_merge(Stats& s, const Stats& o) {
 // VEC values of the student (z) and teacher (t)
 // (exponentials: accurate for fp32 rows, the hardware path for bf16 rows, as the
 // hard-label kernels)
-template <typename T, int VEC>
+// PAD: some values are -inf padding (both z and t) past the end of the row; a zero
+// teacher weight then contributes nothing to A and B (plain fmaf would give 0 * -inf).
+template <typename T, int VEC, bool PAD = false>
 __device__ __forceinline__ void stats_add(Stats& s, const float* z, const float* t) {
   float vz = z[0], vt = t[0];
 #pragma unroll
@@ -65,6 +68,7 @@ __device__ __forceinline__ void stats_add(Stats& s, const float* z, const float*
     s.ss += xent::ex<T>(z[j] - s.ms);
     const float e = xent::ex<T>(t[j] - s.mt);
     s.st += e;
+    if (PAD && e == 0.f) continue;
     s.a = fmaf(e, z[j], s.a);
     s.b = fmaf(e, t[j], s.b);
   }
@@ -232,8 +236,11 @@ __global__ __launch_bounds__(kRowThreads) void soft_row(DistillArgs a, const T* 
 
 // Any row length and alignment: the second sweep re-reads both rows.  dz may alias z
 // (each element is read by the thread that writes it; the merge barrier separates the
-// first sweep's reads from the writes).
-template <typename T, int VEC>
+// first sweep's reads from the writes).  UA (rows of any element alignment and length,
+// VEC > 1): full vectors are 16-byte accesses at element-aligned addresses (gfx950
+// serves global memory in unaligned mode), the partial last vector goes element by
+// element, read as -inf padding past the row.
+template <typename T, int VEC, bool UA = false>
 __global__ __launch_bounds__(kRowThreads) void soft_stream(DistillArgs a, const T* z,
                                                           const T* zt, T* dz) {
   __shared__ Stats sh[kRowThreads / kWave];
@@ -242,22 +249,31 @@ __global__ __launch_bounds__(kRowThreads) void soft_stream(DistillArgs a, const 
     masked_row<T>(a, row, dz);
     return;
   }
-  const int64_t n = a.V / VEC;  // vectors (VEC = 1: elements)
+  // vectors (VEC = 1: elements); UA: the last one partial
+  const int64_t n = UA ? ceil_div(a.V, (int64_t)VEC) : a.V / VEC;
   const T* zr = z + row * a.ldz;
   const T* tr = zt + row * a.ldt;
+  auto vec_at = [&](const T* p, int64_t v, bool cached) {
+    if (!UA || (v + 1) * VEC <= a.V) return cached ? load_pack_cached(p + v * VEC) : load_pack(p + v * VEC);
+    Pack<T> r;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+      r.v[j] = v * VEC + j < a.V ? p[v * VEC + j] : from_f32<T>(-INFINITY);
+    return r;
+  };
   Stats s;
   stats_init(s);
   for (int64_t v = threadIdx.x; v < n; v += kRowThreads) {
     float zf[VEC], tf[VEC];
     if constexpr (VEC > 1) {
-      const Pack<T> zp = load_pack_cached(zr + v * VEC), tp = load_pack_cached(tr + v * VEC);
+      const Pack<T> zp = vec_at(zr, v, true), tp = vec_at(tr, v, true);
 #pragma unroll
       for (int j = 0; j < VEC; ++j) { zf[j] = to_f32(zp.v[j]); tf[j] = to_f32(tp.v[j]); }
     } else {
       zf[0] = to_f32(zr[v]);
       tf[0] = to_f32(tr[v]);
     }
-    stats_add<T, VEC>(s, zf, tf);
+    stats_add<T, VEC, UA>(s, zf, tf);
   }
   const Stats r = block_stats<kRowThreads>(s, sh);
   float lse_z, lse_t;
@@ -267,13 +283,19 @@ __global__ __launch_bounds__(kRowThreads) void soft_stream(DistillArgs a, const 
   T* dr = dz + row * a.ldd;
   for (int64_t v = threadIdx.x; v < n; v += kRowThreads) {
     if constexpr (VEC > 1) {
-      const Pack<T> zp = load_pack(zr + v * VEC), tp = load_pack(tr + v * VEC);
+      const Pack<T> zp = vec_at(zr, v, false), tp = vec_at(tr, v, false);
       Pack<T> o;
 #pragma unroll
       for (int j = 0; j < VEC; ++j)
         o.v[j] = from_f32<T>(scale * (xent::ex<T>(to_f32(zp.v[j]) - lse_z) -
                                       xent::ex<T>(to_f32(tp.v[j]) - lse_t)));
-      store_pack(dr + v * VEC, o);
+      if (!UA || (v + 1) * VEC <= a.V) {
+        store_pack(dr + v * VEC, o);
+      } else {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+          if (v * VEC + j < a.V) dr[v * VEC + j] = o.v[j];
+      }
     } else {
       dr[v] = from_f32<T>(scale * (xent::ex<T>(to_f32(zr[v]) - lse_z) -
                                    xent::ex<T>(to_f32(tr[v]) - lse_t)));
@@ -344,6 +366,11 @@ int distill_impl(const DistillArgs& a0, const T* z, const T* zt, T* dz, float* l
       else soft_row<T, 16, 9><<<pgrid, block, 0, st>>>(a, z, zt, dz);
     } else if (vec) {
       soft_stream<T, VEC><<<grid, block, 0, st>>>(a, z, zt, dz);
+    } else if (reinterpret_cast<uintptr_t>(z) % sizeof(T) == 0 &&
+               reinterpret_cast<uintptr_t>(zt) % sizeof(T) == 0 &&
+               reinterpret_cast<uintptr_t>(dz) % sizeof(T) == 0) {
+      // element-aligned rows of any alignment and length: 16-byte accesses still
+      soft_stream<T, VEC, true><<<grid, block, 0, st>>>(a, z, zt, dz);
     } else {
       soft_stream<T, 1><<<grid, block, 0, st>>>(a, z, zt, dz);
     }

@@ -37,10 +37,12 @@ def cfg_of(dtype, T, V, seed=31, logit_std=3.0):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("V", [100, 1000, 4096, 49152, 128256, 151936])
+@pytest.mark.parametrize("V", [100, 1000, 4096, 49152, 50257, 128256, 151936])
 def test_vocab_paths(gpu, dtype, V):
-    # V 100 (unaligned: element path), 1000/4096 (4 vectors), 49152 (8), 128256 (16 with
-    # the teacher partly in LDS), 151936 (beyond on-chip rows: streaming)
+    # V 100 and 50257 (rows off the 16-byte grid: 16-byte accesses at element-aligned
+    # addresses, the partial last vector element by element), 1000/4096 (4 vectors),
+    # 49152 (8), 128256 (16 with the teacher partly in LDS), 151936 (beyond on-chip rows:
+    # streaming)
     T = 6 if V > 50000 else 23
     i = synth.distill_inputs(cfg_of(dtype, T, V))
     o = run(gpu, i["logits"], i["teacher"], i["row_mask"])
@@ -99,3 +101,17 @@ def test_full_size_sampled(gpu):
         kl += b["kl"] * b["n_valid"]
     check_loss(o["loss"].item(), ce / n)
     check_loss(o["kl"].item(), kl / n, "kl", rel=5e-4)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unaligned_rows_in_place(gpu, dtype):
+    # a 50257-wide vocabulary (every row at another alignment), gradient written over the
+    # student logits: the same bits as out of place
+    i = synth.distill_inputs(cfg_of(dtype, 10, 50257, seed=9))
+    z, zt, m = i["logits"].to(DEV), i["teacher"].to(DEV), i["row_mask"].to(DEV)
+    a = gpu.fo_distill_fwd_bwd(z, zt, m)
+    zc = z.clone()
+    b = gpu.fo_distill_fwd_bwd(zc, zt, m, dlogits=zc)
+    torch.cuda.synchronize()
+    assert torch.equal(a["dlogits"].cpu(), b["dlogits"].cpu())
+    assert torch.equal(a["loss"].cpu(), b["loss"].cpu()) and torch.equal(a["kl"].cpu(), b["kl"].cpu())
