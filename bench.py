@@ -404,7 +404,8 @@ def distill_line(fo, synth, torch, stream, med, reps, copy_gbs):
 def unaligned_lines(fo, synth, torch, stream, med):
     """Rows that are not a multiple of the 16-byte vector, at the Llama-3-8B token count,
     reported apart from the aligned per-op lines: RMSNorm with d = 4097, SwiGLU with
-    F = 14337 and cross-entropy over a 50257-entry vocabulary (GPT-2's)."""
+    F = 14337 (contiguous, and as the halves of one [T, 2F] projection) and cross-entropy
+    over a 50257-entry vocabulary (GPT-2's)."""
     import dataclasses
     c3 = synth.CONFIGS[3]
     cu = dataclasses.replace(c3, d=4097, F=14337)
@@ -421,6 +422,12 @@ def unaligned_lines(fo, synth, torch, stream, med):
     h = torch.empty_like(g)
     F = g.shape[1]
     b = 2
+    # gate and up as the two halves of one [T, 2F] projection with an odd F: strided rows
+    # off the 16-byte grid (not walkable as one flat array)
+    gu2 = torch.cat([g, u], dim=1)
+    g2, u2 = gu2[:, :F], gu2[:, F:]
+    dh2 = s["dh"].to("cuda")
+    dgu2 = torch.empty_like(gu2)
     cv = dataclasses.replace(c3, V=50257)
     xe = synth.xent_inputs(cv)
     lg, tg = xe["logits"].to("cuda"), xe["targets"].to("cuda")
@@ -435,6 +442,9 @@ def unaligned_lines(fo, synth, torch, stream, med):
         ("rmsnorm_bwd_d4097", lambda: fo.fo_rmsnorm_bwd(dy, x, w, rstd, cu.eps, dx=dx, dw=dw, ws=ws),
          3 * T * d * b + d * b + 4 * T + 4 * d),
         ("swiglu_fwd_F14337", lambda: fo.fo_swiglu_fwd(g, u, h=h), 3 * T * F * b),
+        ("swiglu_fwd_halves_F14337", lambda: fo.fo_swiglu_fwd(g2, u2, h=h), 3 * T * F * b),
+        ("swiglu_bwd_halves_F14337", lambda: fo.fo_swiglu_bwd(dh2, g2, u2, dgate=dgu2[:, :F],
+                                                               dup=dgu2[:, F:]), 5 * T * F * b),
         ("xent_fwd_bwd_V50257", lambda: fo.fo_xent_fwd_bwd(lg, tg, -100, cv.z_loss, 1.0, dlogits=dlg,
                                                            ws=xws, out=xo),
          (2 * (T - n_ign) + n_ign) * V * b + 8 * T),

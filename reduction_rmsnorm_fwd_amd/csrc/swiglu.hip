@@ -12,7 +12,9 @@
 // each output written once with 16-byte vector accesses, the gate and up reads of an
 // element issued together so one pass produces the output.  Rows may have their own
 // strides (halves of a [T, 2F] tensor work); fully contiguous operands are walked as
-// one flat row.
+// one flat row.  bf16 rows off the 16-byte grid (odd F, or halves of a [T, 2F] tensor
+// with odd F) still move their full vectors as 16-byte accesses at element-aligned
+// addresses, the partial last vector of a row element by element.
 #include "fo_common.hpp"
 
 namespace fo {
@@ -50,8 +52,33 @@ __device__ __forceinline__ float act_d(float x) {
 
 // Index space: rows x nvr vectors (VEC elements each); nb column blocks per row.
 // GATED: h = act(g) u; otherwise h = act(g) (u unused).
-template <typename T, int VEC, int ACT, bool GATED>
-__global__ __launch_bounds__(kThreads) void swiglu_fwd_k(int64_t nvr, int64_t nb,
+// Vector v of a row of nel elements.  UA (rows of any element alignment and length):
+// a full vector is one 16-byte access at its element-aligned address (gfx950 serves
+// global memory in unaligned mode), the partial last vector goes element by element.
+template <typename T, bool UA>
+__device__ __forceinline__ Pack<T> ld_v(const T* p, int64_t v, int64_t nel) {
+  constexpr int VEC = Vec<T>::N;
+  if (!UA || (v + 1) * VEC <= nel) return load_pack(p + v * VEC);
+  Pack<T> r;
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) r.v[j] = v * VEC + j < nel ? p[v * VEC + j] : from_f32<T>(0.f);
+  return r;
+}
+template <typename T, bool UA>
+__device__ __forceinline__ void st_v(T* p, int64_t v, int64_t nel, const Pack<T>& o) {
+  constexpr int VEC = Vec<T>::N;
+  if (!UA || (v + 1) * VEC <= nel) {
+    store_pack(p + v * VEC, o);
+  } else {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+      if (v * VEC + j < nel) p[v * VEC + j] = o.v[j];
+  }
+}
+
+// nel: elements per row (= nvr * VEC unless UA, where the last vector may be partial)
+template <typename T, int VEC, int ACT, bool GATED, bool UA = false>
+__global__ __launch_bounds__(kThreads) void swiglu_fwd_k(int64_t nvr, int64_t nb, int64_t nel,
                                                          const T* g, int64_t ldg, const T* u,
                                                          int64_t ldu, T* h, int64_t ldh) {
   const int64_t row = blockIdx.x / nb;
@@ -66,8 +93,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_fwd_k(int64_t nvr, int64_t nb
     for (int i = 0; i < kUnroll; ++i) {
       const int64_t v = v0 + i * kThreads;
       if (v < nvr) {
-        gv[i] = load_pack(gr + v * VEC);
-        if constexpr (GATED) uv[i] = load_pack(ur + v * VEC);
+        gv[i] = ld_v<T, UA>(gr, v, nel);
+        if constexpr (GATED) uv[i] = ld_v<T, UA>(ur, v, nel);
       }
     }
 #pragma unroll
@@ -81,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_fwd_k(int64_t nvr, int64_t nb
           if constexpr (GATED) o.v[j] = from_f32<T>(act_f<ACT>(gf) * to_f32(uv[i].v[j]));
           else o.v[j] = from_f32<T>(act_f<ACT>(gf));
         }
-        store_pack(hr + v * VEC, o);
+        st_v<T, UA>(hr, v, nel, o);
       }
     }
   } else {
@@ -98,8 +125,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_fwd_k(int64_t nvr, int64_t nb
 }
 
 // GATED: dg = dh u act'(g), du = dh act(g); otherwise dg = dh act'(g) (u, du unused).
-template <typename T, int VEC, int ACT, bool GATED>
-__global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t nvr, int64_t nb,
+template <typename T, int VEC, int ACT, bool GATED, bool UA = false>
+__global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t nvr, int64_t nb, int64_t nel,
                                                          const T* dh, int64_t lddh,
                                                          const T* g, int64_t ldg, const T* u,
                                                          int64_t ldu, T* dg, int64_t lddg,
@@ -118,9 +145,9 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t nvr, int64_t nb
     for (int i = 0; i < kUnroll; ++i) {
       const int64_t v = v0 + i * kThreads;
       if (v < nvr) {
-        hv[i] = load_pack(dhr + v * VEC);
-        gv[i] = load_pack(gr + v * VEC);
-        if constexpr (GATED) uv[i] = load_pack(ur + v * VEC);
+        hv[i] = ld_v<T, UA>(dhr, v, nel);
+        gv[i] = ld_v<T, UA>(gr, v, nel);
+        if constexpr (GATED) uv[i] = ld_v<T, UA>(ur, v, nel);
       }
     }
 #pragma unroll
@@ -146,8 +173,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t nvr, int64_t nb
             og.v[j] = from_f32<T>(hf * act_d<ACT>(gf));
           }
         }
-        store_pack(dgr + v * VEC, og);
-        if constexpr (GATED) store_pack(dur + v * VEC, ou);
+        st_v<T, UA>(dgr, v, nel, og);
+        if constexpr (GATED) st_v<T, UA>(dur, v, nel, ou);
       }
     }
   } else {
@@ -176,8 +203,9 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t nvr, int64_t nb
 // Launch geometry: rows x vectors-per-row; one flat row when every operand is a
 // single contiguous [T*F] run.
 struct Geo {
-  int64_t rows, nvr, nb;
-  bool vec;
+  int64_t rows, nvr, nb, nel;
+  bool vec;  // 16-byte vectors on the 16-byte grid
+  bool ua;   // otherwise, bf16: 16-byte vectors at element-aligned addresses
 };
 
 template <typename T>
@@ -189,11 +217,17 @@ Geo plan(int64_t T_, int64_t F, int n, const void* const* ptr, const int64_t* ld
     aligned = aligned && aligned16(ptr[i]);
     ld_ok = ld_ok && ld[i] % VEC == 0;
   }
+  bool elem = true;
+  for (int i = 0; i < n; ++i) elem = elem && reinterpret_cast<uintptr_t>(ptr[i]) % sizeof(T) == 0;
   Geo g;
   const int64_t per_row = contiguous ? T_ * F : F;
   g.rows = contiguous ? 1 : T_;
   g.vec = aligned && per_row % VEC == 0 && (contiguous || ld_ok);
-  g.nvr = g.vec ? per_row / VEC : per_row;
+  // 2-byte elements one by one are bound by the access issue rate; fp32 element
+  // accesses coalesce well enough to keep
+  g.ua = !g.vec && sizeof(T) == 2 && elem;
+  g.nel = per_row;
+  g.nvr = g.vec ? per_row / VEC : g.ua ? ceil_div(per_row, (int64_t)VEC) : per_row;
   g.nb = ceil_div(g.nvr, kThreads * kUnroll);
   return g;
 }
@@ -210,9 +244,11 @@ int fwd_impl(int64_t T_, int64_t F, const void* g, int64_t ldg, const void* u, i
   const T* up = static_cast<const T*>(u);
   T* hp = static_cast<T*>(h);
   if (geo.vec)
-    swiglu_fwd_k<T, Vec<T>::N, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, gp, ldg, up, ldu, hp, ldh);
+    swiglu_fwd_k<T, Vec<T>::N, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, geo.nel, gp, ldg, up, ldu, hp, ldh);
+  else if (geo.ua)
+    swiglu_fwd_k<T, Vec<T>::N, ACT, GATED, true><<<grid, block, 0, st>>>(geo.nvr, geo.nb, geo.nel, gp, ldg, up, ldu, hp, ldh);
   else
-    swiglu_fwd_k<T, 1, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, gp, ldg, up, ldu, hp, ldh);
+    swiglu_fwd_k<T, 1, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, geo.nel, gp, ldg, up, ldu, hp, ldh);
   return launch_status();
 }
 
@@ -230,10 +266,13 @@ int bwd_impl(int64_t T_, int64_t F, const void* dh, int64_t lddh, const void* g,
   T* dgp = static_cast<T*>(dg);
   T* dup = static_cast<T*>(du);
   if (geo.vec)
-    swiglu_bwd_k<T, Vec<T>::N, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, dhp, lddh, gp, ldg, up,
-                                                                   ldu, dgp, lddg, dup, lddu);
+    swiglu_bwd_k<T, Vec<T>::N, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, geo.nel, dhp, lddh, gp, ldg,
+                                                                   up, ldu, dgp, lddg, dup, lddu);
+  else if (geo.ua)
+    swiglu_bwd_k<T, Vec<T>::N, ACT, GATED, true><<<grid, block, 0, st>>>(geo.nvr, geo.nb, geo.nel, dhp, lddh, gp,
+                                                                         ldg, up, ldu, dgp, lddg, dup, lddu);
   else
-    swiglu_bwd_k<T, 1, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, dhp, lddh, gp, ldg, up, ldu,
+    swiglu_bwd_k<T, 1, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, geo.nel, dhp, lddh, gp, ldg, up, ldu,
                                                            dgp, lddg, dup, lddu);
   return launch_status();
 }

@@ -45,9 +45,11 @@ def test_unaligned_widths(gpu, dtype, F):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_halves_of_fused_projection(gpu, dtype):
-    # gate and up as the two halves of one [T, 2F] tensor (row stride 2F)
-    T, F = 77, 1408
+@pytest.mark.parametrize("F", [1408, 1409, 14337])
+def test_halves_of_fused_projection(gpu, dtype, F):
+    # gate and up as the two halves of one [T, 2F] tensor (row stride 2F); with an odd F
+    # every row of the up half, and every other row of both, starts off the 16-byte grid
+    T = 77 if F < 10000 else 9
     g = torch.Generator().manual_seed(1)
     td = synth.torch_dtype(dtype)
     gu = torch.randn(T, 2 * F, generator=g).to(td)
