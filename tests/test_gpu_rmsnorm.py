@@ -122,3 +122,25 @@ def test_full_size_sampled(gpu, cid):
     for r0 in range(0, cfg.T, 2048):
         rdw += oracle.rmsnorm_bwd(i["dy"][r0:r0 + 2048], i["x"][r0:r0 + 2048], w, cfg.eps)[1]
     check(dw, rdw, "f32", "dw")
+
+
+def test_unaligned_full_size_sampled(gpu):
+    # the bench's unaligned line: Llama-3-8B token count with d = 4097 (bf16, contiguous,
+    # so 7 rows in 8 start off the 16-byte grid), sampled rows; dw over every row
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS[3], d=4097)
+    i = synth.rmsnorm_inputs(cfg)
+    y, rstd, dx, dw = run(gpu, i["x"], i["w"], i["dy"], cfg.eps)
+    rows = np.unique(np.concatenate([[0, 1, 2, 7, cfg.T - 1],
+                                     np.random.default_rng(4097).integers(0, cfg.T, 27)]))
+    x, w, dy = i["x"][rows], i["w"], i["dy"][rows]
+    ry, rr = oracle.rmsnorm_fwd(x, w, cfg.eps)
+    rdx, _ = oracle.rmsnorm_bwd(dy, x, w, cfg.eps)
+    check(y[rows], ry, cfg.dtype, "y", single_rounding=True)
+    check(rstd[rows], rr, "f32", "rstd")
+    check(dx[rows], rdx, cfg.dtype, "dx", single_rounding=True)
+    rdw = np.zeros(cfg.d)
+    for r0 in range(0, cfg.T, 2048):
+        rdw += oracle.rmsnorm_bwd(i["dy"][r0:r0 + 2048], i["x"][r0:r0 + 2048], w, cfg.eps)[1]
+    check(dw, rdw, "f32", "dw")
+

@@ -97,3 +97,21 @@ def test_full_size_sampled(gpu, cid):
                                      np.random.default_rng(cid).integers(0, cfg.T, 14)]))
     compare(i["gate"][rows], i["up"][rows], i["dh"][rows], cfg.dtype,
             (h[rows], dg[rows], du[rows]))
+
+
+def test_halves_full_size_sampled(gpu):
+    # the bench's unaligned line: gate and up as halves of one [8192, 2 x 14337] bf16
+    # tensor (strided rows off the 16-byte grid), sampled rows
+    T, F = 8192, 14337
+    g = torch.Generator().manual_seed(14337)
+    gu = torch.randn(T, 2 * F, generator=g).to(torch.bfloat16)
+    dh = torch.randn(T, F, generator=g).to(torch.bfloat16)
+    gug = gu.to(DEV)
+    h = gpu.fo_swiglu_fwd(gug[:, :F], gug[:, F:])
+    dgu = torch.empty_like(gug)
+    gpu.fo_swiglu_bwd(dh.to(DEV), gug[:, :F], gug[:, F:], dgate=dgu[:, :F], dup=dgu[:, F:])
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, T - 1], np.random.default_rng(2).integers(0, T, 13)]))
+    h, dgu = h.cpu(), dgu.cpu()
+    compare(gu[rows, :F], gu[rows, F:], dh[rows], "bf16", (h[rows], dgu[rows, :F], dgu[rows, F:]))
+

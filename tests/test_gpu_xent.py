@@ -159,3 +159,27 @@ def test_full_size(gpu, cid):
             b = oracle.xent_fwd_bwd(z[r0:r0 + 512], t[r0:r0 + 512], IGN, cfg.z_loss, 1.0)
             tot += b["loss"] * b["n_valid"]
         check_loss(o["loss"].item(), tot / n_full)
+
+
+def test_unaligned_full_size(gpu):
+    # the bench's unaligned line: Llama-3-8B logits shape with GPT-2's 50257-entry
+    # vocabulary (every row at another alignment), z-loss 1e-4: sampled gradient rows and
+    # the loss over every row (oracle in row blocks)
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS[3], V=50257)
+    i = synth.xent_inputs(cfg)
+    z, t = i["logits"], i["targets"]
+    o = run(gpu, z, t, cfg.z_loss)
+    rows = np.unique(np.concatenate([[0, 1, cfg.T - 1], np.random.default_rng(50257).integers(0, cfg.T, 13)]))
+    n_full = int(((t != IGN) & (t >= 0) & (t < cfg.V)).sum())
+    tg = t[rows].numpy()
+    valid = (tg != IGN) & (tg >= 0) & (tg < cfg.V)
+    _, _, _, dz = oracle.xent_rows(z[rows].double().numpy(), tg, valid, n_full, cfg.z_loss, 1.0)
+    check(o["dlogits"][rows], dz, cfg.dtype, "dlogits", single_rounding=True)
+    assert o["n_valid"].item() == n_full
+    tot = 0.0
+    for r0 in range(0, cfg.T, 512):
+        b = oracle.xent_fwd_bwd(z[r0:r0 + 512], t[r0:r0 + 512], IGN, cfg.z_loss, 1.0)
+        tot += b["loss"] * b["n_valid"]
+    check_loss(o["loss"].item(), tot / n_full)
+
