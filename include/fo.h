@@ -25,9 +25,14 @@
  *    ignore_index is counted into *status and treated as ignored; non-finite inputs
  *    propagate to the outputs.
  *  - Row strides `ld*` are in elements and must be >= the row length.  Any alignment
- *    is accepted: 16-byte-aligned bases and strides with a row length that is a
- *    multiple of the 16-byte vector take the vector path, anything else a scalar path
- *    with the same results.
+ *    is accepted (pointers aligned to their element type): 16-byte-aligned bases and
+ *    strides with a row length that is a multiple of the 16-byte vector take the vector
+ *    path.  Other rows of the RMSNorm, LayerNorm, cross-entropy and distillation calls,
+ *    and other bf16 rows of the MLP activations, still move their full vectors as
+ *    16-byte accesses at element-aligned addresses, with each row's partial last vector
+ *    element by element.  Anything else takes a scalar path.  Every path computes the
+ *    same results within rounding: the order of a row's reductions may differ between
+ *    paths, and is fixed for each.
  *  - Floating-point results are deterministic: no float atomics; every reduction runs
  *    in a fixed order, so two identical calls give identical bits.
  *  - T = 0 (no tokens) is valid: the call writes its defined empty result.
