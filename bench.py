@@ -697,6 +697,25 @@ def cpu_baseline():
     t["flce"] = time.perf_counter() - a
     T = c3.T
     est = (t["rmsnorm"] + t["rope"] + t["swiglu"] + t["xent"]) * T / n_layer + t["flce"] * T / n_head
+    # the oracle's rate on the same algorithmic work as the GPU lines (sample sizes)
+    Ts, d, b = n_layer, c3.d, 2
+    heads, D, F, V = c3.n_q + c3.n_kv, c3.head_dim, c3.F, c3.V
+    n_ign = int((xe["targets"] == synth.IGNORE_INDEX).sum())
+    alg = {
+        "rmsnorm": (2 * Ts * d * b + d * b + 4 * Ts) + (3 * Ts * d * b + d * b + 4 * Ts + 4 * d),
+        "rope": 2 * (2 * Ts * heads * D * b + 8 * Ts),
+        "swiglu": 8 * Ts * F * b,
+        "xent": (2 * (Ts - n_ign) + n_ign) * V * b + 8 * Ts,
+    }
+    n_valid_head = int((tg != synth.IGNORE_INDEX).sum())
+    rates = {f"{k}_GBps": round(v / t[k] / 1e9, 3) for k, v in alg.items()}
+    rates["flce_TFLOPs"] = round(6 * n_valid_head * c5.flce_H * c5.V / t["flce"] / 1e12, 4)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": round(T / est, 3), "unit": "tokens/s", "cores": int(blas_threads),
         "kind": "oracle",
@@ -707,6 +726,9 @@ def cpu_baseline():
         "seconds_measured": round(sum(t.values()), 2),
         "est_seconds_per_step": round(est, 2),
         "per_op_seconds_sample": {k: round(v, 3) for k, v in t.items()},
+        "per_op_rate_sample": rates,
+        "cpu_model": cpu_model,
+        "host_cpus": os.cpu_count(),
     }
 
 
