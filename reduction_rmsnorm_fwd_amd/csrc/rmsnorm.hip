@@ -441,12 +441,14 @@ __global__ __launch_bounds__(256) void rmsnorm_dw_partial_block(
   }
 }
 
-// dw[j] = sum_g partial[g, j].  A workgroup covers 16 columns as 4 float4 lanes; its
-// 64 row phases each sum a contiguous block of partial rows in order (the loads of up
-// to 8 rows issued before the first add), then 16 threads add the 64 phase sums in
-// order 0..63.  The many small workgroups keep every CU loading.
-constexpr int kReducePhases = 64;
-constexpr int kReduceCols = 16;
+// dw[j] = sum_g partial[g, j].  A workgroup covers 32 columns (one 128-byte line of a
+// partial row) as 8 float4 lanes; its 32 row phases each sum a contiguous block of
+// partial rows in order (up to 16 rows' loads issued before the first add), then 32
+// threads add the 32 phase sums in order 0..31.  Each line is read by one workgroup
+// only, and whole, so no two XCDs fetch the same line.
+constexpr int kReducePhases = 32;
+constexpr int kReduceCols = 32;
+constexpr int kReduceUnroll = 16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Columns [0, split) go to out0, columns [split, d) to out1 (LayerNorm: dw then db from
 // one launch over the 2d-wide partial rows).
@@ -454,22 +456,25 @@ __global__ __launch_bounds__(256) void rmsnorm_dw_reduce(int64_t G, int64_t d, i
                                                         const float* __restrict__ partial,
                                                         float* __restrict__ out0, int64_t split,
                                                         float* __restrict__ out1) {
+  constexpr int Q = kReduceCols / 4;  // float4 lanes per row phase
+  static_assert(Q * kReducePhases == 256, "one thread per (phase, float4 lane)");
   __shared__ float sh[kReducePhases][kReduceCols + 1];
-  const int q = threadIdx.x & 3;  // column quad
-  const int ph = threadIdx.x >> 2;
+  const int q = threadIdx.x % Q;
+  const int ph = threadIdx.x / Q;
   const int64_t j = (int64_t)blockIdx.x * kReduceCols + q * 4;
   const int64_t per = (G + kReducePhases - 1) / kReducePhases;
   const int64_t g0 = ph * per;
   const int64_t g1 = (g0 + per < G) ? g0 + per : G;
   float a[4] = {0.f, 0.f, 0.f, 0.f};
   if (j + 3 < d && ldp % 4 == 0 && (reinterpret_cast<uintptr_t>(partial) & 15) == 0) {
-    for (int64_t g = g0; g < g1; g += 8) {
-      f32x4 v[8];
+    for (int64_t g = g0; g < g1; g += kReduceUnroll) {
+      f32x4 v[kReduceUnroll];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (g + u < g1) v[u] = *reinterpret_cast<const f32x4*>(partial + (g + u) * ldp + j);
+      for (int u = 0; u < kReduceUnroll; ++u)
+        if (g + u < g1)
+          v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(partial + (g + u) * ldp + j));
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < kReduceUnroll; ++u)
         if (g + u < g1)
 #pragma unroll
           for (int c = 0; c < 4; ++c) a[c] += v[u][c];
@@ -485,8 +490,12 @@ __global__ __launch_bounds__(256) void rmsnorm_dw_reduce(int64_t G, int64_t d, i
   __syncthreads();
   if (threadIdx.x < kReduceCols) {
     const int64_t jc = (int64_t)blockIdx.x * kReduceCols + threadIdx.x;
-    float t = sh[0][threadIdx.x];
-    for (int p = 1; p < kReducePhases; ++p) t += sh[p][threadIdx.x];
+    float v[kReducePhases];
+#pragma unroll
+    for (int p = 0; p < kReducePhases; ++p) v[p] = sh[p][threadIdx.x];
+    float t = v[0];
+#pragma unroll
+    for (int p = 1; p < kReducePhases; ++p) t += v[p];
     if (jc < split) out0[jc] = t;
     else if (jc < d) out1[jc - split] = t;
   }
