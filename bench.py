@@ -669,25 +669,36 @@ def cpu_baseline():
     c3, c5 = synth.CONFIGS[3], synth.CONFIGS[5]
     n_layer, n_head = 4096, 2048
     s3 = synth.scaled(c3, n_layer)
+    # the layer ops are per token: their oracle calls are mapped over row blocks on a
+    # thread pool (numpy releases the GIL inside its loops), at most 16 workers (one
+    # GPU's share of the host)
+    from concurrent.futures import ThreadPoolExecutor
+    workers = max(1, min(16, os.cpu_count() or 1))
+    blocks = [(i * n_layer // workers, (i + 1) * n_layer // workers) for i in range(workers)]
+
+    def on_blocks(fn):
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda b: fn(*b), blocks))
+
     t = {}
     r = synth.rmsnorm_inputs(s3)
     a = time.perf_counter()
-    oracle.rmsnorm_fwd(r["x"], r["w"], c3.eps)
-    oracle.rmsnorm_bwd(r["dy"], r["x"], r["w"], c3.eps)
+    on_blocks(lambda i, j: (oracle.rmsnorm_fwd(r["x"][i:j], r["w"], c3.eps),
+                            oracle.rmsnorm_bwd(r["dy"][i:j], r["x"][i:j], r["w"], c3.eps)))
     t["rmsnorm"] = time.perf_counter() - a
     ro = synth.rope_inputs(s3)
     a = time.perf_counter()
-    oracle.rope_fwd(ro["q"], ro["k"], ro["pos"], c3.theta)
-    oracle.rope_bwd(ro["dq"], ro["dk"], ro["pos"], c3.theta)
+    on_blocks(lambda i, j: (oracle.rope_fwd(ro["q"][i:j], ro["k"][i:j], ro["pos"][i:j], c3.theta),
+                            oracle.rope_bwd(ro["dq"][i:j], ro["dk"][i:j], ro["pos"][i:j], c3.theta)))
     t["rope"] = time.perf_counter() - a
     s = synth.swiglu_inputs(s3)
     a = time.perf_counter()
-    oracle.swiglu_fwd(s["gate"], s["up"])
-    oracle.swiglu_bwd(s["dh"], s["gate"], s["up"])
+    on_blocks(lambda i, j: (oracle.swiglu_fwd(s["gate"][i:j], s["up"][i:j]),
+                            oracle.swiglu_bwd(s["dh"][i:j], s["gate"][i:j], s["up"][i:j])))
     t["swiglu"] = time.perf_counter() - a
     xe = synth.xent_inputs(s3)
     a = time.perf_counter()
-    oracle.xent_fwd_bwd(xe["logits"], xe["targets"], -100, c3.z_loss, 1.0)
+    on_blocks(lambda i, j: oracle.xent_fwd_bwd(xe["logits"][i:j], xe["targets"][i:j], -100, c3.z_loss, 1.0))
     t["xent"] = time.perf_counter() - a
     fl = synth.flce_inputs(c5)  # the full weight; a token sample of the hidden states
     h = fl["hidden"][:n_head]
@@ -717,12 +728,13 @@ def cpu_baseline():
     except OSError:
         pass
     return {
-        "value": round(T / est, 3), "unit": "tokens/s", "cores": int(blas_threads),
+        "value": round(T / est, 3), "unit": "tokens/s", "cores": int(max(workers, blas_threads)),
         "kind": "oracle",
         "sample": f"fp64 numpy oracle on {n_layer} of 8192 tokens for RMSNorm/RoPE/SwiGLU/xent "
                   f"and {n_head} tokens for the lm-head FLCE (full 128256x4096 weight), scaled "
-                  f"linearly to one 8192-token step; elementwise numpy runs on 1 thread, the "
-                  f"FLCE matmuls on {blas_threads} BLAS threads",
+                  f"linearly to one 8192-token step; the layer ops' oracle calls mapped over "
+                  f"{workers} row blocks on {workers} threads, the FLCE matmuls on "
+                  f"{blas_threads} BLAS threads",
         "seconds_measured": round(sum(t.values()), 2),
         "est_seconds_per_step": round(est, 2),
         "per_op_seconds_sample": {k: round(v, 3) for k, v in t.items()},
