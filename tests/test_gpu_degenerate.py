@@ -110,3 +110,63 @@ def test_xent_one_and_two_classes(gpu, dtype, V):
     check_loss(o["z_loss"].item(), r["z_loss"], "z_loss")
     check(o["dlogits"].cpu(), r["dlogits"], dtype, "dlogits", single_rounding=True)
     assert torch.all(o["dlogits"][4].cpu().float() == 0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [1, 2, 3])
+def test_layernorm_tiny_rows(gpu, dtype, d):
+    # d 1: the centred row is exactly zero, so y = b exactly, while dx is the difference
+    # of r g and r mean(g), zero up to the fp32 rounding of those two terms (the
+    # reference is identically zero, so the one-rounding bound, relative to the
+    # reference, does not apply there); eps 0.5 as for RMSNorm above
+    T, eps = 19, 0.5
+    td = synth.torch_dtype(dtype)
+    x, dy = randn((T, d), d + 7, dtype), randn((T, d), d + 107, dtype)
+    x[5] = 0
+    w = (1 + 0.1 * randn((d,), d + 207, "f32")).to(td)
+    b = (0.1 * randn((d,), d + 307, "f32")).to(td)
+    xg, wg = x.to(DEV), w.to(DEV)
+    y, mean, rstd = gpu.fo_layernorm_fwd(xg, wg, b.to(DEV), eps)
+    dx, dw, db = gpu.fo_layernorm_bwd(dy.to(DEV), xg, wg, mean, rstd)
+    torch.cuda.synchronize()
+    ry, rmu, rr = oracle.layernorm_fwd(x, w, b, eps)
+    rdx, rdw, rdb = oracle.layernorm_bwd(dy, x, w, eps)
+    check(y.cpu(), ry, dtype, "y", single_rounding=True)
+    check(mean.cpu(), rmu, "f32", "mean")
+    check(rstd.cpu(), rr, "f32", "rstd")
+    check(dx.cpu(), rdx, dtype, "dx", single_rounding=d > 1)
+    check(dw.cpu(), rdw, "f32", "dw")
+    check(db.cpu(), rdb, "f32", "db")
+    if d == 1:
+        assert torch.equal(y.cpu(), b.expand(T, 1))
+        r_gw = (rr[:, None] * (w.double() * dy.double()).numpy()).__abs__().max()
+        assert dx.cpu().double().abs().max().item() <= 2 * 2.0 ** -24 * r_gw
+
+
+@pytest.mark.parametrize("act", ["silu", "gelu", "relu"])
+def test_activation_single_unit(gpu, act):
+    T = 29
+    x, dy = randn((T, 1), 11, "bf16", 3.0), randn((T, 1), 12, "bf16")
+    y = gpu.fo_act_fwd(act, x.to(DEV))
+    dx = gpu.fo_act_bwd(act, dy.to(DEV), x.to(DEV))
+    torch.cuda.synchronize()
+    check(y.cpu(), oracle.act_fwd(x, act), "bf16", "y", single_rounding=True)
+    check(dx.cpu(), oracle.act_bwd(dy, x, act), "bf16", "dx", single_rounding=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 2])
+def test_distill_one_and_two_classes(gpu, dtype, V):
+    # V 1: both distributions are the point mass, so loss, KL and gradient vanish
+    T = 13
+    z, zt = randn((T, V), 21 + V, dtype, 2.0), randn((T, V), 31 + V, dtype, 2.0)
+    o = gpu.fo_distill_fwd_bwd(z.to(DEV), zt.to(DEV), None, 1.0)
+    torch.cuda.synchronize()
+    r = oracle.distill_fwd_bwd(z, zt, None, 1.0)
+    assert o["n_valid"].item() == r["n_valid"] == T
+    check_loss(o["loss"].item(), r["loss"])
+    check_loss(o["kl"].item(), r["kl"], "kl", rel=5e-4)
+    check(o["dlogits"].cpu(), r["dlogits"], dtype, "dlogits")
+    if V == 1:
+        assert abs(o["loss"].item()) <= 1e-6 and abs(o["kl"].item()) <= 1e-6
+        assert o["dlogits"].cpu().float().abs().max().item() <= 1e-7
