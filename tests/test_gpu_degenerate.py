@@ -115,10 +115,10 @@ def test_xent_one_and_two_classes(gpu, dtype, V):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [1, 2, 3])
 def test_layernorm_tiny_rows(gpu, dtype, d):
-    # d 1: the centred row is exactly zero, so y = b exactly, while dx is the difference
-    # of r g and r mean(g), zero up to the fp32 rounding of those two terms (the
-    # reference is identically zero, so the one-rounding bound, relative to the
-    # reference, does not apply there); eps 0.5 as for RMSNorm above
+    # d 1: the centred row is exactly zero, so y = b exactly, while dx = r g - r mean(g)
+    # is evaluated as fma(r, g, -c) with c the rounded r mean(g): the rounding error of
+    # c, not zero (the reference is identically zero, so the one-rounding bound, relative
+    # to the reference, does not apply there); eps 0.5 as for RMSNorm above
     T, eps = 19, 0.5
     td = synth.torch_dtype(dtype)
     x, dy = randn((T, d), d + 7, dtype), randn((T, d), d + 107, dtype)
