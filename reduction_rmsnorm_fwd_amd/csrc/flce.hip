@@ -19,14 +19,14 @@
 //                               counted once over all T targets up front
 //   3. dH_c = dZ_c W            bf16 MFMA reading W as it is stored ([V, H]: k-major
 //                               for this product), bf16 out
-//   4. dW (+)= dZ_g^T H_g       bf16 MFMA reading dZ and H as stored (token-major:
-//                               k-major for this product) over a group of chunks whose
-//                               dZ rows sit together in one buffer (at most four
-//                               chunks within kDzBudget: all four of an 8192-token
-//                               batch with a 128K vocabulary), fp32 accumulation
-//                               across groups in dW (or a workspace buffer, cast to
-//                               bf16 once at the end); one group means dW is written
-//                               once, never read
+//   4. dW (+)= dZ_c^T H_c       bf16 MFMA reading dZ and H as stored (token-major:
+//                               k-major for this product), fp32 accumulation across
+//                               chunks in dW (or a workspace buffer, cast to bf16
+//                               once at the end): the first chunk's product writes
+//                               dW, each later one loads the dW tile into its
+//                               accumulators and writes the sum back
+// The workspace holds one chunk's bf16 dZ rows ([C, V]), so it grows with the chunk,
+// never with T * V.
 // The k-major operands go through LDS untransposed and are read with the transposing
 // LDS loads of gfx950, so no operand is ever transposed in memory.
 // Rows whose target is ignored (or out of range) contribute nothing, so the valid rows
@@ -41,15 +41,9 @@ namespace fo {
 namespace {
 
 constexpr int64_t kAutoChunk = 2048;
-// a dW product covers a group of at most kMaxGroup chunks whose bf16 dZ rows take at
-// most kDzBudget bytes (so the dZ buffer scales with the chunk size the caller picks)
-constexpr int64_t kMaxGroup = 4;
-constexpr int64_t kDzBudget = (int64_t)2 << 30;
 
 struct Layout {
   int64_t C, Vpad;
-  int64_t group;    // chunks per dW product
-  int64_t dzrows;   // rows of the dZ buffer (group chunks)
   int64_t nparts;   // logsumexp partials per logits row
   int64_t dh_smax;  // split-K slice bound of the dH product (1: no split)
   size_t off_cnt, off_loss, off_z, off_dz, off_dw, off_part, off_stats, off_idx,
@@ -62,26 +56,25 @@ Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
   if (C > T) C = T > 0 ? T : 1;
   L.C = C;
   L.Vpad = align_up((size_t)V, 64);
-  const int64_t nchunks = T > C ? ceil_div(T, C) : 1;
-  int64_t fit = kDzBudget / (C * L.Vpad * 2);
-  fit = fit < kMaxGroup ? (fit > 1 ? fit : 1) : kMaxGroup;
-  L.group = nchunks < fit ? nchunks : fit;
-  L.dzrows = L.group * C;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
   L.off_cnt = take(256);
   L.off_loss = take((size_t)(T > 0 ? T : 1) * 4);
   L.off_z = take((size_t)(T > 0 ? T : 1) * 4);
-  L.off_dz = take((size_t)L.dzrows * L.Vpad * 2);
+  L.off_dz = take((size_t)C * L.Vpad * 2);
   L.off_dw = take(dw_dtype == FO_BF16 ? (size_t)V * H * 4 : 0);
   // dH of a chunk has few 256x256 tiles: split it over the vocabulary, the slice count
-  // chosen on the device from the chunk's valid rows (at most 8, each >= 2048 deep)
+  // chosen on the device from the chunk's valid rows (at most 8, each >= 2048 deep);
+  // the partials are packed, so the buffer holds the largest slices x rows product
+  // any row count up to C can choose
   L.dh_smax = 1;
   if (gemm::split_plan(C, H, L.Vpad).splits > 1) {
     L.dh_smax = L.Vpad / 2048 < 8 ? L.Vpad / 2048 : 8;
     if (L.dh_smax < 1) L.dh_smax = 1;
   }
-  L.off_part = take(L.dh_smax > 1 ? (size_t)L.dh_smax * C * H * 4 : 0);
+  L.off_part = take(L.dh_smax > 1
+                        ? (size_t)gemm::split_rows_bound(C, H, L.Vpad, L.dh_smax) * H * 4
+                        : 0);
   const size_t Tn = (size_t)(T > 0 ? T : 1);
   L.nparts = ceil_div(V, gemm::kStatsCols);
   L.off_stats = take((size_t)C * L.nparts * 8);
@@ -206,7 +199,7 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
   float* row_loss = reinterpret_cast<float*>(ws + L.off_loss);
   float* row_z = reinterpret_cast<float*>(ws + L.off_z);
   float* zy = reinterpret_cast<float*>(ws + L.off_zy);
-  bf16* dZbuf = reinterpret_cast<bf16*>(ws + L.off_dz);
+  bf16* dZ = reinterpret_cast<bf16*>(ws + L.off_dz);
   int* idx = reinterpret_cast<int*>(ws + L.off_idx);
   int* pos_of = reinterpret_cast<int*>(ws + L.off_pos);
   int64_t* tgv = reinterpret_cast<int64_t*>(ws + L.off_tgv);
@@ -223,11 +216,6 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
     const bool need_grad = dH != nullptr || dW != nullptr;
     for (int64_t c0 = 0; c0 < T; c0 += L.C) {
       const int64_t cl = (T - c0 < L.C) ? T - c0 : L.C;  // rows at most (valid rows: on device)
-      // the chunks of a group share the dZ buffer, chunk s of the group in rows
-      // [sC, (s+1)C), so the group's dZ rows are contiguous for dW
-      const int64_t slot = (c0 / L.C) % L.group;
-      const int64_t koff = slot * L.C;
-      bf16* dZ = dZbuf + koff * L.Vpad;
       // 1. logits of the chunk's valid rows: row partials, target logits and (gradient
       //    wanted) exp(z - m) in the chunk's dZ rows
       gemm::Args g;
@@ -257,29 +245,28 @@ int flce_impl(int64_t T, int64_t H, int64_t V, const bf16* Hm, const bf16* W,
         if (L.dh_smax > 1) {
           float* part = reinterpret_cast<float*>(ws + L.off_part);
           h.C = part; h.ldc = H;
-          h.split_max = L.dh_smax; h.c_split = cl * H;
+          h.split_max = L.dh_smax; h.split_compact = true;
           FO_HIP((gemm::run<gemm::kStoreF32, false, true>(h, gemm::kWide, st)));
           gemm::reduce_splits_bf16<<<2048, 256, 0, st>>>(part, L.dh_smax, cl * H, H,
                                                          dHv + c0 * H, H, nv, c0, L.Vpad,
-                                                         L.dh_smax);
+                                                         L.dh_smax, true);
           FO_HIP(hipGetLastError());
         } else {
           h.C = dHv + c0 * H; h.ldc = H;
           FO_HIP((gemm::run<gemm::kStoreBF16, false, true>(h, gemm::kNarrow, st)));
         }
       }
-      // 4. dW contribution of the group's rows, once all its chunks are in (or at
-      //    the end): dZ^T Hv with both operands read k-major (token-major as stored),
-      //    K = the valid rows since the group's first row, read on the device.
-      if (dW != nullptr && (slot == L.group - 1 || c0 + L.C >= T)) {
-        const int64_t base = c0 - koff;
+      // 4. dW contribution of the chunk's rows: dZ_c^T Hv_c with both operands read
+      //    k-major (token-major as stored), K = the chunk's valid rows, read on the
+      //    device.  The first chunk writes dW, later ones accumulate into it.
+      if (dW != nullptr) {
         gemm::Args w;
-        w.A = dZbuf; w.lda = L.Vpad;
-        w.B = Hv + base * H; w.ldb = H;
+        w.A = dZ; w.lda = L.Vpad;
+        w.B = Hv + c0 * H; w.ldb = H;
         w.C = dW32; w.ldc = H;
-        w.M = V; w.N = H; w.K = koff + cl;
-        w.dev_count = nv; w.count_base = base; w.dev_dim = 2;
-        if (base == 0) FO_HIP((gemm::run<gemm::kStoreF32, true, true>(w, gemm::kWide, st)));
+        w.M = V; w.N = H; w.K = cl;
+        w.dev_count = nv; w.count_base = c0; w.dev_dim = 2;
+        if (c0 == 0) FO_HIP((gemm::run<gemm::kStoreF32, true, true>(w, gemm::kWide, st)));
         else FO_HIP((gemm::run<gemm::kAccumF32, true, true>(w, gemm::kWide, st)));
       }
     }

@@ -51,9 +51,12 @@ struct Args {
   int64_t M, N, K;
   int64_t lda, ldb, ldc;
   // split-K: slice y covers the K range [y*k_split, (y+1)*k_split) and writes its
-  // fp32 partial at C + y*c_split (elements); k_split = 0: no split
+  // fp32 partial at C + y*c_split (elements); k_split = 0: no split.  split_compact:
+  // the partials are packed, slice y at C + y*M*ldc for the effective M (so a buffer
+  // for the largest slices x rows product the device may choose is enough)
   int64_t k_split = 0;
   int64_t c_split = 0;
+  bool split_compact = false;
   // device-side extent: when dev_count is set, the effective M (dev_dim 1) or K
   // (dev_dim 2) is clamp(*dev_count - count_base, 0, M or K), K rounded up to 64 (the
   // operands hold zeros up to that point).  The grid stays sized for the static M;
@@ -142,7 +145,7 @@ __device__ __forceinline__ bool locate(const Args& in, Args& a, int64_t& om, int
     a.B += BT ? kb * in.ldb : kb;
     a.K = (a.K - kb < ks) ? a.K - kb : ks;
     a.b_rows = a.b_rows - kb < 0 ? 0 : (a.b_rows - kb < a.K ? a.b_rows - kb : a.K);
-    a.C = static_cast<float*>(in.C) + sl * in.c_split;
+    a.C = static_cast<float*>(in.C) + sl * (in.split_compact ? a.M * in.ldc : in.c_split);
   }
   return true;
 }
@@ -831,16 +834,32 @@ inline SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
   return {ceil_div(K, ks), ks};
 }
 
+// Largest (slice count x rows) a product of at most M rows (N columns, K deep, at most
+// smax slices, dyn_splits on the device) can choose: the rows of a packed partial
+// buffer (Args::split_compact).  dyn_splits depends on M only through its 256-row tile
+// count, so the largest M of each tile count is the worst case.
+inline int64_t split_rows_bound(int64_t M, int64_t N, int64_t K, int64_t smax) {
+  int64_t worst = 0;
+  for (int64_t m = 256; m < M + 256; m += 256) {
+    const int64_t rows = m < M ? m : M;
+    const int64_t s = dyn_splits(rows, N, K, smax);
+    if (s * rows > worst) worst = s * rows;
+  }
+  return worst;
+}
+
 // out[m, n] = bf16(sum_s part[s, m, n]) summed in the order s = 0, 1, ...
 // (dev_rows: only rows m < *dev_rows - rows_base exist; split_max > 0: the slice count
-// is dyn_splits of those rows, as the product chose it, for a K-deep product.)
+// is dyn_splits of those rows, as the product chose it, for a K-deep product;
+// compact: the partials are packed, slice s at part + s * rows * N for the rows that
+// exist, as the product wrote them with Args::split_compact.)
 __global__ __launch_bounds__(256) void reduce_splits_bf16(const float* __restrict__ part,
                                                           int64_t splits, int64_t MN,
                                                           int64_t N, bf16* __restrict__ out,
                                                           int64_t ldo,
                                                           const long long* dev_rows,
                                                           int64_t rows_base, int64_t K,
-                                                          int64_t split_max) {
+                                                          int64_t split_max, bool compact) {
   int64_t len = MN;  // elements to reduce; MN stays the stride between partials
   if (dev_rows != nullptr) {
     int64_t eff = *dev_rows - rows_base;
@@ -848,12 +867,13 @@ __global__ __launch_bounds__(256) void reduce_splits_bf16(const float* __restric
     if (eff * N < len) len = eff * N;
   }
   if (split_max > 0) splits = ceil_div(K, split_len(K, dyn_splits(len / N, N, K, split_max)));
+  const int64_t stride = compact ? len : MN;
   for (int64_t e4 = (int64_t)blockIdx.x * 256 + threadIdx.x; e4 * 4 < len;
        e4 += (int64_t)gridDim.x * 256) {
     const int64_t e = e4 * 4;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     for (int64_t s = 0; s < splits; ++s) {
-      const float4 p = *reinterpret_cast<const float4*>(part + s * MN + e);
+      const float4 p = *reinterpret_cast<const float4*>(part + s * stride + e);
       v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
     }
 #pragma unroll

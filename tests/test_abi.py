@@ -192,6 +192,24 @@ def test_flce_validation(lib):
     assert call(a17=-1) == SHAPE
 
 
+def test_flce_workspace_bounded_by_chunk(lib):
+    # the fused linear cross-entropy exists so that the [T, V] logits never exist in
+    # memory ("Kernels（自定义内核）", section Liger): at the lm-head workload (T 8192,
+    # H 4096, V 128256) its whole workspace stays under half of the bf16 logits, and it
+    # grows with the chunk, not with T * V
+    T, H, V = 8192, 4096, 128256
+    logits_bf16 = T * V * 2
+    ws = lib.fo_flce_workspace(T, H, V, 0, F32)
+    assert 0 < ws <= logits_bf16 // 2, (ws, logits_bf16)
+    # doubling T adds per-token rows (hidden copies, statistics), not logits rows
+    ws2 = lib.fo_flce_workspace(2 * T, H, V, 0, F32)
+    assert ws2 - ws <= T * (2 * H * 2 + 64)
+    # a smaller chunk needs less: the dZ rows scale with the chunk
+    assert lib.fo_flce_workspace(T, H, V, 1024, F32) < ws - 1024 * V * 2
+    # a bf16 dweight adds exactly its fp32 accumulator (V x H), nothing per token
+    assert lib.fo_flce_workspace(T, H, V, 0, BF16) - ws <= V * H * 4 + 256
+
+
 def test_adamw_validation(lib):
     f = lib.fo_adamw_step
     i64 = ctypes.c_int64
