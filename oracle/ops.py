@@ -332,11 +332,16 @@ def distill_fwd_bwd(logits, teacher, row_mask=None, dloss=1.0):
 # it does not change the result beyond fp64 summation order.
 # ---------------------------------------------------------------------------
 def flce_fwd_bwd(hidden, weight, targets, ignore_index=-100, z_loss=0.0, dloss=1.0,
-                 chunk=None, dh_rows=None, dw_rows=None):
+                 chunk=None, dh_rows=None, dw_rows=None, n_norm=None, abs_products=False):
     """Returns dict(loss, z_loss, n_valid, n_bad, dhidden, dweight).
 
     dh_rows / dw_rows: optional index arrays; when given only those rows of dH
-    ([len, H]) and of dW ([len, H]) are formed (for sampled checks at large sizes)."""
+    ([len, H]) and of dW ([len, H]) are formed (for sampled checks at large sizes).
+    n_norm: the N that the mean and the gradient scale divide by, when these rows are
+    one block of a larger batch (default: this call's valid count); the block results
+    then add up to the batch's.
+    abs_products: also return dhidden_abs = |dZ| |W| and dweight_abs = |dZ|^T |H| for
+    the same rows (the scale of each output's rounding errors, for error bounds)."""
     Hm = _f64(hidden)
     W = _f64(weight)
     tg = _i64(targets)
@@ -344,28 +349,39 @@ def flce_fwd_bwd(hidden, weight, targets, ignore_index=-100, z_loss=0.0, dloss=1
     V = W.shape[0]
     valid, bad = _valid_mask(tg, V, ignore_index)
     n = int(valid.sum())
+    nn = n if n_norm is None else int(n_norm)
     chunk = T if chunk is None else int(chunk)
     want_dh = np.arange(T) if dh_rows is None else np.asarray(dh_rows)
     want_dw = None if dw_rows is None else np.asarray(dw_rows)
     dH = np.zeros((len(want_dh), Hm.shape[1]))
     dW = np.zeros((V if want_dw is None else len(want_dw), Hm.shape[1]))
+    dH_abs = np.zeros_like(dH) if abs_products else None
+    dW_abs = np.zeros_like(dW) if abs_products else None
     loss_sum = 0.0
     z_sum = 0.0
     pos_in_dh = {int(r): i for i, r in enumerate(want_dh)}
     for c0 in range(0, T, chunk):
         c1 = min(T, c0 + chunk)
         Z = Hm[c0:c1] @ W.T
-        lr, zt, _, dZ = xent_rows(Z, tg[c0:c1], valid[c0:c1], n, z_loss, dloss)
+        lr, zt, _, dZ = xent_rows(Z, tg[c0:c1], valid[c0:c1], nn, z_loss, dloss)
         loss_sum += lr.sum()
         z_sum += zt.sum()
         rows = [r for r in range(c0, c1) if r in pos_in_dh]
         if rows:
-            dH[[pos_in_dh[r] for r in rows]] = dZ[np.array(rows) - c0] @ W
+            sel = np.array(rows) - c0
+            dH[[pos_in_dh[r] for r in rows]] = dZ[sel] @ W
+            if abs_products:
+                dH_abs[[pos_in_dh[r] for r in rows]] = np.abs(dZ[sel]) @ np.abs(W)
         dZ_sel = dZ if want_dw is None else dZ[:, want_dw]
         dW += dZ_sel.T @ Hm[c0:c1]
-    return dict(loss=float(loss_sum / n) if n else 0.0,
-                z_loss=float(z_sum / n) if n else 0.0,
-                n_valid=n, n_bad=int(bad.sum()), dhidden=dH, dweight=dW)
+        if abs_products:
+            dW_abs += np.abs(dZ_sel).T @ np.abs(Hm[c0:c1])
+    out = dict(loss=float(loss_sum / nn) if nn else 0.0,
+               z_loss=float(z_sum / nn) if nn else 0.0,
+               n_valid=n, n_bad=int(bad.sum()), dhidden=dH, dweight=dW)
+    if abs_products:
+        out.update(dhidden_abs=dH_abs, dweight_abs=dW_abs)
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -105,3 +105,54 @@ def test_equals_xent_of_the_product():
     b = oracle.xent_fwd_bwd(Hm @ W.T, t, z_loss=1e-3)
     assert abs(a["loss"] - b["loss"]) < 1e-14
     assert np.max(np.abs(a["dhidden"] - b["dlogits"] @ W)) < 1e-14
+
+
+def test_row_blocks_with_the_batch_normaliser_add_up_to_the_batch():
+    # rows are independent once N is fixed: blocks normalised by the batch's N sum to
+    # the batch's loss and dW, and give the batch's dH rows (the full-size GPU parity
+    # test maps blocks over threads this way)
+    r = rng(5)
+    T, Hd, V, c = 17, 6, 13, 1e-3
+    Hm = r.standard_normal((T, Hd))
+    W = r.standard_normal((V, Hd)) * 0.4
+    t = r.integers(0, V, T)
+    t[[1, 8, 9]] = IGN
+    a = oracle.flce_fwd_bwd(Hm, W, t, z_loss=c, dloss=0.7)
+    N = a["n_valid"]
+    loss = zl = 0.0
+    dW = np.zeros_like(a["dweight"])
+    for b0 in (0, 5, 11):
+        b1 = {0: 5, 5: 11, 11: T}[b0]
+        b = oracle.flce_fwd_bwd(Hm[b0:b1], W, t[b0:b1], z_loss=c, dloss=0.7, n_norm=N)
+        loss += b["loss"]
+        zl += b["z_loss"]
+        dW += b["dweight"]
+        assert np.max(np.abs(b["dhidden"] - a["dhidden"][b0:b1])) < 1e-15
+    assert abs(loss - a["loss"]) < 1e-13 and abs(zl - a["z_loss"]) < 1e-15
+    assert np.max(np.abs(dW - a["dweight"])) < 1e-14
+
+
+def test_abs_products_brute_force():
+    # dhidden_abs[i, j] = sum_v |dZ[i, v]| |W[v, j]| and dweight_abs[v, j] =
+    # sum_i |dZ[i, v]| |H[i, j]|, written out element by element from the logit gradient
+    # of the plain cross-entropy of the product
+    r = rng(6)
+    T, Hd, V = 4, 3, 5
+    Hm = r.standard_normal((T, Hd))
+    W = r.standard_normal((V, Hd))
+    t = np.array([4, IGN, 0, 2])
+    out = oracle.flce_fwd_bwd(Hm, W, t, z_loss=1e-2, abs_products=True,
+                              dh_rows=np.array([2, 0]), dw_rows=np.array([1, 4]))
+    Z = [[sum(Hm[i, k] * W[v, k] for k in range(Hd)) for v in range(V)] for i in range(T)]
+    dZ = oracle.xent_fwd_bwd(np.array(Z), t, z_loss=1e-2)["dlogits"]
+    for a, i in enumerate((2, 0)):
+        for j in range(Hd):
+            e = sum(abs(dZ[i, v]) * abs(W[v, j]) for v in range(V))
+            assert abs(out["dhidden_abs"][a, j] - e) < 1e-15
+    for a, v in enumerate((1, 4)):
+        for j in range(Hd):
+            e = sum(abs(dZ[i, v]) * abs(Hm[i, j]) for i in range(T))
+            assert abs(out["dweight_abs"][a, j] - e) < 1e-15
+    # and the products bound the gradients themselves (triangle inequality)
+    assert np.all(np.abs(out["dhidden"]) <= out["dhidden_abs"] + 1e-15)
+    assert np.all(np.abs(out["dweight"]) <= out["dweight_abs"] + 1e-15)

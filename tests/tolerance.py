@@ -18,6 +18,23 @@ much tighter check
 
 (half a bf16 ulp is at most 2^-8 |r|; 3e-5 |r| covers the fp32 arithmetic before the
 rounding; the rms floor covers cancellation in the fp32 arithmetic).
+
+The fused linear cross-entropy's weight and hidden gradients are products dZ X of the
+logit gradient with an exact bf16 operand X (W for dH, H for dW).  The kernel's dZ
+carries two bf16 roundings (exp(z - m) stored in bf16, then dZ itself), each at most
+2^-8 relative, so it is within (2^-7 + 2^-16) |dz| of the exact one; the fp32 logits,
+logsumexp and accumulation add far less than 2^-9 relative (fp32 sums of a few
+thousand terms).  Hence, elementwise, with A = |dz| |X| the product of the absolute
+values (the oracle returns it):
+
+  product gradient:  |g - r| <= (2^-7 + 2^-9) A + [output rounded to bf16] (2^-8 + 3e-5) |r|
+                                + 1e-6 rms(A)
+
+The distillation gradient dz = s (q - p) (s = dloss/N) is the difference of two fp32
+softmax values, each within a few 1e-6 relative of the exact one (fp32 exponentials of
+arguments up to ~40 in size, fp32 logsumexps), then rounded once:
+
+  softmax difference:  |g - r| <= [bf16] (2^-8 + 3e-5) |r| + 1e-5 |s| (q + p)
 """
 from __future__ import annotations
 
@@ -53,6 +70,32 @@ def check_bf16(g, r, name="out", single_rounding=False):
         b2 = (2.0 ** -8 + 3e-5) * np.abs(r) + 1e-5 * rms
         assert np.all(d <= b2), _report(name + " [bf16 single rounding]", d > b2, g, r, b2)
     return float(np.max(d)) if d.size else 0.0
+
+
+def check_product_grad(g, r, absprod, name="out", rounded_out=True):
+    g, r, a = _np(g), _np(r), _np(absprod)
+    assert g.shape == r.shape == a.shape, (name, g.shape, r.shape, a.shape)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite GPU output"
+    if not r.size:
+        return 0.0
+    d = np.abs(g - r)
+    bound = (2.0 ** -7 + 2.0 ** -9) * a + 1e-6 * np.sqrt(np.mean(a * a))
+    if rounded_out:
+        bound = bound + (2.0 ** -8 + 3e-5) * np.abs(r)
+    assert np.all(d <= bound), _report(name + " [product of rounded dZ]", d > bound, g, r, bound)
+    return float(np.max(d / np.where(bound > 0, bound, 1.0)))
+
+
+def check_softmax_diff(g, r, qp_scaled, name="out", rounded_out=True):
+    g, r, a = _np(g), _np(r), _np(qp_scaled)
+    assert g.shape == r.shape == a.shape, (name, g.shape, r.shape, a.shape)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite GPU output"
+    if not r.size:
+        return 0.0
+    d = np.abs(g - r)
+    bound = 1e-5 * np.abs(a) + (2.0 ** -8 + 3e-5 if rounded_out else 2.0 ** -23) * np.abs(r)
+    assert np.all(d <= bound), _report(name + " [softmax difference]", d > bound, g, r, bound)
+    return float(np.max(d / np.where(bound > 0, bound, 1.0)))
 
 
 def check_f32(g, r, name="out", rel=1e-5):
