@@ -42,6 +42,14 @@ def test_configs_small(gpu, cid, T):
     compare(i["x"], i["w"], i["dy"], cfg.eps, cfg.dtype, got2)
 
 
+def test_config1_as_stated(gpu):
+    # the tiny fp32 block at its stated size: T 256, d 512, eps 1e-6, every row
+    cfg = synth.CONFIGS[1]
+    assert cfg.T == 256 and cfg.dtype == "f32"
+    i = synth.rmsnorm_inputs(cfg)
+    compare(i["x"], i["w"], i["dy"], cfg.eps, cfg.dtype, run(gpu, i["x"], i["w"], i["dy"], cfg.eps))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [13, 1000, 1025, 2049, 4097, 8, 8193, 12288])
 def test_unaligned_and_wide_rows(gpu, dtype, d):

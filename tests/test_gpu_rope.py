@@ -39,6 +39,22 @@ def test_configs_small(gpu, cid, T):
     check(bk, ok, cfg.dtype, "dk", single_rounding=True)
 
 
+def test_config1_as_stated(gpu):
+    # the tiny fp32 block at its stated size: T 256 with positions 0..255, 8 Q / 8 KV
+    # heads of 64, theta 1e4, forward and backward over every token
+    cfg = synth.CONFIGS[1]
+    i = synth.rope_inputs(cfg)
+    assert cfg.T == 256 and torch.equal(i["pos"], torch.arange(256))
+    gq, gk = gpu_rope(gpu, i["q"], i["k"], i["pos"], cfg.theta)
+    rq, rk = oracle.rope_fwd(i["q"], i["k"], i["pos"], cfg.theta)
+    check(gq, rq, "f32", "q")
+    check(gk, rk, "f32", "k")
+    bq, bk = gpu_rope(gpu, i["dq"], i["dk"], i["pos"], cfg.theta, bwd=True)
+    oq, ok = oracle.rope_bwd(i["dq"], i["dk"], i["pos"], cfg.theta)
+    check(bq, oq, "f32", "dq")
+    check(bk, ok, "f32", "dk")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_long_positions_fp32_precision(gpu, dtype):
     # positions up to 16383 and beyond: an fp32 angle would be off by ~1e-3 rad here

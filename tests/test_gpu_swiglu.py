@@ -35,6 +35,14 @@ def test_configs_small(gpu, cid, T):
     compare(i["gate"], i["up"], i["dh"], cfg.dtype, run(gpu, i["gate"], i["up"], i["dh"]))
 
 
+def test_config1_as_stated(gpu):
+    # the tiny fp32 block at its stated size: T 256, F 1408, every element
+    cfg = synth.CONFIGS[1]
+    assert cfg.T == 256
+    i = synth.swiglu_inputs(cfg)
+    compare(i["gate"], i["up"], i["dh"], cfg.dtype, run(gpu, i["gate"], i["up"], i["dh"]))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("F", [1409, 7, 8, 513])
 def test_unaligned_widths(gpu, dtype, F):

@@ -6,6 +6,7 @@ import torch
 
 import oracle
 from reduction_rmsnorm_fwd_amd import synth
+from blockwise import map_blocks
 from tolerance import check, check_loss
 
 pytestmark = pytest.mark.gpu
@@ -41,6 +42,16 @@ def test_configs_small(gpu, cid, T):
         t = t.clone()
         t[::4] = IGN
     compare(i["logits"], t, cfg.z_loss, cfg.dtype, run(gpu, i["logits"], t, cfg.z_loss))
+
+
+def test_config1_as_stated(gpu):
+    # the tiny fp32 block at its stated size: T 256 logits over 4096 classes, N(0, 2^2),
+    # uniform targets, every row
+    cfg = synth.CONFIGS[1]
+    assert cfg.T == 256 and cfg.V == 4096
+    i = synth.xent_inputs(cfg)
+    compare(i["logits"], i["targets"], cfg.z_loss, cfg.dtype,
+            run(gpu, i["logits"], i["targets"], cfg.z_loss))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -152,13 +163,21 @@ def test_full_size(gpu, cid):
     ign = (t == IGN).nonzero().flatten()
     if len(ign):
         assert torch.all(o["dlogits"][ign[:64]].view(torch.int16) == 0)
-    # the loss needs every row: oracle in row blocks
-    if cid == 3:
-        tot = 0.0
-        for r0 in range(0, cfg.T, 512):
-            b = oracle.xent_fwd_bwd(z[r0:r0 + 512], t[r0:r0 + 512], IGN, cfg.z_loss, 1.0)
-            tot += b["loss"] * b["n_valid"]
-        check_loss(o["loss"].item(), tot / n_full)
+    # the loss needs every row: the oracle over row blocks (each block's mean times its
+    # valid count), on a thread pool
+    check_losses_full(o, z, t, cfg.z_loss, n_full)
+
+
+def check_losses_full(o, z, t, zc, n_full):
+    def one(r0, r1):
+        b = oracle.xent_fwd_bwd(z[r0:r1], t[r0:r1], IGN, zc, 1.0)
+        return b["loss"] * b["n_valid"], b["z_loss"] * b["n_valid"], b["n_valid"], b["n_bad"]
+
+    parts = map_blocks(one, z.shape[0], 256)
+    assert sum(p[2] for p in parts) == n_full
+    check_loss(o["loss"].item(), sum(p[0] for p in parts) / n_full)
+    check_loss(o["z_loss"].item(), sum(p[1] for p in parts) / n_full, "z_loss")
+    assert o["status"].item() == sum(p[3] for p in parts)
 
 
 def test_unaligned_full_size(gpu):
@@ -177,9 +196,4 @@ def test_unaligned_full_size(gpu):
     _, _, _, dz = oracle.xent_rows(z[rows].double().numpy(), tg, valid, n_full, cfg.z_loss, 1.0)
     check(o["dlogits"][rows], dz, cfg.dtype, "dlogits", single_rounding=True)
     assert o["n_valid"].item() == n_full
-    tot = 0.0
-    for r0 in range(0, cfg.T, 512):
-        b = oracle.xent_fwd_bwd(z[r0:r0 + 512], t[r0:r0 + 512], IGN, cfg.z_loss, 1.0)
-        tot += b["loss"] * b["n_valid"]
-    check_loss(o["loss"].item(), tot / n_full)
-
+    check_losses_full(o, z, t, cfg.z_loss, n_full)
