@@ -6,10 +6,13 @@
 // softmax against the teacher's (temperature 1), over the rows a mask keeps:
 //   q = softmax(z), p = softmax(zt) per row;  loss = (1/N) sum_t -sum_v p log q,
 //   kl = (1/N) sum_t sum_v p (log p - log q),  dz = dloss (q - p) / N.
-// Per row, one sweep gives both online logsumexps and the two p-weighted sums
-//   A = sum_v exp(zt - m_t) z,  B = sum_v exp(zt - m_t) zt   (rescaled with m_t),
-// so -sum p log q = lse_z - A/s_t and -sum p log p = lse_t - B/s_t; a second sweep over
-// the same values writes dz.  For rows of up to 16 K vectors both rows stay on chip
+// Per row, one sweep gives both online logsumexps (m_z, s_z), (m_t, s_t) and the two
+// p-weighted sums
+//   A = sum_v exp(zt - m_t) z,  D = sum_v exp(zt - m_t) (zt - z)   (rescaled with m_t),
+// so -sum p log q = lse_z - A/s_t, and the KL, sum p (zt - z) + lse_z - lse_t, is
+// D/s_t + (m_z - m_t) + log(s_z/s_t): a sum of terms of the size of the KL itself,
+// where the difference of the two cross-entropies would cancel two logsumexp-sized
+// values.  A second sweep over the same values writes dz.  For rows of up to 16 K vectors both rows stay on chip
 // between the sweeps: the student row in VGPRs, the teacher row in VGPRs and (for the
 // longest rows) LDS, filled by buffer loads that write LDS directly; so HBM sees each
 // input once and dz once (3 T V b).  Longer or unaligned rows re-read both rows in the
@@ -28,13 +31,13 @@ typedef unsigned int v4u32_t __attribute__((ext_vector_type(4)));
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
 
 // Per-thread (then per-row) state of the sweep: student (ms, ss), teacher (mt, st) and
-// the teacher-weighted sums A (of z) and B (of zt), all relative to mt.
+// the teacher-weighted sums A (of z) and D (of zt - z), all relative to mt.
 struct Stats {
-  float ms, ss, mt, st, a, b;
+  float ms, ss, mt, st, a, d;
 };
 
 __device__ __forceinline__ void stats_init(Stats& s) {
-  s.ms = -INFINITY; s.ss = 0.f; s.mt = -INFINITY; s.st = 0.f; s.a = 0.f; s.b = 0.f;
+  s.ms = -INFINITY; s.ss = 0.f; s.mt = -INFINITY; s.st = 0.f; s.a = 0.f; s.d = 0.f;
 }
 
 __device__ __forceinline__ void stats_merge(Stats& s, const Stats& o) {
@@ -44,7 +47,7 @@ __device__ __forceinline__ void stats_merge(Stats& s, const Stats& o) {
   const float f1 = __expf(s.mt - m), f2 = __expf(o.mt - m);
   s.st = s.st * f1 + o.st * f2;
   s.a = s.a * f1 + o.a * f2;
-  s.b = s.b * f1 + o.b * f2;
+  s.d = s.d * f1 + o.d * f2;
   s.mt = m;
 }
 
@@ -52,7 +55,7 @@ __device__ __forceinline__ void stats_merge(Stats& s, const Stats& o) {
 // (exponentials: accurate for fp32 rows, the hardware path for bf16 rows, as the
 // hard-label kernels)
 // PAD: some values are -inf padding (both z and t) past the end of the row; a zero
-// teacher weight then contributes nothing to A and B (plain fmaf would give 0 * -inf).
+// teacher weight then contributes nothing to A and D (plain fmaf would give 0 * -inf).
 template <typename T, int VEC, bool PAD = false>
 __device__ __forceinline__ void stats_add(Stats& s, const float* z, const float* t) {
   float vz = z[0], vt = t[0];
@@ -61,7 +64,7 @@ __device__ __forceinline__ void stats_add(Stats& s, const float* z, const float*
   if (vz > s.ms) { s.ss *= xent::ex<T>(s.ms - vz); s.ms = vz; }
   if (vt > s.mt) {
     const float f = xent::ex<T>(s.mt - vt);
-    s.st *= f; s.a *= f; s.b *= f; s.mt = vt;
+    s.st *= f; s.a *= f; s.d *= f; s.mt = vt;
   }
 #pragma unroll
   for (int j = 0; j < VEC; ++j) {
@@ -70,7 +73,7 @@ __device__ __forceinline__ void stats_add(Stats& s, const float* z, const float*
     s.st += e;
     if (PAD && e == 0.f) continue;
     s.a = fmaf(e, z[j], s.a);
-    s.b = fmaf(e, t[j], s.b);
+    s.d = fmaf(e, t[j] - z[j], s.d);
   }
 }
 
@@ -82,7 +85,7 @@ __device__ __forceinline__ Stats block_stats(Stats s, Stats* sh) {
     Stats q;
     q.ms = __shfl_xor(s.ms, o, kWave); q.ss = __shfl_xor(s.ss, o, kWave);
     q.mt = __shfl_xor(s.mt, o, kWave); q.st = __shfl_xor(s.st, o, kWave);
-    q.a = __shfl_xor(s.a, o, kWave); q.b = __shfl_xor(s.b, o, kWave);
+    q.a = __shfl_xor(s.a, o, kWave); q.d = __shfl_xor(s.d, o, kWave);
     stats_merge(s, q);
   }
   const int w = threadIdx.x / kWave;
@@ -106,13 +109,11 @@ struct DistillArgs {
 // The row's loss terms from its totals (thread 0), and the logsumexps for the gradient.
 __device__ __forceinline__ void row_terms(const DistillArgs& a, int64_t row, const Stats& r,
                                           float& lse_z, float& lse_t) {
-  lse_z = r.ms + __logf(r.ss);
-  lse_t = r.mt + __logf(r.st);
+  lse_z = r.ms + logf(r.ss);
+  lse_t = r.mt + logf(r.st);
   if (threadIdx.x == 0) {
-    const float ce = lse_z - r.a / r.st;   // -sum p log q
-    const float h = lse_t - r.b / r.st;    // -sum p log p
-    a.row_ce[row] = ce;
-    a.row_kl[row] = ce - h;
+    a.row_ce[row] = lse_z - r.a / r.st;  // -sum p log q
+    a.row_kl[row] = r.d / r.st + ((r.ms - r.mt) + logf(r.ss / r.st));
   }
 }
 

@@ -115,10 +115,9 @@ def test_xent_one_and_two_classes(gpu, dtype, V):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [1, 2, 3])
 def test_layernorm_tiny_rows(gpu, dtype, d):
-    # d 1: the centred row is exactly zero, so y = b exactly, while dx = r g - r mean(g)
-    # is evaluated as fma(r, g, -c) with c the rounded r mean(g): the rounding error of
-    # c, not zero (the reference is identically zero, so the one-rounding bound, relative
-    # to the reference, does not apply there); eps 0.5 as for RMSNorm above
+    # d 1: the centred row is exactly zero, so y = b exactly; the kernels form g - mean(g)
+    # before scaling it, which is exactly 0 in a one-column row, so dx is exactly zero
+    # as the reference is; eps 0.5 as for RMSNorm above
     T, eps = 19, 0.5
     td = synth.torch_dtype(dtype)
     x, dy = randn((T, d), d + 7, dtype), randn((T, d), d + 107, dtype)
@@ -134,13 +133,12 @@ def test_layernorm_tiny_rows(gpu, dtype, d):
     check(y.cpu(), ry, dtype, "y", single_rounding=True)
     check(mean.cpu(), rmu, "f32", "mean")
     check(rstd.cpu(), rr, "f32", "rstd")
-    check(dx.cpu(), rdx, dtype, "dx", single_rounding=d > 1)
+    check(dx.cpu(), rdx, dtype, "dx", single_rounding=True)
     check(dw.cpu(), rdw, "f32", "dw")
     check(db.cpu(), rdb, "f32", "db")
     if d == 1:
         assert torch.equal(y.cpu(), b.expand(T, 1))
-        r_gw = (rr[:, None] * (w.double() * dy.double()).numpy()).__abs__().max()
-        assert dx.cpu().double().abs().max().item() <= 2 * 2.0 ** -24 * r_gw
+        assert torch.all(dx.cpu() == 0)
 
 
 @pytest.mark.parametrize("act", ["silu", "gelu", "relu"])
@@ -165,7 +163,7 @@ def test_distill_one_and_two_classes(gpu, dtype, V):
     r = oracle.distill_fwd_bwd(z, zt, None, 1.0)
     assert o["n_valid"].item() == r["n_valid"] == T
     check_loss(o["loss"].item(), r["loss"])
-    check_loss(o["kl"].item(), r["kl"], "kl", rel=5e-4)
+    check_loss(o["kl"].item(), r["kl"], "kl")
     check(o["dlogits"].cpu(), r["dlogits"], dtype, "dlogits")
     if V == 1:
         assert abs(o["loss"].item()) <= 1e-6 and abs(o["kl"].item()) <= 1e-6
