@@ -60,6 +60,14 @@ __device__ __forceinline__ void st_vec(T* p, int v, int d, const Pack<T>& o) {
   }
 }
 
+// w g - m with the product rounded before the subtraction (no fused multiply-add), as
+// the row sum that m is the mean of rounds each w g: where every w g of a row equals m
+// (a one-column row) the result is exactly 0 rather than the product's rounding error.
+__device__ __forceinline__ float centred(float w, float g, float m) {
+#pragma clang fp contract(off)
+  return w * g - m;
+}
+
 // ----------------------------------------------------------------- forward, fast
 // LN: LayerNorm (mean subtracted before the variance, bias added); the row is still
 // read once: mean and centred variance are two sweeps over the registers.
@@ -201,8 +209,10 @@ __global__ __launch_bounds__(kGenericThreads) void rmsnorm_fwd_block(
 // row per workgroup: partial[blockIdx.x, :].
 //
 // LN (LayerNorm, mean and rstd saved by the forward): with g = w*dy and xc = x - mean,
-//   dx = r g - r mean_j(g) - r^3 xc mean_j(g xc),  dw += dy xc r,  db += dy,
-// the db partials folded beside the dw partials (partial row of 2d floats).
+//   dx = r (g - mean_j(g)) - r^3 xc mean_j(g xc),  dw += dy xc r,  db += dy,
+// the db partials folded beside the dw partials (partial row of 2d floats).  g - mean(g)
+// is formed first (see centred()), so a row whose centred gradient vanishes exactly
+// (one column) gives dx exactly 0.
 template <typename T, int NV, int RW, bool LN, bool UA>
 __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
     int64_t T_, int nvec, int d, const T* dy, int64_t lddy, const T* x, int64_t ldx,
@@ -297,7 +307,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
       if constexpr (LN) {
         r = rv;
         k = r * r * r * (dot * inv_d);
-        c = r * (ss * inv_d);
+        c = ss * inv_d;
       } else {
         r = rstd != nullptr ? rv : 1.0f / sqrtf(ss * inv_d + eps);
         k = r * r * r * (dot * inv_d);
@@ -313,7 +323,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
             const float gf = to_f32(gv[i].v[j]);
             if constexpr (LN) {
               const float xc = to_f32(xv[i].v[j]) - mv;
-              o.v[j] = from_f32<T>(r * (to_f32(wv[i].v[j]) * gf) - c - k * xc);
+              o.v[j] = from_f32<T>(r * centred(to_f32(wv[i].v[j]), gf, c) - k * xc);
               acc[i][j] = fmaf(gf * xc, r, acc[i][j]);
               accb[i][j] += gf;
             } else {
@@ -391,7 +401,7 @@ __global__ __launch_bounds__(kGenericThreads) void rmsnorm_bwd_dx_block(
   float r, c = 0.f;
   if constexpr (LN) {
     r = rstd[row];
-    c = r * (block_sum<kGenericThreads>(ss, sh) / (float)d);
+    c = block_sum<kGenericThreads>(ss, sh) / (float)d;
   } else if (rstd != nullptr) {
     r = rstd[row];
   } else {
@@ -404,7 +414,8 @@ __global__ __launch_bounds__(kGenericThreads) void rmsnorm_bwd_dx_block(
   // the block_sum barriers separate all reads of the dot product from these writes.
   for (int64_t j = threadIdx.x; j < d; j += kGenericThreads) {
     const float xf = to_f32(xr[j]) - mu;
-    dxr[j] = from_f32<T>(r * (to_f32(w[j]) * to_f32(dyr[j])) - c - k * xf);
+    const float gw = LN ? centred(to_f32(w[j]), to_f32(dyr[j]), c) : to_f32(w[j]) * to_f32(dyr[j]);
+    dxr[j] = from_f32<T>(r * gw - k * xf);
   }
   if constexpr (!LN) {
     if (threadIdx.x == 0) r_out[row] = r;
