@@ -196,6 +196,20 @@ int fo_xent_fwd_bwd(int dtype, int64_t T, int64_t V, const void* logits, int64_t
                     int64_t* n_valid, int32_t* status, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* fo_xent_fwd_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments and results as fo_xent_fwd_bwd.  Its workspace is a
+ * library-owned device array of fo_xent_workspace(FO_XENT_NOALLOC_MAX_T, V) bytes
+ * (8 MiB + 256), one per GPU the library runs on, held until the process ends; the
+ * call allocates nothing.  T > FO_XENT_NOALLOC_MAX_T: FO_ERR_WORKSPACE, nothing
+ * enqueued.  Every call on one GPU shares that GPU's array, so calls that overlap on
+ * one GPU (other streams, other host threads) race: serialise them. */
+#define FO_XENT_NOALLOC_MAX_T 1048576
+int fo_xent_fwd_bwd_noalloc(int dtype, int64_t T, int64_t V, const void* logits, int64_t ldl,
+                            const int64_t* targets, int64_t ignore_index, float z_loss_coef,
+                            float dloss, void* dlogits, int64_t ldd, float* loss, float* z_loss,
+                            int64_t* n_valid, int32_t* status, void* stream);
+
 /* ---- Soft-target cross-entropy / distillation ([FastLLM] 损失函数体系: label-entropy and
  * distillation losses beside the hard-label cross-entropy; read as the cross-entropy
  * of the student's softmax against the teacher's, temperature 1) ----

@@ -16,7 +16,8 @@ import os
 __all__ = [
     "load", "FoError", "FO_F32", "FO_BF16",
     "fo_rmsnorm_fwd", "fo_rmsnorm_bwd", "fo_rope_fwd", "fo_rope_bwd",
-    "fo_swiglu_fwd", "fo_swiglu_bwd", "fo_xent_fwd_bwd", "fo_flce_fwd_bwd",
+    "fo_swiglu_fwd", "fo_swiglu_bwd", "fo_xent_fwd_bwd", "fo_xent_fwd_bwd_noalloc",
+    "fo_flce_fwd_bwd",
     "fo_rmsnorm_bwd_workspace", "fo_xent_workspace", "fo_flce_workspace", "fo_adamw_step",
     "fo_layernorm_fwd", "fo_layernorm_bwd", "fo_layernorm_bwd_workspace",
     "fo_glu_fwd", "fo_glu_bwd", "fo_act_fwd", "fo_act_bwd", "ACTS",
@@ -75,6 +76,10 @@ SIGNATURES = {
                                        _c_i64, ctypes.c_float, ctypes.c_float, _c_ptr, _c_i64,
                                        _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_size_t,
                                        _c_ptr]),
+    "fo_xent_fwd_bwd_noalloc": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_i64,
+                                               _c_ptr, _c_i64, ctypes.c_float, ctypes.c_float,
+                                               _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                               _c_ptr]),
     "fo_distill_workspace": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "fo_distill_fwd_bwd": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr,
                                           _c_i64, _c_ptr, ctypes.c_float, _c_ptr, _c_i64, _c_ptr,
@@ -387,7 +392,29 @@ def fo_xent_fwd_bwd(logits, targets, ignore_index=-100, z_loss=0.0, dloss=1.0, d
     return o
 
 
-# ------------------------------------------------ fused linear cross-entropy
+def fo_xent_fwd_bwd_noalloc(logits, targets, ignore_index=-100, z_loss=0.0, dloss=1.0,
+                            dlogits=None, grad=True, out=None):
+    """fo_xent_fwd_bwd on the library's own per-device workspace (no workspace tensor;
+    the C call allocates nothing).  Outputs as fo_xent_fwd_bwd; pass dlogits and out to
+    allocate nothing on this side either."""
+    import torch
+    lib = load()
+    T, V = logits.shape
+    if grad and dlogits is None:
+        dlogits = torch.empty_like(logits)
+    if not grad:
+        dlogits = None
+    o = out if out is not None else _scalars(logits.device)
+    _check("fo_xent_fwd_bwd_noalloc", lib.fo_xent_fwd_bwd_noalloc(
+        _dt(logits), T, V, _ptr(logits), _rows(logits, "logits"), _ptr(targets),
+        int(ignore_index), float(z_loss), float(dloss), _ptr(dlogits),
+        _rows(dlogits, "dlogits") if dlogits is not None else V, _ptr(o["loss"]),
+        _ptr(o["z_loss"]), _ptr(o["n_valid"]), _ptr(o["status"]), _stream()))
+    o["dlogits"] = dlogits
+    return o
+
+
+# ------------------------------------------------ soft-target cross-entropy
 def fo_distill_workspace(T, V):
     return load_library().fo_distill_workspace(T, V)
 

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in fo.SIGNATURES, f"binding lacks {n}"
@@ -143,6 +143,23 @@ def test_xent_validation(lib):
     assert f(BF16, 16, 0, P, 100, P, -100, 0.0, 1.0, P, 100, P, N, N, N, P, ws, N) == SHAPE
     assert f(BF16, 16, 100, N, 100, P, -100, 0.0, 1.0, P, 100, P, N, N, N, P, ws, N) == NULL
     assert f(3, 16, 100, P, 100, P, -100, 0.0, 1.0, P, 100, P, N, N, N, P, ws, N) == DTYPE
+
+
+def test_xent_noalloc_validation(lib):
+    # the same checks as fo_xent_fwd_bwd, all before the library's device array is
+    # looked up; more tokens than that array holds are refused with FO_ERR_WORKSPACE
+    f = lib.fo_xent_fwd_bwd_noalloc
+    mx = 1048576
+    assert "FO_XENT_NOALLOC_MAX_T %d" % mx in open(HEADER).read()
+    assert f(BF16, 16, 100, P, 100, P, -100, 0.0, 1.0, P, 100, N, N, N, N, N) == NULL
+    assert f(BF16, 16, 100, P, 99, P, -100, 0.0, 1.0, P, 100, P, N, N, N, N) == STRIDE
+    assert f(BF16, 16, 100, P, 100, P, -100, 0.0, 1.0, P, 99, P, N, N, N, N) == STRIDE
+    assert f(BF16, 16, 0, P, 100, P, -100, 0.0, 1.0, P, 100, P, N, N, N, N) == SHAPE
+    assert f(BF16, -1, 100, P, 100, P, -100, 0.0, 1.0, P, 100, P, N, N, N, N) == SHAPE
+    assert f(3, 16, 100, P, 100, P, -100, 0.0, 1.0, P, 100, P, N, N, N, N) == DTYPE
+    assert f(BF16, mx + 1, 100, P, 100, P, -100, 0.0, 1.0, P, 100, P, N, N, N, N) == WS
+    # the array's size is the workspace query at the limit
+    assert lib.fo_xent_workspace(mx, 100) == 256 + 2 * 4 * mx
 
 
 def test_distill_validation(lib):
