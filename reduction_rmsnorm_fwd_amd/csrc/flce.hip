@@ -64,12 +64,13 @@ Layout layout(int64_t T, int64_t H, int64_t V, int64_t chunk, int dw_dtype) {
   L.off_dz = take((size_t)C * L.Vpad * 2);
   L.off_dw = take(dw_dtype == FO_BF16 ? (size_t)V * H * 4 : 0);
   // dH of a chunk has few 256x256 tiles: split it over the vocabulary, the slice count
-  // chosen on the device from the chunk's valid rows (at most 8, each >= 2048 deep);
-  // the partials are packed, so the buffer holds the largest slices x rows product
-  // any row count up to C can choose
+  // chosen on the device from the chunk's valid rows (at most 4, each >= 2048 deep:
+  // as fast as 8 at the lm-head workload, with 201 -> 67 MB of partials); the partials
+  // are packed, so the buffer holds the largest slices x rows product any row count
+  // up to C can choose
   L.dh_smax = 1;
   if (gemm::split_plan(C, H, L.Vpad).splits > 1) {
-    L.dh_smax = L.Vpad / 2048 < 8 ? L.Vpad / 2048 : 8;
+    L.dh_smax = L.Vpad / 2048 < 4 ? L.Vpad / 2048 : 4;
     if (L.dh_smax < 1) L.dh_smax = 1;
   }
   L.off_part = take(L.dh_smax > 1
