@@ -443,11 +443,19 @@ __global__ __launch_bounds__(kPfThreads) void row_pf(RowArgs a, const Tin* z, To
   wait_vm_n<0>();
 }
 
-// Streaming row kernel: any V, any alignment (VEC = 1) or aligned vectors (VEC > 1).
-// The second read of the row is a cached load (the row was just read, it is usually
-// still in L2 or the Infinity Cache).
-template <typename Tin, typename Tout, int VEC, int NT>
+// Streaming row kernel: any V, any alignment (VEC = 1) or aligned vectors (VEC > 1), for
+// rows longer than the register-resident kernels hold.  With vectors, each thread keeps
+// its first KEEP vectors of the row in registers from the first pass to the second (as
+// the register-resident kernel does with the whole row) and streams the rest twice:
+// the first pass (cached loads) gives (max, sum), the second, served mostly by L2 and
+// the Infinity Cache, re-reads only that rest to write its gradient.  Streamed vectors
+// are loaded kStreamUnroll at a time before any is used, so a wave keeps that many
+// 16-byte loads in flight, and every gradient vector goes out as one 16-byte store.
+constexpr int kStreamUnroll = 8;
+
+template <typename Tin, typename Tout, int VEC, int NT, int KEEP = 0, int U = kStreamUnroll>
 __global__ __launch_bounds__(NT) void row_stream(RowArgs a, const Tin* z, Tout* dz) {
+  static_assert(KEEP == 0 || VEC > 1, "registers hold whole vectors");
   __shared__ float shm[NT / kWave], shs[NT / kWave];
   __shared__ float sh_zy;
   const int64_t row = blockIdx.x;
@@ -464,21 +472,41 @@ __global__ __launch_bounds__(NT) void row_stream(RowArgs a, const Tin* z, Tout* 
   const int64_t nvec = a.V / VEC;  // VEC divides V on this path
   if (threadIdx.x == 0) sh_zy = to_f32(zr[y]);
   float m = -INFINITY, s = 0.f;
-  for (int64_t v = threadIdx.x; v < nvec; v += NT) {
-    float x[VEC];
-    if constexpr (VEC > 1) {
-      const Pack<Tin> p = load_pack_cached(zr + v * VEC);
+  constexpr int KR = KEEP > 0 ? KEEP : 1;
+  Pack<Tin> kept[KR];  // vectors threadIdx.x + i*NT, i < KEEP
+  auto fold = [&](const Pack<Tin>& p) {
+    float vm = to_f32(p.v[0]);
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) x[j] = to_f32(p.v[j]);
-    } else {
-      x[0] = to_f32(zr[v]);
-    }
-    float vm = x[0];
-#pragma unroll
-    for (int j = 1; j < VEC; ++j) vm = fmaxf(vm, x[j]);
+    for (int j = 1; j < VEC; ++j) vm = fmaxf(vm, to_f32(p.v[j]));
     if (vm > m) { s *= ex<Tin>(m - vm); m = vm; }
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) s += ex<Tin>(x[j] - m);
+    for (int j = 0; j < VEC; ++j) s += ex<Tin>(to_f32(p.v[j]) - m);
+  };
+  const int64_t tail0 = threadIdx.x + (int64_t)KEEP * NT;  // first streamed vector
+  if constexpr (VEC > 1) {
+    if constexpr (KEEP > 0) {
+#pragma unroll
+      for (int i = 0; i < KEEP; ++i)
+        if (threadIdx.x + i * NT < nvec) kept[i] = load_pack_cached(zr + (threadIdx.x + i * NT) * VEC);
+#pragma unroll
+      for (int i = 0; i < KEEP; ++i)
+        if (threadIdx.x + i * NT < nvec) fold(kept[i]);
+    }
+    for (int64_t v0 = tail0; v0 < nvec; v0 += (int64_t)U * NT) {
+      Pack<Tin> p[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (v0 + u * NT < nvec) p[u] = load_pack_cached(zr + (v0 + u * NT) * VEC);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (v0 + u * NT < nvec) fold(p[u]);
+    }
+  } else {
+    for (int64_t v = threadIdx.x; v < nvec; v += NT) {
+      const float x = to_f32(zr[v]);
+      if (x > m) { s *= ex<Tin>(m - x); m = x; }
+      s += ex<Tin>(x - m);
+    }
   }
   const float lse = block_lse<NT>(m, s, shm, shs);
   if (threadIdx.x == 0) {
@@ -492,20 +520,43 @@ __global__ __launch_bounds__(NT) void row_stream(RowArgs a, const Tin* z, Tout* 
   const float scale = a.dloss / (float)a.cnt->n_valid;
   const float coef = scale * fmaf(2.f * a.zc, lse, 1.f);
   Tout* dr = dz + row * a.ldd;
-  for (int64_t v = threadIdx.x; v < nvec; v += NT) {
-    float x[VEC];
-    if constexpr (VEC > 1) {
-      const Pack<Tin> p = load_pack(zr + v * VEC);
+  if constexpr (VEC > 1) {
+    auto grad = [&](const Pack<Tin>& p, int64_t v) {
+      float g[VEC];
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) x[j] = to_f32(p.v[j]);
-    } else {
-      x[0] = to_f32(zr[v]);
+      for (int j = 0; j < VEC; ++j) {
+        g[j] = coef * ex<Tin>(to_f32(p.v[j]) - lse);
+        if (v * VEC + j == y) g[j] -= scale;
+      }
+      if constexpr (Vec<Tout>::N == VEC) {
+        Pack<Tout> o;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) o.v[j] = from_f32<Tout>(g[j]);
+        store_pack(dr + v * VEC, o);
+      } else {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) dr[v * VEC + j] = from_f32<Tout>(g[j]);
+      }
+    };
+    for (int64_t v0 = tail0; v0 < nvec; v0 += (int64_t)U * NT) {
+      Pack<Tin> p[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (v0 + u * NT < nvec) p[u] = load_pack_cached(zr + (v0 + u * NT) * VEC);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (v0 + u * NT < nvec) grad(p[u], v0 + u * NT);
     }
+    if constexpr (KEEP > 0) {
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      float g = coef * ex<Tin>(x[j] - lse);
-      if (v * VEC + j == y) g -= scale;
-      dr[v * VEC + j] = from_f32<Tout>(g);
+      for (int i = 0; i < KEEP; ++i)
+        if (threadIdx.x + i * NT < nvec) grad(kept[i], threadIdx.x + i * NT);
+    }
+  } else {
+    for (int64_t v = threadIdx.x; v < nvec; v += NT) {
+      float g = coef * ex<Tin>(to_f32(zr[v]) - lse);
+      if (v == y) g -= scale;
+      dr[v] = from_f32<Tout>(g);
     }
   }
 }
@@ -581,7 +632,12 @@ hipError_t launch_rows(const RowArgs& a, const Tin* z, Tout* dz, hipStream_t st,
           row_reg<Tin, Tout, 16, 1024><<<grid, 1024, 0, st>>>(a, z, dz);
         }
         break;
-      default: row_stream<Tin, Tout, VEC, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      default:
+        // longer rows: the first 16 vectors per thread stay in registers between the
+        // passes, the rest is read twice, 4 vectors in flight per thread (V 151936 at
+        // T 8192: 1389 -> 1093 us against one vector in flight and nothing kept)
+        row_stream<Tin, Tout, VEC, 1024, 16, 4><<<grid, 1024, 0, st>>>(a, z, dz);
+        break;
     }
   } else if (ua_ok) {
     // rows of any element alignment and length that fit the registers

@@ -55,10 +55,13 @@ def test_config1_as_stated(gpu):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("V", [4097, 7, 8, 1000, 32001, 50257, 131072, 151936, 200000])
+@pytest.mark.parametrize("V", [4097, 7, 8, 1000, 32001, 50257, 131072, 131080, 151936, 163840,
+                               81920, 200000])
 def test_vocab_sizes(gpu, dtype, V):
     # rows off the 16-byte grid (4097, 7, 32001, 50257: every row starts at another
-    # alignment), tiny, register-resident and streaming rows
+    # alignment), tiny and register-resident rows, rows split between registers and LDS
+    # (bf16 131080: 17 vectors per thread, 151936: 19, 163840: 20, the most; fp32 81920:
+    # 20) and streaming rows (longer)
     g = torch.Generator().manual_seed(V)
     T = 9
     z = (2 * torch.randn(T, V, generator=g)).to(synth.torch_dtype(dtype))
