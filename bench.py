@@ -75,6 +75,8 @@ def parse():
                    help="skip the rows after the step (AdamW, LayerNorm, GeLU MLP "
                         "activations, soft-target cross-entropy)")
     p.add_argument("--no-isolated", action="store_true")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-(config, op) records of configs 1-4")
     p.add_argument("--only", default="", help="comma list of ops to run (profiling)")
     p.add_argument("--calib-copy", action="store_true",
                    help="first run one plain 1 GiB device copy (counter calibration)")
@@ -118,6 +120,7 @@ class Workload:
         self.flce_ws = torch.empty(fo.fo_flce_workspace(c5.T, c5.flce_H, c5.V, 0, fo.FO_F32),
                                    dtype=torch.uint8, device=dev)
         self.fo_out = fo._scalars(dev)
+        self.flce_memory = {}
         self.n_valid_x = int((xe["targets"] != synth.IGNORE_INDEX).sum())
         self.n_valid_f = int((fl["targets"] != synth.IGNORE_INDEX).sum())
         del r, ro, s, xe, fl
@@ -165,6 +168,29 @@ class Workload:
                                                         ws=self.flce_ws, out=self.fo_out),
              flce_flops, "mfma"),
         ]
+
+
+def flce_memory(fo, torch, wl):
+    """Device memory of one fused linear cross-entropy call at the lm-head workload: the
+    caller's inputs, outputs and workspace (the library allocates nothing: checked by the
+    allocator's count across a call), against the bf16 logits [T, V] the fusion never
+    stores."""
+    c5 = wl.c5
+    T, H, V = c5.T, c5.flce_H, c5.V
+    ins = sum(t.numel() * t.element_size() for t in (wl.H, wl.W, wl.ftg))
+    outs = sum(t.numel() * t.element_size() for t in (wl.dH, wl.dW))
+    ws = wl.flce_ws.numel()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    before = torch.cuda.memory_allocated()
+    wl.ops[[o[0] for o in wl.ops].index("flce_fwd_bwd")][1]()
+    torch.cuda.synchronize()
+    return {"workspace_bytes": ws,
+            "full_logits_bf16_bytes": T * V * 2,
+            "workspace_frac_of_logits": round(ws / (T * V * 2), 4),
+            "input_bytes": ins, "output_bytes": outs,
+            "peak_bytes_in_call": ins + outs + ws,
+            "bytes_allocated_by_call": torch.cuda.max_memory_allocated() - before}
 
 
 def measured_peaks(fo, torch, stream, med):
@@ -401,6 +427,109 @@ def distill_line(fo, synth, torch, stream, med, reps, copy_gbs):
     return ent
 
 
+def iso_times(torch, stream, fn, reps, scratch):
+    """Isolated event times (ms) of fn: the 1 GiB scratch written before each call evicts
+    L2 and the Infinity Cache, so every call reads its inputs from HBM."""
+    fn()
+    ts = []
+    for _ in range(reps):
+        scratch.fill_(1.0)
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        e.record(stream)
+        e.synchronize()
+        ts.append(a.elapsed_time(e))
+    return ts
+
+
+LAUNCH_BOUND_US = 7.0  # ops whose bytes take less than this at 70% of peak: launch-bound
+
+
+def config_lines(fo, synth, torch, stream, med, reps, copy_gbs):
+    """One record per (config, op) for the layer-op configs: the tiny fp32 block (T 256),
+    the Qwen2.5-0.5B shapes (T 4096, vocabulary 151936), the Llama-3-8B shapes (T 8192,
+    vocabulary 128256, z-loss) and the packed 16k batch (document-reset positions, 25%
+    ignored targets): RMSNorm, RoPE and SwiGLU forward and backward, and cross-entropy
+    forward+backward, each isolated with caches flushed, against the config's algorithmic
+    bytes; fwd+bwd pairs as (bytes_f + bytes_b) / (t_f + t_b).  Ops whose bytes would take
+    under LAUNCH_BOUND_US at 70% of the HBM peak are flagged launch_bound (parity cases;
+    their rate is not a bandwidth figure)."""
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    out = {}
+    for cid in (1, 2, 3, 4):
+        cfg = synth.CONFIGS[cid]
+        T, d, D, F, V = cfg.T, cfg.d, cfg.head_dim, cfg.F, cfg.V
+        heads = cfg.n_q + cfg.n_kv
+        r = synth.rmsnorm_inputs(cfg)
+        x, w, dy = (r[k].to("cuda") for k in ("x", "w", "dy"))
+        b = x.element_size()
+        y, rstd = fo.fo_rmsnorm_fwd(x, w, cfg.eps)
+        dx = torch.empty_like(x)
+        dw = torch.empty(d, dtype=torch.float32, device="cuda")
+        rws = torch.empty(fo.fo_rmsnorm_bwd_workspace(T, d), dtype=torch.uint8, device="cuda")
+        ro = synth.rope_inputs(cfg)
+        q, k, dq, dk, pos = (ro[n].to("cuda") for n in ("q", "k", "dq", "dk", "pos"))
+        sw = synth.swiglu_inputs(cfg)
+        g, u, dh = (sw[n].to("cuda") for n in ("gate", "up", "dh"))
+        h, dg, du = torch.empty_like(g), torch.empty_like(g), torch.empty_like(g)
+        xe = synth.xent_inputs(cfg)
+        lg, tg = xe["logits"].to("cuda"), xe["targets"].to("cuda")
+        dlg = torch.empty_like(lg)
+        xws = torch.empty(fo.fo_xent_workspace(T, V), dtype=torch.uint8, device="cuda")
+        xo = fo._scalars("cuda")
+        n_ign = int((xe["targets"] == synth.IGNORE_INDEX).sum())
+        del r, ro, sw, xe
+        cases = [
+            ("rmsnorm_fwd", lambda: fo.fo_rmsnorm_fwd(x, w, cfg.eps, y=y, rstd=rstd),
+             2 * T * d * b + d * b + 4 * T),
+            ("rmsnorm_bwd", lambda: fo.fo_rmsnorm_bwd(dy, x, w, rstd, cfg.eps, dx=dx, dw=dw, ws=rws),
+             3 * T * d * b + d * b + 4 * T + 4 * d),
+            ("rope_fwd", lambda: fo.fo_rope_fwd(q, k, pos, cfg.theta), 2 * T * heads * D * b + 8 * T),
+            ("rope_bwd", lambda: fo.fo_rope_bwd(dq, dk, pos, cfg.theta), 2 * T * heads * D * b + 8 * T),
+            ("swiglu_fwd", lambda: fo.fo_swiglu_fwd(g, u, h=h), 3 * T * F * b),
+            ("swiglu_bwd", lambda: fo.fo_swiglu_bwd(dh, g, u, dgate=dg, dup=du), 5 * T * F * b),
+            ("xent_fwd_bwd", lambda: fo.fo_xent_fwd_bwd(lg, tg, -100, cfg.z_loss, 1.0, dlogits=dlg,
+                                                        ws=xws, out=xo),
+             (2 * (T - n_ign) + n_ign) * V * b + 8 * T),
+        ]
+        ent = {"workload": f"{cfg.name}: T {T}, d {d}, {cfg.n_q}/{cfg.n_kv} heads x {D}, ffn {F}, "
+                           f"vocab {V}, {cfg.dtype}" + (", packed documents" if cfg.packed else "")
+                           + (f", {n_ign} ignored targets" if n_ign else "")
+                           + (f", z-loss {cfg.z_loss:g}" if cfg.z_loss else ""),
+               "ops": {}}
+        for name, fn, byt in cases:
+            ts = iso_times(torch, stream, fn, reps, scratch)
+            t = med(ts)
+            e = {"ms_isolated_median": round(t, 4),
+                 "ms_isolated_p10_p90": [round(sorted(ts)[len(ts) // 10], 4),
+                                         round(sorted(ts)[(9 * len(ts)) // 10], 4)],
+                 "algorithmic_MB": round(byt / 1e6, 3),
+                 "GBps": round(byt / (t * 1e-3) / 1e9, 1),
+                 "frac_hbm_peak": round(byt / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "launch_bound": byt / (0.7 * HBM_PEAK_GBS * 1e9) * 1e6 < LAUNCH_BOUND_US}
+            if copy_gbs:
+                e["frac_measured_copy"] = round(e["GBps"] / copy_gbs, 4)
+            if name == "xent_fwd_bwd":
+                e["tokens_per_s"] = round(T / (t * 1e-3), 1)
+            ent["ops"][name] = e
+        pairs = {}
+        for base in ("rmsnorm", "rope", "swiglu"):
+            f_, b_ = ent["ops"][base + "_fwd"], ent["ops"][base + "_bwd"]
+            byt = (f_["algorithmic_MB"] + b_["algorithmic_MB"]) * 1e6
+            t = (f_["ms_isolated_median"] + b_["ms_isolated_median"]) * 1e-3
+            pairs[base] = {"GBps": round(byt / t / 1e9, 1),
+                           "frac_hbm_peak": round(byt / t / 1e9 / HBM_PEAK_GBS, 4),
+                           "launch_bound": f_["launch_bound"] and b_["launch_bound"]}
+        ent["fwd_bwd"] = pairs
+        out[f"cfg{cid}"] = ent
+        del x, w, dy, y, rstd, dx, dw, rws, q, k, dq, dk, pos, g, u, dh, h, dg, du, lg, tg, dlg, xws
+        torch.cuda.empty_cache()
+        print(f"# config {cid} lines done", file=sys.stderr, flush=True)
+    del scratch
+    return out
+
+
 def unaligned_lines(fo, synth, torch, stream, med):
     """Rows that are not a multiple of the 16-byte vector, at the Llama-3-8B token count,
     reported apart from the aligned per-op lines: RMSNorm with d = 4097, SwiGLU with
@@ -507,6 +636,8 @@ def gpu_bench(args):
         step()
     torch.cuda.synchronize()
     print("# warmup done", file=sys.stderr, flush=True)
+    if any(o[0] == "flce_fwd_bwd" for o in wl.ops):
+        wl.flce_memory = flce_memory(fo, torch, wl)
 
     nops = len(wl.ops)
     evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
@@ -547,6 +678,9 @@ def gpu_bench(args):
     same = (None if args.no_probes or not hbm_bytes
             else same_size_copies(fo, torch, stream, med, hbm_bytes, args.iso_reps))
     unaligned = None if args.no_probes or only else unaligned_lines(fo, synth, torch, stream, med)
+    configs = (None if args.no_configs or only
+               else config_lines(fo, synth, torch, stream, med, args.iso_reps,
+                                 peaks["copy_GBps"] if peaks else None))
     next_ops = None
     if not (args.no_next or only):
         cg = peaks["copy_GBps"] if peaks else None
@@ -585,6 +719,8 @@ def gpu_bench(args):
             else:
                 e["frac_measured_mfma"] = round(e["TFLOPs"] / peaks["mfma_TFLOPs"], 4)
         e["traffic_MB"] = round(traffic[name] / 1e6, 1) if traffic and name in traffic else None
+        if name == "flce_fwd_bwd":
+            e.update(wl.flce_memory)
         per_op[name] = e
 
     ms_step = wall / args.steps * 1e3
@@ -631,6 +767,8 @@ def gpu_bench(args):
         out["next_ops"] = next_ops
     if unaligned is not None:
         out["unaligned"] = unaligned
+    if configs is not None:
+        out["configs"] = configs
     # dominant op of the step: the fused linear cross-entropy (MFMA-bound)
     if "flce_fwd_bwd" in per_op:
         i = [o[0] for o in wl.ops].index("flce_fwd_bwd")
@@ -639,8 +777,8 @@ def gpu_bench(args):
         ach = work / (ms * 1e-3) / 1e12
         out["roofline"] = {
             "kernel": "fo_flce_fwd_bwd (per call: per 2048-row chunk the logits and split-K dH "
-                      "bf16 MFMA products and ce_apply; one dW product over all chunks; "
-                      "compaction, gather/scatter)",
+                      "bf16 MFMA products, ce_apply and the dW product accumulating into the "
+                      "fp32 dW; compaction, gather/scatter)",
             "bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic.get("flce_fwd_bwd") if traffic else None,
