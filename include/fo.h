@@ -220,8 +220,9 @@ int fo_xent_fwd_bwd_noalloc(int dtype, int64_t T, int64_t V, const void* logits,
  *   logits, teacher, dlogits [T,V] of dtype (FO_F32 or FO_BF16) with row strides ldl,
  *   ldt, ldd; dlogits may be NULL (forward only) or the logits memory itself (same
  *   stride).  loss, kl (may be NULL), n_valid (may be NULL): device scalars.
- *   ws: fo_distill_workspace(T, V) bytes.  HBM traffic: both rows read once and dlogits
- *   written once for rows of up to 16 K vectors (131072 bf16 / 65536 fp32 values).
+ *   ws: fo_distill_workspace(T, V) bytes.  HBM traffic: both rows read about once (the
+ *   second sweep re-reads the part not kept in registers from L2 and the Infinity Cache)
+ *   and dlogits written once.
  */
 size_t fo_distill_workspace(int64_t T, int64_t V);
 int fo_distill_fwd_bwd(int dtype, int64_t T, int64_t V, const void* logits, int64_t ldl,

@@ -12,12 +12,12 @@
 // so -sum p log q = lse_z - A/s_t, and the KL, sum p (zt - z) + lse_z - lse_t, is
 // D/s_t + (m_z - m_t) + log(s_z/s_t): a sum of terms of the size of the KL itself,
 // where the difference of the two cross-entropies would cancel two logsumexp-sized
-// values.  A second sweep over the same values writes dz.  For rows of up to 16 K vectors both rows stay on chip
-// between the sweeps: the student row in VGPRs, the teacher row in VGPRs and (for the
-// longest rows) LDS, filled by buffer loads that write LDS directly; so HBM sees each
-// input once and dz once (3 T V b).  Longer or unaligned rows re-read both rows in the
-// second sweep (from L2 / MALL); unaligned rows still move their full vectors as
-// 16-byte accesses.
+// values.  A second sweep over the same values writes dz.  A workgroup per row streams
+// both rows with several 16-byte loads of each in flight per thread; for rows longer
+// than 8 vectors per thread the first 8 of each row stay in registers between the
+// sweeps, and the second sweep re-reads the rest, mostly from L2 and the Infinity
+// Cache, so HBM sees each input about once and dz once (3 T V b).  Unaligned rows
+// still move their full vectors as 16-byte accesses.
 #include "xent_kernels.hpp"
 
 namespace fo {
@@ -26,9 +26,6 @@ namespace {
 using xent::Counters;
 
 constexpr int kRowThreads = 1024;
-typedef __attribute__((address_space(3))) void* lds_vptr;
-typedef unsigned int v4u32_t __attribute__((ext_vector_type(4)));
-constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
 
 // Per-thread (then per-row) state of the sweep: student (ms, ss), teacher (mt, st) and
 // the teacher-weighted sums A (of z) and D (of zt - z), all relative to mt.
@@ -121,118 +118,9 @@ template <typename T>
 __device__ __forceinline__ void masked_row(const DistillArgs& a, int64_t row, T* dz) {
   if (dz != nullptr) {
     T* dr = dz + row * a.ldd;
-    for (int64_t e = threadIdx.x; e < a.V; e += kRowThreads) dr[e] = from_f32<T>(0.f);
+    for (int64_t e = threadIdx.x; e < a.V; e += blockDim.x) dr[e] = from_f32<T>(0.f);
   }
   if (threadIdx.x == 0) { a.row_ce[row] = 0.f; a.row_kl[row] = 0.f; }
-}
-
-// On-chip rows: NS vectors per thread of the student in VGPRs; of the teacher, the first
-// NL in LDS and the rest in VGPRs.  Requires V % VEC == 0, aligned rows and strides,
-// V/VEC <= kRowThreads * NS.  Persistent: workgroup b walks rows b, b + gridDim.x, ...;
-// the loads of a row are issued as soon as the previous row's gradient stores are (and,
-// for its LDS part, once every wave has finished reading the previous row there), so a
-// CU streams the next row in while the current one drains.  dz may alias z (a row is
-// wholly loaded before any of its writes, and a row's writes come before the next
-// row's loads only in program order of the same threads that load it).
-template <typename T, int NS, int NL>
-__global__ __launch_bounds__(kRowThreads) void soft_row(DistillArgs a, const T* z, const T* zt,
-                                                       T* dz) {
-  constexpr int VEC = Vec<T>::N;
-  constexpr int NR = NS - NL;  // teacher vectors per thread in VGPRs
-  __shared__ __attribute__((aligned(16))) u32x4 stage[NL > 0 ? NL * kRowThreads : 1];
-  __shared__ Stats sh[kRowThreads / kWave];
-  const int tid = threadIdx.x;
-  const int64_t nvec = a.V / VEC;
-  Pack<T> zv[NS], tv[NR > 0 ? NR : 1];
-  auto kept = [&](int64_t row) { return row < a.T && (a.mask == nullptr || a.mask[row] != 0); };
-  // issue every load of `row` (nothing for a dropped or missing row).  Buffer accesses
-  // over the row: one 32-bit lane offset, the vector index in the scalar offset, and
-  // vectors past the row read as zeros (no per-vector address registers or branches).
-  const uint32_t lane_off = (uint32_t)tid * 16u;
-  auto row_rsrc = [&](const T* base, int64_t row, int64_t ld) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row * ld), (short)0,
-                                             (int)(nvec * 16), kBufFlags);
-  };
-  auto issue = [&](int64_t row) {
-    if (!kept(row)) return;
-    const __amdgpu_buffer_rsrc_t rz = row_rsrc(z, row, a.ldz);
-    const __amdgpu_buffer_rsrc_t rt = row_rsrc(zt, row, a.ldt);
-    if constexpr (NL > 0) {
-      // teacher vectors tid + i*1024 (i < NL) into LDS slot i*1024 + tid
-      const int wbase = tid & ~(kWave - 1);
-#pragma unroll
-      for (int i = 0; i < NL; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (lds_vptr)(stage + i * kRowThreads + wbase),
-                                                 16, lane_off, i * kRowThreads * 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-      zv[i].raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rz, lane_off, i * kRowThreads * 16, 0));
-#pragma unroll
-    for (int i = 0; i < NR; ++i)
-      tv[i].raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rt, lane_off, (NL + i) * kRowThreads * 16, 0));
-  };
-  auto teacher = [&](int i) -> Pack<T> {
-    Pack<T> p;
-    if (i < NL) p.raw = stage[i * kRowThreads + tid];
-    else p = tv[i - NL];
-    return p;
-  };
-  issue(blockIdx.x);
-  for (int64_t row = blockIdx.x; row < a.T; row += gridDim.x) {
-    const int64_t next = row + gridDim.x;
-    if (!kept(row)) {
-      masked_row<T>(a, row, dz);
-      issue(next);
-      continue;
-    }
-    // each lane reads back only the LDS slots its own DMA lane wrote: its own wait
-    // suffices (it also covers the previous row's stores, which drain meanwhile)
-    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0) (lgkm, exp at max)
-    Stats s;
-    stats_init(s);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int64_t v = tid + (int64_t)i * kRowThreads;
-      if (v < nvec) {
-        const Pack<T> tp = teacher(i);
-        float zf[VEC], tf[VEC];
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) { zf[j] = to_f32(zv[i].v[j]); tf[j] = to_f32(tp.v[j]); }
-        stats_add<T, VEC>(s, zf, tf);
-      }
-    }
-    const Stats r = block_stats<kRowThreads>(s, sh);
-    float lse_z, lse_t;
-    row_terms(a, row, r, lse_z, lse_t);
-    if (dz != nullptr) {
-      const float scale = a.dloss / (float)a.cnt->n_valid;
-      // keep both rows packed between the sweeps (re-widened below)
-#pragma unroll
-      for (int i = 0; i < NS; ++i) asm volatile("" : "+v"(zv[i].raw));
-#pragma unroll
-      for (int i = 0; i < NR; ++i) asm volatile("" : "+v"(tv[i].raw));
-      // stores past the row fall outside the buffer and are dropped
-      const __amdgpu_buffer_rsrc_t rd = row_rsrc(dz, row, a.ldd);
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        const Pack<T> tp = teacher(i);
-        Pack<T> o;
-#pragma unroll
-        for (int j = 0; j < VEC; ++j)
-          o.v[j] = from_f32<T>(scale * (xent::ex<T>(to_f32(zv[i].v[j]) - lse_z) -
-                                        xent::ex<T>(to_f32(tp.v[j]) - lse_t)));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, o.raw), rd, lane_off,
-                                               i * kRowThreads * 16, 0);
-      }
-    }
-    // every wave is done with this row's LDS part (and with sh) before the next row's
-    // copy lands there
-    __syncthreads();
-    issue(next);
-  }
 }
 
 // Any row length and alignment: the second sweep re-reads both rows.  dz may alias z
@@ -304,6 +192,92 @@ __global__ __launch_bounds__(kRowThreads) void soft_stream(DistillArgs a, const 
   }
 }
 
+// Aligned rows of any length (V % VEC == 0), streamed: each thread keeps its first KS
+// vectors of both rows in registers from the first sweep to the second and re-reads the
+// rest (from L2 and the Infinity Cache); streamed vectors of both rows are loaded U at a
+// time before any is used (2U 16-byte loads in flight per thread), and the gradient
+// goes out as 16-byte vectors.  dz may alias z (each element is read by the thread that
+// writes it; the merge barrier separates the first sweep's reads from the writes).
+template <typename T, int U, int KS, int NT = kRowThreads>
+__global__ __launch_bounds__(NT) void soft_stream_u(DistillArgs a, const T* z, const T* zt,
+                                                   T* dz) {
+  constexpr int VEC = Vec<T>::N;
+  constexpr int KR = KS > 0 ? KS : 1;
+  __shared__ Stats sh[NT / kWave];
+  const int64_t row = blockIdx.x;
+  if (a.mask != nullptr && a.mask[row] == 0) {
+    masked_row<T>(a, row, dz);
+    return;
+  }
+  const int64_t n = a.V / VEC;
+  const T* zr = z + row * a.ldz;
+  const T* tr = zt + row * a.ldt;
+  const int64_t tid = threadIdx.x;
+  Pack<T> kz[KR], kt[KR];
+  Stats s;
+  stats_init(s);
+  auto add = [&](const Pack<T>& zp, const Pack<T>& tp) {
+    float zf[VEC], tf[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) { zf[j] = to_f32(zp.v[j]); tf[j] = to_f32(tp.v[j]); }
+    stats_add<T, VEC>(s, zf, tf);
+  };
+  if constexpr (KS > 0) {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const int64_t v = tid + (int64_t)i * NT;
+      if (v < n) { kz[i] = load_pack_cached(zr + v * VEC); kt[i] = load_pack_cached(tr + v * VEC); }
+    }
+#pragma unroll
+    for (int i = 0; i < KS; ++i)
+      if (tid + (int64_t)i * NT < n) add(kz[i], kt[i]);
+  }
+  const int64_t tail0 = tid + (int64_t)KS * NT;
+  for (int64_t v0 = tail0; v0 < n; v0 += (int64_t)U * NT) {
+    Pack<T> zp[U], tp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * NT;
+      if (v < n) { zp[u] = load_pack_cached(zr + v * VEC); tp[u] = load_pack_cached(tr + v * VEC); }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (v0 + u * NT < n) add(zp[u], tp[u]);
+  }
+  const Stats r = block_stats<NT>(s, sh);
+  float lse_z, lse_t;
+  row_terms(a, row, r, lse_z, lse_t);
+  if (dz == nullptr) return;
+  const float scale = a.dloss / (float)a.cnt->n_valid;
+  T* dr = dz + row * a.ldd;
+  auto grad = [&](const Pack<T>& zp, const Pack<T>& tp, int64_t v) {
+    Pack<T> o;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+      o.v[j] = from_f32<T>(scale * (xent::ex<T>(to_f32(zp.v[j]) - lse_z) -
+                                    xent::ex<T>(to_f32(tp.v[j]) - lse_t)));
+    store_pack(dr + v * VEC, o);
+  };
+  for (int64_t v0 = tail0; v0 < n; v0 += (int64_t)U * NT) {
+    Pack<T> zp[U], tp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * NT;
+      if (v < n) { zp[u] = load_pack_cached(zr + v * VEC); tp[u] = load_pack_cached(tr + v * VEC); }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (v0 + u * NT < n) grad(zp[u], tp[u], v0 + u * NT);
+  }
+  if constexpr (KS > 0) {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const int64_t v = tid + (int64_t)i * NT;
+      if (v < n) grad(kz[i], kt[i], v);
+    }
+  }
+}
+
 // N = rows the mask keeps (all T without a mask), into cnt.  One workgroup.
 __global__ __launch_bounds__(1024) void count_mask(int64_t T_, const uint8_t* __restrict__ mask,
                                                    Counters* cnt) {
@@ -339,11 +313,6 @@ Ws ws_layout(int64_t T_) {
 template <typename T>
 int distill_impl(const DistillArgs& a0, const T* z, const T* zt, T* dz, float* loss, float* kl,
                  int64_t* n_valid, char* ws, hipStream_t st) {
-  int dev = 0, n_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      n_cu < 1)
-    return FO_ERR_HIP;
   const Ws w = ws_layout(a0.T);
   DistillArgs a = a0;
   Counters* cnt = reinterpret_cast<Counters*>(ws + w.off_cnt);
@@ -357,16 +326,13 @@ int distill_impl(const DistillArgs& a0, const T* z, const T* zt, T* dz, float* l
                      aligned16(zt) && (dz == nullptr || (a.ldd % VEC == 0 && aligned16(dz)));
     const int64_t nvec = a.V / VEC;
     const dim3 grid((unsigned)a.T), block(kRowThreads);
-    if (vec && nvec <= 16 * kRowThreads) {
-      // persistent: one workgroup per CU (a row pair fills a CU's registers)
-      const dim3 pgrid((unsigned)(a.T < n_cu ? a.T : n_cu));
-      const int64_t per = ceil_div(nvec, kRowThreads);
-      if (per <= 4) soft_row<T, 4, 0><<<pgrid, block, 0, st>>>(a, z, zt, dz);
-      else if (per <= 8) soft_row<T, 8, 0><<<pgrid, block, 0, st>>>(a, z, zt, dz);
-      else if (per <= 12) soft_row<T, 12, 5><<<pgrid, block, 0, st>>>(a, z, zt, dz);
-      else soft_row<T, 16, 9><<<pgrid, block, 0, st>>>(a, z, zt, dz);
-    } else if (vec) {
-      soft_stream<T, VEC><<<grid, block, 0, st>>>(a, z, zt, dz);
+    if (vec) {
+      // both rows streamed; beyond 8 vectors per thread the first 8 of each row stay in
+      // registers between the sweeps (T 8192, bf16: V 4096 329 -> 181 us, 32000
+      // 474 -> 398, 128256 1525 -> 1324 against rows held on chip, one per CU)
+      if (nvec <= 4 * 256) soft_stream_u<T, 4, 0, 256><<<grid, dim3(256), 0, st>>>(a, z, zt, dz);
+      else if (nvec <= 8 * kRowThreads) soft_stream_u<T, 4, 0><<<grid, block, 0, st>>>(a, z, zt, dz);
+      else soft_stream_u<T, 4, 8><<<grid, block, 0, st>>>(a, z, zt, dz);
     } else if (reinterpret_cast<uintptr_t>(z) % sizeof(T) == 0 &&
                reinterpret_cast<uintptr_t>(zt) % sizeof(T) == 0 &&
                reinterpret_cast<uintptr_t>(dz) % sizeof(T) == 0) {
