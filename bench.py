@@ -454,7 +454,9 @@ def config_lines(fo, synth, torch, stream, med, reps, copy_gbs):
     forward+backward, each isolated with caches flushed, against the config's algorithmic
     bytes; fwd+bwd pairs as (bytes_f + bytes_b) / (t_f + t_b).  Ops whose bytes would take
     under LAUNCH_BOUND_US at 70% of the HBM peak are flagged launch_bound (parity cases;
-    their rate is not a bandwidth figure)."""
+    their rate is not a bandwidth figure).  Each record also carries the isolated time of
+    the library's copy probe moving the same bytes (frac_same_size_copy = copy time / op
+    time): what a plain copy of that size reaches, start-up and drain included."""
     scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     out = {}
     for cid in (1, 2, 3, 4):
@@ -498,6 +500,7 @@ def config_lines(fo, synth, torch, stream, med, reps, copy_gbs):
                            + (f", {n_ign} ignored targets" if n_ign else "")
                            + (f", z-loss {cfg.z_loss:g}" if cfg.z_loss else ""),
                "ops": {}}
+        copy_ms = same_size_copies(fo, torch, stream, med, [byt for _, _, byt in cases], reps)
         for name, fn, byt in cases:
             ts = iso_times(torch, stream, fn, reps, scratch)
             t = med(ts)
@@ -510,6 +513,9 @@ def config_lines(fo, synth, torch, stream, med, reps, copy_gbs):
                  "launch_bound": byt / (0.7 * HBM_PEAK_GBS * 1e9) * 1e6 < LAUNCH_BOUND_US}
             if copy_gbs:
                 e["frac_measured_copy"] = round(e["GBps"] / copy_gbs, 4)
+            # the library's copy probe moving the same bytes (half in, half out), isolated
+            e["same_size_copy_ms"] = round(copy_ms[byt], 4)
+            e["frac_same_size_copy"] = round(copy_ms[byt] / t, 4)
             if name == "xent_fwd_bwd":
                 e["tokens_per_s"] = round(T / (t * 1e-3), 1)
             ent["ops"][name] = e

@@ -30,7 +30,8 @@
  *    path.  Other rows of the RMSNorm, LayerNorm, cross-entropy and distillation calls,
  *    and other bf16 rows of the MLP activations, still move their full vectors as
  *    16-byte accesses at element-aligned addresses, with each row's partial last vector
- *    element by element.  Anything else takes a scalar path.  Every path computes the
+ *    element by element (RMSNorm and LayerNorm: one element per lane of the row's first
+ *    wave, beside its full vectors).  Anything else takes a scalar path.  Every path computes the
  *    same results within rounding: the order of a row's reductions may differ between
  *    paths, and is fixed for each.
  *  - Floating-point results are deterministic: no float atomics; every reduction runs

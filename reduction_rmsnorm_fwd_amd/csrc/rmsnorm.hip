@@ -17,7 +17,8 @@
 // partial rows in a fixed order.  Rows that start off a 16-byte boundary or whose
 // length is not a multiple of the vector take the same kernels (template flag UA):
 // their full vectors are still moved as 16-byte accesses at element-aligned addresses,
-// their last partial vector element by element.  Rows too long for the registers take a
+// and the d % VEC elements past the last full vector go to the first lanes of the row's
+// first wave, one element each.  Rows too long for the registers take a
 // workgroup-per-row path that reads the row twice (the second read from L2).
 #include <initializer_list>
 #include <type_traits>
@@ -33,31 +34,23 @@ constexpr int kMaxPartials = 512;  // dw partial rows (workgroups of the backwar
 constexpr int kGenericThreads = 256;
 
 // ------------------------------------------------------- vectors of a row, any alignment
+// A row is nvec = d / VEC full vectors, then (UA only) a tail of d % VEC elements.
 // UA = false: the row (or w, b) starts on 16 bytes and d is a multiple of the vector.
-// UA = true: it starts on any element and d is any length.  The full vectors of the row
-// are still moved as 16-byte accesses at their element-aligned addresses (gfx950 runs
-// global memory in unaligned mode: such loads cost nothing extra, stores ~12%, measured
-// against aligned ones), so every byte read or written is one of the row's; only the
-// last, partial vector goes element by element, with zeros past the row.
-template <typename T, bool UA, bool NT>
-__device__ __forceinline__ Pack<T> ld_vec(const T* p, int v, int d) {
+// UA = true: it starts on any element and d is any length.  The full vectors are still
+// moved as 16-byte accesses at their element-aligned addresses (gfx950 runs global
+// memory in unaligned mode: such loads cost nothing extra, stores ~12%, measured
+// against aligned ones), so every byte read or written is one of the row's.  Tail
+// element k (k < d % VEC) belongs to lane k of the row's first wave, which loads,
+// reduces and stores it beside its vectors, so the vectors keep the lane layout (and
+// launch plan) of a row of d - d % VEC elements.
+template <typename T, bool NT>
+__device__ __forceinline__ Pack<T> ld_vec(const T* p, int v) {
   constexpr int VEC = Vec<T>::N;
-  if (!UA || (v + 1) * VEC <= d) return NT ? load_pack(p + (int64_t)v * VEC) : load_pack_cached(p + (int64_t)v * VEC);
-  Pack<T> r;
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) r.v[j] = v * VEC + j < d ? p[(int64_t)v * VEC + j] : from_f32<T>(0.f);
-  return r;
+  return NT ? load_pack(p + (int64_t)v * VEC) : load_pack_cached(p + (int64_t)v * VEC);
 }
-template <typename T, bool UA>
-__device__ __forceinline__ void st_vec(T* p, int v, int d, const Pack<T>& o) {
-  constexpr int VEC = Vec<T>::N;
-  if (!UA || (v + 1) * VEC <= d) {
-    store_pack(p + (int64_t)v * VEC, o);
-  } else {
-#pragma unroll
-    for (int j = 0; j < VEC; ++j)
-      if (v * VEC + j < d) p[(int64_t)v * VEC + j] = o.v[j];
-  }
+template <typename T>
+__device__ __forceinline__ void st_vec(T* p, int v, const Pack<T>& o) {
+  store_pack(p + (int64_t)v * Vec<T>::N, o);
 }
 
 // w g - m with the product rounded before the subtraction (no fused multiply-add), as
@@ -71,7 +64,7 @@ __device__ __forceinline__ float centred(float w, float g, float m) {
 // ----------------------------------------------------------------- forward, fast
 // LN: LayerNorm (mean subtracted before the variance, bias added); the row is still
 // read once: mean and centred variance are two sweeps over the registers.
-// nvec: vectors per row, the last one partial when UA and d is not a multiple of VEC.
+// nvec: full vectors per row (d / VEC); UA: lanes k < d % VEC also own tail element k.
 template <typename T, int NV, bool LN, bool UA>
 __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
     int64_t T_, int nvec, int d, const T* __restrict__ x, int64_t ldx,
@@ -82,13 +75,16 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
   const int64_t row = (int64_t)blockIdx.x * kFwdWaves + (threadIdx.x / kWave);
   if (row >= T_) return;
   const T* xr = x + row * ldx;
+  const int tcol = nvec * VEC + lane;  // this lane's tail element (UA)
+  const bool tl = UA && tcol < d;
   Pack<T> xv[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int v = lane + i * kWave;
-    if (v < nvec) xv[i] = ld_vec<T, UA, true>(xr, v, d);
+    if (v < nvec) xv[i] = ld_vec<T, true>(xr, v);
     else xv[i].raw = u32x4{0, 0, 0, 0};
   }
+  const float xt = tl ? to_f32(xr[tcol]) : 0.f;
   float mu = 0.f;
   if constexpr (LN) {
     float s = 0.f;
@@ -96,7 +92,7 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
     for (int i = 0; i < NV; ++i)
 #pragma unroll
       for (int j = 0; j < VEC; ++j) s += to_f32(xv[i].v[j]);
-    mu = wave_sum(s) / (float)d;
+    mu = wave_sum(UA ? s + xt : s) / (float)d;
     // re-widen for the variance sweep instead of holding fp32 copies (as below)
 #pragma unroll
     for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(xv[i].raw));
@@ -108,13 +104,15 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
     for (int j = 0; j < VEC; ++j) {
       if constexpr (LN) {
         const float f = to_f32(xv[i].v[j]) - mu;
-        // padding holds 0, not mu
-        if ((lane + i * kWave) * VEC + j < d) ss = fmaf(f, f, ss);
+        // unused slots hold 0, not mu.  (Aligned rows test per element: the same set,
+        // and measured 9% faster at T 8192, d 4096 bf16 than the per-vector test.)
+        if (UA ? lane + i * kWave < nvec : (lane + i * kWave) * VEC + j < d) ss = fmaf(f, f, ss);
       } else {
         const float f = to_f32(xv[i].v[j]);
         ss = fmaf(f, f, ss);
       }
     }
+  if (tl) ss = fmaf(xt - mu, xt - mu, ss);
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
   T* yr = y + row * ldy;
@@ -126,10 +124,10 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
   for (int i = 0; i < NV; ++i) {
     const int v = lane + i * kWave;
     if (v < nvec) {
-      const Pack<T> wv = ld_vec<T, UA, false>(w, v, d);
+      const Pack<T> wv = ld_vec<T, false>(w, v);
       Pack<T> o;
       if constexpr (LN) {
-        const Pack<T> bv = ld_vec<T, UA, false>(b, v, d);
+        const Pack<T> bv = ld_vec<T, false>(b, v);
 #pragma unroll
         for (int j = 0; j < VEC; ++j)
           o.v[j] = from_f32<T>(fmaf((to_f32(xv[i].v[j]) - mu) * r, to_f32(wv.v[j]), to_f32(bv.v[j])));
@@ -137,8 +135,12 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
 #pragma unroll
         for (int j = 0; j < VEC; ++j) o.v[j] = from_f32<T>(to_f32(xv[i].v[j]) * r * to_f32(wv.v[j]));
       }
-      st_vec<T, UA>(yr, v, d, o);
+      st_vec<T>(yr, v, o);
     }
+  }
+  if (tl) {
+    if constexpr (LN) yr[tcol] = from_f32<T>(fmaf((xt - mu) * r, to_f32(w[tcol]), to_f32(b[tcol])));
+    else yr[tcol] = from_f32<T>(xt * r * to_f32(w[tcol]));
   }
   if (lane == 0) {
     if (rstd != nullptr) rstd[row] = r;
@@ -213,6 +215,8 @@ __global__ __launch_bounds__(kGenericThreads) void rmsnorm_fwd_block(
 // the db partials folded beside the dw partials (partial row of 2d floats).  g - mean(g)
 // is formed first (see centred()), so a row whose centred gradient vanishes exactly
 // (one column) gives dx exactly 0.
+// nvec: full vectors per row (d / VEC); UA: lanes k < d % VEC of each row group's first
+// wave also own tail element k, held as scalars beside the vectors.
 template <typename T, int NV, int RW, bool LN, bool UA>
 __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
     int64_t T_, int nvec, int d, const T* dy, int64_t lddy, const T* x, int64_t ldx,
@@ -227,12 +231,16 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
   const int wave = threadIdx.x / kWave;
   const int rg = wave / RW, wr = wave % RW;
   const int vbase = wr * kWave + lane;
+  const int tcol = nvec * VEC + lane;  // this lane's tail element (UA, first wave only)
+  const bool tl = UA && wr == 0 && tcol < d;
+  const float wt = tl ? to_f32(w[tcol]) : 0.f;
+  float acct = 0.f, accbt = 0.f;
   Pack<T> wv[NV];
   float acc[NV][VEC], accb[NB][VEC];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int v = vbase + i * RW * kWave;
-    if (v < nvec) wv[i] = ld_vec<T, UA, false>(w, v, d);
+    if (v < nvec) wv[i] = ld_vec<T, false>(w, v);
     else wv[i].raw = u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < VEC; ++j) acc[i][j] = 0.f;
@@ -247,7 +255,9 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
   Pack<T> gv[NV], xv[NV], gn[NV], xn[NV];
   float rv = 0.f, rn = 0.f;  // the saved 1/rms (1/std) of the row (loaded with the row)
   float mv = 0.f, mn = 0.f;  // LN: the saved mean of the row
-  auto load_round = [&](int64_t rd, Pack<T>* g, Pack<T>* xx, float& r, float& m) {
+  float gt = 0.f, xt = 0.f, gtn = 0.f, xtn = 0.f;  // the tail element of dy and x (UA)
+  auto load_round = [&](int64_t rd, Pack<T>* g, Pack<T>* xx, float& r, float& m, float& g1,
+                        float& x1) {
     const int64_t row = (int64_t)blockIdx.x * RG + rg + rd * stride;
     const bool live = rd < rounds && row < T_;
     if (rstd != nullptr && live) r = rstd[row];
@@ -258,19 +268,23 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
     for (int i = 0; i < NV; ++i) {
       const int v = vbase + i * RW * kWave;
       if (live && v < nvec) {
-        g[i] = ld_vec<T, UA, true>(dy + row * lddy, v, d);
-        xx[i] = ld_vec<T, UA, true>(x + row * ldx, v, d);
+        g[i] = ld_vec<T, true>(dy + row * lddy, v);
+        xx[i] = ld_vec<T, true>(x + row * ldx, v);
       } else {
         g[i].raw = u32x4{0, 0, 0, 0};
         xx[i].raw = u32x4{0, 0, 0, 0};
       }
     }
+    if constexpr (UA) {
+      g1 = live && tl ? to_f32(dy[row * lddy + tcol]) : 0.f;
+      x1 = live && tl ? to_f32(x[row * ldx + tcol]) : 0.f;
+    }
   };
-  load_round(0, gv, xv, rv, mv);
+  load_round(0, gv, xv, rv, mv, gt, xt);
   for (int64_t rd = 0; rd < rounds; ++rd) {
     const int64_t row = (int64_t)blockIdx.x * RG + rg + rd * stride;
     const bool live = row < T_;
-    load_round(rd + 1, gn, xn, rn, mn);
+    load_round(rd + 1, gn, xn, rn, mn, gtn, xtn);
     // RMS: dot = sum g x, ss = sum x^2;  LN: dot = sum g (x - mean), ss = sum g
     float dot = 0.f, ss = 0.f;
 #pragma unroll
@@ -288,6 +302,17 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
           ss = fmaf(xf, xf, ss);
         }
       }
+    if constexpr (UA) {
+      // lanes without a tail element hold zeros in wt, gt and xt
+      const float gf = wt * gt;
+      if constexpr (LN) {
+        dot = fmaf(gf, xt - mv, dot);
+        ss += gf;
+      } else {
+        dot = fmaf(gf, xt, dot);
+        ss = fmaf(xt, xt, ss);
+      }
+    }
     dot = wave_sum(dot);
     ss = wave_sum(ss);
     // keep the operands packed across the reduction (re-widened below)
@@ -332,7 +357,18 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
               acc[i][j] = fmaf(gf * xf, r, acc[i][j]);
             }
           }
-          st_vec<T, UA>(dxr, v, d, o);
+          st_vec<T>(dxr, v, o);
+        }
+      }
+      if (tl) {
+        if constexpr (LN) {
+          const float xc = xt - mv;
+          dxr[tcol] = from_f32<T>(r * centred(wt, gt, c) - k * xc);
+          acct = fmaf(gt * xc, r, acct);
+          accbt += gt;
+        } else {
+          dxr[tcol] = from_f32<T>(r * (wt * gt) - k * xt);
+          acct = fmaf(gt * xt, r, acct);
         }
       }
     }
@@ -343,6 +379,8 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
     }
     rv = rn;
     mv = mn;
+    gt = gtn;
+    xt = xtn;
   }
   // fold the row groups' column partials in order 0,1,2,... (RW waves of a group own
   // disjoint columns, so they write their slots in the same step)
@@ -354,7 +392,6 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
         if (v < nvec) {
 #pragma unroll
           for (int j = 0; j < VEC; ++j) {
-            if (UA && v * VEC + j >= d) continue;  // past the row (fold holds d columns)
             float* p = &fold[v * VEC + j];
             *p = (s == 0) ? acc[i][j] : (*p + acc[i][j]);
             if constexpr (LN) {
@@ -363,6 +400,10 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
             }
           }
         }
+      }
+      if (tl) {
+        fold[tcol] = (s == 0) ? acct : (fold[tcol] + acct);
+        if constexpr (LN) fold[d + tcol] = (s == 0) ? accbt : (fold[d + tcol] + accbt);
       }
     }
     __syncthreads();
@@ -529,10 +570,11 @@ bool vector_ok(int64_t d, const void* a, int64_t lda, const void* b, int64_t ldb
 }
 
 // Rows of any alignment and length that still fit the registers of the wave kernels
-// (UA = true there): element-aligned pointers, at most 16 vectors per lane.
+// (UA = true there): element-aligned pointers, at most 16 full vectors per lane (the
+// tail of fewer than VEC elements rides on scalar registers beside them).
 template <typename T>
 bool unaligned_ok(int64_t d, std::initializer_list<const void*> ptrs) {
-  bool ok = ceil_div(d, (int64_t)Vec<T>::N) <= 16 * kWave;
+  bool ok = d / Vec<T>::N <= 16 * kWave;
   for (const void* p : ptrs) ok = ok && reinterpret_cast<uintptr_t>(p) % sizeof(T) == 0;
   return ok;
 }
@@ -552,7 +594,7 @@ int fwd_impl(int64_t T_, int64_t d, const void* x, int64_t ldx, const void* w, c
   T* yp = static_cast<T*>(y);
   const bool aligned = vector_ok<T>(d, x, ldx, y, ldy, x, ldx, w) && (!LN || aligned16(b));
   if (aligned || unaligned_ok<T>(d, {x, y, w, LN ? b : x})) {
-    const int nvec = (int)ceil_div(d, (int64_t)Vec<T>::N);
+    const int nvec = (int)(d / Vec<T>::N);  // full vectors; the rest is the tail (UA)
     const dim3 grid((unsigned)ceil_div(T_, kFwdWaves));
     const dim3 block(kFwdWaves * kWave);
     auto go = [&](auto ua) {
@@ -625,7 +667,7 @@ int bwd_impl(int64_t T_, int64_t d, const void* dy, int64_t lddy, const void* x,
   int64_t G;
   const bool aligned = vector_ok<T>(d, dy, lddy, x, ldx, dx, lddx, w);
   if (aligned || unaligned_ok<T>(d, {dy, x, dx, w})) {
-    const int nvec = (int)ceil_div(d, (int64_t)Vec<T>::N);
+    const int nvec = (int)(d / Vec<T>::N);  // full vectors; the rest is the tail (UA)
     const BwdPlan p = bwd_plan<T>(T_, nvec);
     G = p.groups;
     constexpr int kMaxNV = 16 / Vec<T>::N;

@@ -47,9 +47,13 @@ def test_configs_small(gpu, cid, T):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("d", [13, 1000, 1025, 4097, 8, 8192, 12288])
-def test_unaligned_and_wide_rows(gpu, dtype, d):
-    cfg = small_cfg(dtype, 37, d)
+@pytest.mark.parametrize("T,d", [(37, d) for d in (3, 5, 13, 1000, 1025, 4097, 4099, 4100, 8,
+                                                   8192, 8199, 8200, 12288)] + [(5000, 1027)])
+def test_unaligned_and_wide_rows(gpu, dtype, T, d):
+    # as for RMSNorm: tail-only rows (3, 5), tails of 1 to 7 elements, the widest rows the
+    # wave kernels hold (4099 fp32, 8192 and 8199 bf16) and just beyond, and several
+    # backward rounds (T 5000)
+    cfg = small_cfg(dtype, T, d)
     i = synth.layernorm_inputs(cfg)
     got = run(gpu, i["x"], i["w"], i["b"], i["dy"], cfg.eps)
     compare(i["x"], i["w"], i["b"], i["dy"], cfg.eps, dtype, got)

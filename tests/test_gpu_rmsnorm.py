@@ -51,11 +51,17 @@ def test_config1_as_stated(gpu):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("d", [13, 1000, 1025, 2049, 4097, 8, 8193, 12288])
-def test_unaligned_and_wide_rows(gpu, dtype, d):
-    cfg = synth.Config(0, "odd", dtype, T=37, d=d, n_q=1, n_kv=1, head_dim=2, F=1, V=2,
+@pytest.mark.parametrize("T,d", [(37, d) for d in (3, 5, 13, 1000, 1025, 2049, 4097, 4099, 4100,
+                                                   8, 8191, 8199, 8200, 12288)] + [(5000, 1027)])
+def test_unaligned_and_wide_rows(gpu, dtype, T, d):
+    # rows shorter than one vector (3, 5: tail only), vectors plus a tail (4099 fp32 and
+    # 8199 bf16: the 1024 full vectors the wave kernels hold at most, and the longest
+    # tail), just past that bound (4100 fp32, 8200 bf16) and far past it (12288), and a
+    # batch whose backward workgroups each take several rounds of rows with a tail
+    # (T 5000, d 1027)
+    cfg = synth.Config(0, "odd", dtype, T=T, d=d, n_q=1, n_kv=1, head_dim=2, F=1, V=2,
                        eps=1e-5, theta=1e4, logit_std=1, z_loss=0, ignore_frac=0,
-                       packed=False, doc_lengths=(37,), seed=11)
+                       packed=False, doc_lengths=(T,), seed=11)
     i = synth.rmsnorm_inputs(cfg)
     got = run(gpu, i["x"], i["w"], i["dy"], cfg.eps)
     compare(i["x"], i["w"], i["dy"], cfg.eps, dtype, got)
