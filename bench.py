@@ -393,8 +393,9 @@ def activation_lines(fo, synth, torch, stream, med, reps, copy_gbs):
 def distill_line(fo, synth, torch, stream, med, reps, copy_gbs):
     """Soft-target cross-entropy (a row after the step's ops, reported apart from the
     step) on the Llama-3-8B lm-head logits shape (T 8192, V 128256, bf16, 10% of rows
-    masked), isolated with caches flushed.  Bytes 3TVb (student and teacher read,
-    dlogits written) + T (mask)."""
+    masked), isolated with caches flushed.  Bytes (3 K + M) V b + T: a kept row reads
+    the student and teacher rows and writes its gradient, a masked one only writes zeros
+    (K kept rows, M masked), plus the mask."""
     cfg = synth.scaled(synth.CONFIGS[3], 8192)
     i = synth.distill_inputs(cfg)
     z, zt, mask = (i[k].to("cuda") for k in ("logits", "teacher", "row_mask"))
@@ -415,7 +416,8 @@ def distill_line(fo, synth, torch, stream, med, reps, copy_gbs):
             ts.append(a.elapsed_time(e))
     del scratch
     ms = med(ts)
-    byt = 3 * T * V * z.element_size() + T
+    kept = int(i["row_mask"].sum())
+    byt = (3 * kept + (T - kept)) * V * z.element_size() + T
     ent = {"workload": f"T {T}, V {V}, bf16, 10% of rows masked (Llama-3-8B lm-head logits shape)",
            "ms_isolated_median": round(ms, 4), "algorithmic_MB": round(byt / 1e6, 1),
            "GBps": round(byt / (ms * 1e-3) / 1e9, 1),

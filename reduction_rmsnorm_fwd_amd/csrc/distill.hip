@@ -49,8 +49,8 @@ __device__ __forceinline__ void stats_merge(Stats& s, const Stats& o) {
 }
 
 // VEC values of the student (z) and teacher (t)
-// (exponentials: accurate for fp32 rows, the hardware path for bf16 rows, as the
-// hard-label kernels)
+// (exponentials: accurate for fp32 rows, for bf16 rows one fused multiply-add into the
+// hardware 2^x per value, as the hard-label kernels)
 // PAD: some values are -inf padding (both z and t) past the end of the row; a zero
 // teacher weight then contributes nothing to A and D (plain fmaf would give 0 * -inf).
 template <typename T, int VEC, bool PAD = false>
@@ -63,10 +63,11 @@ __device__ __forceinline__ void stats_add(Stats& s, const float* z, const float*
     const float f = xent::ex<T>(s.mt - vt);
     s.st *= f; s.a *= f; s.d *= f; s.mt = vt;
   }
+  const float nz = xent::nl2e<T>(s.ms), nt = xent::nl2e<T>(s.mt);
 #pragma unroll
   for (int j = 0; j < VEC; ++j) {
-    s.ss += xent::ex<T>(z[j] - s.ms);
-    const float e = xent::ex<T>(t[j] - s.mt);
+    s.ss += xent::exs<T>(z[j], nz);
+    const float e = xent::exs<T>(t[j], nt);
     s.st += e;
     if (PAD && e == 0.f) continue;
     s.a = fmaf(e, z[j], s.a);
@@ -169,6 +170,7 @@ __global__ __launch_bounds__(kRowThreads) void soft_stream(DistillArgs a, const 
   row_terms(a, row, r, lse_z, lse_t);
   if (dz == nullptr) return;
   const float scale = a.dloss / (float)a.cnt->n_valid;
+  const float nz = xent::nl2e<T>(lse_z), nt = xent::nl2e<T>(lse_t);
   T* dr = dz + row * a.ldd;
   for (int64_t v = threadIdx.x; v < n; v += kRowThreads) {
     if constexpr (VEC > 1) {
@@ -176,8 +178,8 @@ __global__ __launch_bounds__(kRowThreads) void soft_stream(DistillArgs a, const 
       Pack<T> o;
 #pragma unroll
       for (int j = 0; j < VEC; ++j)
-        o.v[j] = from_f32<T>(scale * (xent::ex<T>(to_f32(zp.v[j]) - lse_z) -
-                                      xent::ex<T>(to_f32(tp.v[j]) - lse_t)));
+        o.v[j] = from_f32<T>(scale * (xent::exs<T>(to_f32(zp.v[j]), nz) -
+                                      xent::exs<T>(to_f32(tp.v[j]), nt)));
       if (!UA || (v + 1) * VEC <= a.V) {
         store_pack(dr + v * VEC, o);
       } else {
@@ -249,13 +251,14 @@ __global__ __launch_bounds__(NT) void soft_stream_u(DistillArgs a, const T* z, c
   row_terms(a, row, r, lse_z, lse_t);
   if (dz == nullptr) return;
   const float scale = a.dloss / (float)a.cnt->n_valid;
+  const float nz = xent::nl2e<T>(lse_z), nt = xent::nl2e<T>(lse_t);
   T* dr = dz + row * a.ldd;
   auto grad = [&](const Pack<T>& zp, const Pack<T>& tp, int64_t v) {
     Pack<T> o;
 #pragma unroll
     for (int j = 0; j < VEC; ++j)
-      o.v[j] = from_f32<T>(scale * (xent::ex<T>(to_f32(zp.v[j]) - lse_z) -
-                                    xent::ex<T>(to_f32(tp.v[j]) - lse_t)));
+      o.v[j] = from_f32<T>(scale * (xent::exs<T>(to_f32(zp.v[j]), nz) -
+                                    xent::exs<T>(to_f32(tp.v[j]), nt)));
     store_pack(dr + v * VEC, o);
   };
   for (int64_t v0 = tail0; v0 < n; v0 += (int64_t)U * NT) {

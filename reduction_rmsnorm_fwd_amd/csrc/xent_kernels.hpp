@@ -45,6 +45,21 @@ template <typename T> __device__ __forceinline__ float ex(float x);
 template <> __device__ __forceinline__ float ex<float>(float x) { return expf(x); }
 template <> __device__ __forceinline__ float ex<bf16>(float x) { return __expf(x); }
 
+// exp(x - m) inside a row sweep, with nb = nl2e<T>(m) formed once per shift m.  bf16
+// rows: 2^(x log2 e - m log2 e) as one fused multiply-add into the hardware 2^x, where
+// __expf(x - m) takes a subtraction, a multiplication and the same 2^x (one VALU
+// operation less per element and pass; the shift's rounding, |m| log2(e) 2^-24, stays
+// far below a bf16 step).  fp32 rows keep expf(x - m).
+constexpr float kLog2e = 1.4426950408889634f;
+template <typename T> __device__ __forceinline__ float nl2e(float m) {
+  return std::is_same<T, bf16>::value ? -m * kLog2e : m;
+}
+template <typename T> __device__ __forceinline__ float exs(float x, float nb);
+template <> __device__ __forceinline__ float exs<float>(float x, float m) { return expf(x - m); }
+template <> __device__ __forceinline__ float exs<bf16>(float x, float nb) {
+  return __builtin_amdgcn_exp2f(fmaf(x, kLog2e, nb));
+}
+
 // Count valid and bad targets of rows [0, T).  One workgroup of 1024 threads.
 __global__ __launch_bounds__(1024) void count_targets(int64_t T_, int64_t V,
                                                       const int64_t* __restrict__ tg,
@@ -216,8 +231,9 @@ __global__ __launch_bounds__(NT) void row_reg(RowArgs a, const Tin* z, Tout* dz)
 #pragma unroll
       for (int j = 1; j < VEC; ++j) vm = fmaxf(vm, to_f32(xv[i].v[j]));
       if (vm > m) { s *= ex<Tin>(m - vm); m = vm; }
+      const float nb = nl2e<Tin>(m);
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) s += ex<Tin>(to_f32(xv[i].v[j]) - m);
+      for (int j = 0; j < VEC; ++j) s += exs<Tin>(to_f32(xv[i].v[j]), nb);
     }
   }
   const float lse = block_lse<NT>(m, s, shm, shs);
@@ -236,13 +252,14 @@ __global__ __launch_bounds__(NT) void row_reg(RowArgs a, const Tin* z, Tout* dz)
   for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(xv[i].raw));
   const int64_t yv = y / VEC;          // the vector holding the target
   const int yj = (int)(y - yv * VEC);  // and its element
+  const float nl = nl2e<Tin>(lse);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int64_t v = threadIdx.x + (int64_t)i * NT;
     if (v < nvec) {
       float g[VEC];
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) g[j] = coef * ex<Tin>(to_f32(xv[i].v[j]) - lse);
+      for (int j = 0; j < VEC; ++j) g[j] = coef * exs<Tin>(to_f32(xv[i].v[j]), nl);
       if (v == yv) {
 #pragma unroll
         for (int j = 0; j < VEC; ++j)
@@ -405,8 +422,9 @@ __global__ __launch_bounds__(kPfThreads) void row_pf(RowArgs a, const Tin* z, To
 #pragma unroll
         for (int j = 1; j < VEC; ++j) vm = fmaxf(vm, to_f32(xv[i].v[j]));
         if (vm > m) { s *= ex<Tin>(m - vm); m = vm; }
+        const float nb = nl2e<Tin>(m);
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) s += ex<Tin>(to_f32(xv[i].v[j]) - m);
+        for (int j = 0; j < VEC; ++j) s += exs<Tin>(to_f32(xv[i].v[j]), nb);
       }
     }
     const float lse = block_lse<NT>(m, s, shm, shs);  // (its barrier publishes sh_zy)
@@ -418,6 +436,7 @@ __global__ __launch_bounds__(kPfThreads) void row_pf(RowArgs a, const Tin* z, To
     if (dr == nullptr) continue;
     const float scale = a.dloss / (float)a.cnt->n_valid;
     const float coef = scale * fmaf(2.f * a.zc, lse, 1.f);
+    const float nl = nl2e<Tin>(lse);
 #pragma unroll
     for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(xv[i].raw));
 #pragma unroll
@@ -426,7 +445,7 @@ __global__ __launch_bounds__(kPfThreads) void row_pf(RowArgs a, const Tin* z, To
       if (v < nvec) {
         float g[VEC];
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) g[j] = coef * ex<Tin>(to_f32(xv[i].v[j]) - lse);
+        for (int j = 0; j < VEC; ++j) g[j] = coef * exs<Tin>(to_f32(xv[i].v[j]), nl);
         if (v == yv) {
 #pragma unroll
           for (int j = 0; j < VEC; ++j)
@@ -479,8 +498,9 @@ __global__ __launch_bounds__(NT) void row_stream(RowArgs a, const Tin* z, Tout* 
 #pragma unroll
     for (int j = 1; j < VEC; ++j) vm = fmaxf(vm, to_f32(p.v[j]));
     if (vm > m) { s *= ex<Tin>(m - vm); m = vm; }
+    const float nb = nl2e<Tin>(m);
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) s += ex<Tin>(to_f32(p.v[j]) - m);
+    for (int j = 0; j < VEC; ++j) s += exs<Tin>(to_f32(p.v[j]), nb);
   };
   const int64_t tail0 = threadIdx.x + (int64_t)KEEP * NT;  // first streamed vector
   if constexpr (VEC > 1) {
@@ -521,11 +541,12 @@ __global__ __launch_bounds__(NT) void row_stream(RowArgs a, const Tin* z, Tout* 
   const float coef = scale * fmaf(2.f * a.zc, lse, 1.f);
   Tout* dr = dz + row * a.ldd;
   if constexpr (VEC > 1) {
+    const float nl = nl2e<Tin>(lse);
     auto grad = [&](const Pack<Tin>& p, int64_t v) {
       float g[VEC];
 #pragma unroll
       for (int j = 0; j < VEC; ++j) {
-        g[j] = coef * ex<Tin>(to_f32(p.v[j]) - lse);
+        g[j] = coef * exs<Tin>(to_f32(p.v[j]), nl);
         if (v * VEC + j == y) g[j] -= scale;
       }
       if constexpr (Vec<Tout>::N == VEC) {
