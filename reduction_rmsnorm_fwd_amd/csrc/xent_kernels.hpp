@@ -642,7 +642,9 @@ hipError_t launch_rows(const RowArgs& a, const Tin* z, Tout* dz, hipStream_t st,
       case 1: row_reg<Tin, Tout, 1, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
       case 2: row_reg<Tin, Tout, 2, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
       case 3: case 4: row_reg<Tin, Tout, 4, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
-      case 5: case 6: case 7: case 8: row_reg<Tin, Tout, 8, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      // 512-thread workgroups of 16 vectors per thread (114 VGPRs): two rows per CU,
+      // where 1024 threads of 8 (71 VGPRs) fit one (T 16384, V 49152: 607 -> 520 us)
+      case 5: case 6: case 7: case 8: row_reg<Tin, Tout, 16, 512><<<grid, 512, 0, st>>>(a, z, dz); break;
       case 9: case 10: case 11: case 12: row_reg<Tin, Tout, 12, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
       case 13: case 14: case 15: case 16:
         if constexpr (std::is_same<Tin, bf16>::value && std::is_same<Tout, bf16>::value) {
@@ -674,7 +676,7 @@ hipError_t launch_rows(const RowArgs& a, const Tin* z, Tout* dz, hipStream_t st,
       case 1: row_reg<Tin, Tout, 1, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
       case 2: row_reg<Tin, Tout, 2, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
       case 3: case 4: row_reg<Tin, Tout, 4, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
-      case 5: case 6: case 7: case 8: row_reg<Tin, Tout, 8, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      case 5: case 6: case 7: case 8: row_reg<Tin, Tout, 16, 512, true><<<grid, 512, 0, st>>>(a, z, dz); break;
       case 9: case 10: case 11: case 12: row_reg<Tin, Tout, 12, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
       default: row_reg<Tin, Tout, 16, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
     }
