@@ -77,10 +77,19 @@ def parse():
     p.add_argument("--no-isolated", action="store_true")
     p.add_argument("--no-configs", action="store_true",
                    help="skip the per-(config, op) records of configs 1-4")
+    p.add_argument("--config", default="1,2,3,4",
+                   help="comma list of the configs (1-4) the per-(config, op) records cover")
     p.add_argument("--only", default="", help="comma list of ops to run (profiling)")
     p.add_argument("--calib-copy", action="store_true",
                    help="first run one plain 1 GiB device copy (counter calibration)")
-    return p.parse_args()
+    a = p.parse_args()
+    try:
+        a.cids = tuple(int(c) for c in a.config.split(",") if c.strip())
+    except ValueError:
+        a.cids = (0,)
+    if any(c not in (1, 2, 3, 4) for c in a.cids):
+        p.error("--config takes configs 1-4 (config 5, the lm-head FLCE, is part of the step)")
+    return a
 
 
 class Workload:
@@ -448,7 +457,7 @@ def iso_times(torch, stream, fn, reps, scratch):
 LAUNCH_BOUND_US = 7.0  # ops whose bytes take less than this at 70% of peak: launch-bound
 
 
-def config_lines(fo, synth, torch, stream, med, reps, copy_gbs):
+def config_lines(fo, synth, torch, stream, med, reps, copy_gbs, cids=(1, 2, 3, 4)):
     """One record per (config, op) for the layer-op configs: the tiny fp32 block (T 256),
     the Qwen2.5-0.5B shapes (T 4096, vocabulary 151936), the Llama-3-8B shapes (T 8192,
     vocabulary 128256, z-loss) and the packed 16k batch (document-reset positions, 25%
@@ -461,7 +470,7 @@ def config_lines(fo, synth, torch, stream, med, reps, copy_gbs):
     time): what a plain copy of that size reaches, start-up and drain included."""
     scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     out = {}
-    for cid in (1, 2, 3, 4):
+    for cid in cids:
         cfg = synth.CONFIGS[cid]
         T, d, D, F, V = cfg.T, cfg.d, cfg.head_dim, cfg.F, cfg.V
         heads = cfg.n_q + cfg.n_kv
@@ -686,9 +695,9 @@ def gpu_bench(args):
     same = (None if args.no_probes or not hbm_bytes
             else same_size_copies(fo, torch, stream, med, hbm_bytes, args.iso_reps))
     unaligned = None if args.no_probes or only else unaligned_lines(fo, synth, torch, stream, med)
-    configs = (None if args.no_configs or only
+    configs = (None if args.no_configs or only or not args.cids
                else config_lines(fo, synth, torch, stream, med, args.iso_reps,
-                                 peaks["copy_GBps"] if peaks else None))
+                                 peaks["copy_GBps"] if peaks else None, args.cids))
     next_ops = None
     if not (args.no_next or only):
         cg = peaks["copy_GBps"] if peaks else None
@@ -894,9 +903,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only; the library has no "
-                                   "multi-GPU path (see the sharding paragraph of the design "
-                                   "notes). Run with --gpus 1."}))
+        print(json.dumps({"error": "bench.py measures one GPU: the library has no multi-GPU "
+                                   "path (every call runs on one device and stream). Run with "
+                                   "--gpus 1."}))
         sys.exit(2)
     out, wl = gpu_bench(args)
     del wl
