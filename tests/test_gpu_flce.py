@@ -167,3 +167,64 @@ def test_full_size_against_oracle(gpu):
     check_product_grad(o1["dhidden"][dh_rows], r["dhidden"], r["dhidden_abs"], "dhidden c1024")
     check_product_grad(o1["dweight"][dw_rows], r["dweight"], r["dweight_abs"], "dweight c1024",
                        rounded_out=False)
+
+
+def test_bad_targets_are_counted_and_ignored(gpu):
+    # targets outside [0, V) that are not ignore_index: counted into status, and their
+    # rows treated as ignored (no loss, +0.0 dH rows, nothing in dW)
+    cfg = synth.flce_small(64, 128, 1000, seed=21)
+    i = synth.flce_inputs(cfg)
+    t = i["targets"].clone()
+    bad = [3, 17, 40]
+    t[bad] = torch.tensor([1000, -5, 10**12])
+    o = run(gpu, i["hidden"], i["weight"], t, cfg.z_loss)
+    r = compare(i["hidden"], i["weight"], t, cfg.z_loss, o)
+    assert o["status"].item() == r["n_bad"] == 3
+    assert torch.all(o["dhidden"][bad].view(torch.int16) == 0)
+
+
+@pytest.mark.parametrize("dwt", [torch.float32, torch.bfloat16])
+def test_empty_batch(gpu, dwt):
+    h = torch.empty(0, 64, dtype=torch.bfloat16)
+    w = torch.randn(300, 64).to(torch.bfloat16)
+    o = run(gpu, h, w, torch.empty(0, dtype=torch.int64), 1e-4, dwt=dwt)
+    assert o["loss"].item() == 0.0 and o["n_valid"].item() == 0 and o["status"].item() == 0
+    assert o["dweight"].shape == (300, 64) and torch.all(o["dweight"] == 0)
+
+
+def test_forward_only_and_one_gradient(gpu):
+    # no gradient, dH only and dW only (null outputs through the C ABI): the loss and each
+    # gradient bit-identical to the call that forms both
+    import ctypes
+    cfg = synth.flce_small(300, 256, 3000, seed=31)
+    i = synth.flce_inputs(cfg)
+    h, w, t = (i[k].to(DEV) for k in ("hidden", "weight", "targets"))
+    T, H = h.shape
+    V = w.shape[0]
+    full = gpu.fo_flce_fwd_bwd(h, w, t, IGN, cfg.z_loss, 1.0, chunk_tokens=128)
+    fwd = gpu.fo_flce_fwd_bwd(h, w, t, IGN, cfg.z_loss, 1.0, chunk_tokens=128, grad=False)
+    lib = gpu.load()
+
+    def partial(dh, dw):
+        o = gpu._scalars(DEV)
+        ws = gpu._ws(lib.fo_flce_workspace(T, H, V, 128, gpu.FO_F32), DEV)
+        rc = lib.fo_flce_fwd_bwd(gpu.FO_BF16, T, H, V, gpu._ptr(h), gpu._ptr(w), gpu._ptr(t), IGN,
+                                 ctypes.c_float(cfg.z_loss), ctypes.c_float(1.0),
+                                 gpu._ptr(dh) if dh is not None else None,
+                                 gpu._ptr(dw) if dw is not None else None, gpu.FO_F32,
+                                 gpu._ptr(o["loss"]), gpu._ptr(o["z_loss"]), gpu._ptr(o["n_valid"]),
+                                 gpu._ptr(o["status"]), 128, gpu._ptr(ws), ws.numel(), gpu._stream())
+        assert rc == 0, rc
+        return o
+
+    dh = torch.empty_like(h)
+    dw = torch.empty((V, H), dtype=torch.float32, device=DEV)
+    a = partial(dh, None)
+    b = partial(None, dw)
+    torch.cuda.synchronize()
+    for o in (fwd, a, b):
+        assert torch.equal(o["loss"].cpu(), full["loss"].cpu())
+        assert torch.equal(o["z_loss"].cpu(), full["z_loss"].cpu())
+    assert fwd["dhidden"] is None and fwd["dweight"] is None
+    assert torch.equal(dh.cpu(), full["dhidden"].cpu())
+    assert torch.equal(dw.cpu(), full["dweight"].cpu())
