@@ -1,0 +1,184 @@
+"""GPU parity on seeded random shapes: widths of any length and alignment, bases off the
+16-byte grid, padded row strides, odd head counts and vocabularies, against the fp64
+oracle under the same bounds as the targeted tests.  Every case prints its parameters in
+the assertion message."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tolerance import check, check_loss, check_softmax_diff
+from test_gpu_distill import softmax_sum
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+IGN = -100
+TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def width(g):
+    # short rows, rows around the vector and wave boundaries, and long rows
+    return int(g.choice([g.integers(1, 17), g.integers(17, 600), g.integers(600, 4200),
+                         g.integers(4200, 9000)]))
+
+
+def view(g, T, n, dt, scale=1.0, shift=0.0):
+    """A [T, n] view into a larger buffer: base 0-7 elements off, row stride n + 0-9; the
+    view (on the device) and its values (on the host)."""
+    off, pad = int(g.integers(0, 8)), int(g.integers(0, 10))
+    buf = torch.from_numpy(g.standard_normal((T, n + off + pad)) * scale + shift).float().to(TD[dt])
+    return buf.to(DEV)[:, off:off + n], buf[:, off:off + n].clone()
+
+
+def cases(n, seed):
+    g = np.random.default_rng(seed)
+    return [(int(s), "bf16" if s % 3 else "f32") for s in g.integers(0, 2**31, n)]
+
+
+@pytest.mark.parametrize("seed,dt", cases(40, 1))
+def test_rmsnorm(gpu, seed, dt):
+    g = np.random.default_rng(seed)
+    T, d = int(g.integers(1, 300)), width(g)
+    eps = float(g.choice([1e-6, 1e-5]))
+    x, xh = view(g, T, d, dt)
+    dy, dyh = view(g, T, d, dt)
+    w, wh = view(g, 1, d, dt, 0.1, 1.0)
+    y, rstd = gpu.fo_rmsnorm_fwd(x, w[0], eps)
+    dx, dw = gpu.fo_rmsnorm_bwd(dy, x, w[0], rstd, eps)
+    torch.cuda.synchronize()
+    ry, rr = oracle.rmsnorm_fwd(xh, wh[0], eps)
+    rdx, rdw = oracle.rmsnorm_bwd(dyh, xh, wh[0], eps)
+    tag = f"rmsnorm seed={seed} {dt} T={T} d={d}"
+    check(y.cpu(), ry, dt, tag + " y", single_rounding=True)
+    check(rstd.cpu(), rr, "f32", tag + " rstd")
+    check(dx.cpu(), rdx, dt, tag + " dx", single_rounding=True)
+    check(dw.cpu(), rdw, "f32", tag + " dw")
+
+
+@pytest.mark.parametrize("seed,dt", cases(30, 2))
+def test_layernorm(gpu, seed, dt):
+    g = np.random.default_rng(seed)
+    T, d = int(g.integers(1, 300)), width(g)
+    x, xh = view(g, T, d, dt, 1.0, 0.5)
+    dy, dyh = view(g, T, d, dt)
+    w, wh = view(g, 1, d, dt, 0.1, 1.0)
+    b, bh = view(g, 1, d, dt, 0.1)
+    y, mean, rstd = gpu.fo_layernorm_fwd(x, w[0], b[0], 1e-5)
+    dx, dw, db = gpu.fo_layernorm_bwd(dy, x, w[0], mean, rstd)
+    torch.cuda.synchronize()
+    ry, rm, rr = oracle.layernorm_fwd(xh, wh[0], bh[0], 1e-5)
+    rdx, rdw, rdb = oracle.layernorm_bwd(dyh, xh, wh[0], 1e-5)
+    tag = f"layernorm seed={seed} {dt} T={T} d={d}"
+    check(y.cpu(), ry, dt, tag + " y", single_rounding=True)
+    check(mean.cpu(), rm, "f32", tag + " mean")
+    check(rstd.cpu(), rr, "f32", tag + " rstd")
+    check(dx.cpu(), rdx, dt, tag + " dx", single_rounding=True)
+    check(dw.cpu(), rdw, "f32", tag + " dw")
+    check(db.cpu(), rdb, "f32", tag + " db")
+
+
+@pytest.mark.parametrize("seed,dt", cases(30, 3))
+def test_swiglu(gpu, seed, dt):
+    g = np.random.default_rng(seed)
+    T, F = int(g.integers(1, 200)), width(g)
+    gate, gh = view(g, T, F, dt, 2.0)
+    up, uh = view(g, T, F, dt)
+    dh, dhh = view(g, T, F, dt)
+    h = gpu.fo_swiglu_fwd(gate, up)
+    dg, du = gpu.fo_swiglu_bwd(dh, gate, up)
+    torch.cuda.synchronize()
+    rg, ru = oracle.swiglu_bwd(dhh, gh, uh)
+    tag = f"swiglu seed={seed} {dt} T={T} F={F}"
+    check(h.cpu(), oracle.swiglu_fwd(gh, uh), dt, tag + " h", single_rounding=True)
+    check(dg.cpu(), rg, dt, tag + " dgate", single_rounding=True)
+    check(du.cpu(), ru, dt, tag + " dup", single_rounding=True)
+
+
+@pytest.mark.parametrize("seed,dt", cases(30, 4))
+def test_rope(gpu, seed, dt):
+    g = np.random.default_rng(seed)
+    T = int(g.integers(1, 100))
+    nkv = int(g.integers(1, 5))
+    nq = nkv * int(g.integers(1, 5))
+    D = 2 * int(g.integers(1, 129))
+    theta = float(g.choice([1e4, 5e5, 1e6]))
+    # packed positions: documents of random lengths, each counting from 0
+    pos = np.concatenate([np.arange(n) for n in g.integers(1, 40, T)])[:T]
+    pos = torch.from_numpy(pos + int(g.choice([0, 0, 5000]))).long()
+    q, qh = view(g, T, nq * D, dt)
+    k, kh = view(g, T, nkv * D, dt)
+    q3, k3 = q.unflatten(1, (nq, D)), k.unflatten(1, (nkv, D))
+    gpu.fo_rope_fwd(q3, k3, pos.to(DEV), theta)
+    torch.cuda.synchronize()
+    rq, rk = oracle.rope_fwd(qh.unflatten(1, (nq, D)), kh.unflatten(1, (nkv, D)), pos, theta)
+    tag = f"rope seed={seed} {dt} T={T} heads={nq}/{nkv} D={D}"
+    check(q3.cpu(), rq, dt, tag + " q", single_rounding=True)
+    check(k3.cpu(), rk, dt, tag + " k", single_rounding=True)
+
+
+@pytest.mark.parametrize("seed,dt", cases(30, 5))
+def test_cross_entropy(gpu, seed, dt):
+    g = np.random.default_rng(seed)
+    T = int(g.integers(1, 48))
+    V = int(g.choice([g.integers(1, 600), g.integers(600, 20000), g.integers(20000, 70000)]))
+    zc = float(g.choice([0.0, 1e-4, 1e-3]))
+    z, zh = view(g, T, V, dt, 2.0)
+    t = torch.from_numpy(g.integers(0, V, T)).long()
+    t[torch.from_numpy(g.random(T) < 0.2)] = IGN
+    if T > 2:
+        t[1] = V  # a bad target: counted, treated as ignored
+    o = gpu.fo_xent_fwd_bwd(z, t.to(DEV), IGN, zc, 0.7)
+    torch.cuda.synchronize()
+    r = oracle.xent_fwd_bwd(zh, t, IGN, zc, 0.7)
+    tag = f"xent seed={seed} {dt} T={T} V={V}"
+    check_loss(o["loss"].item(), r["loss"], tag + " loss")
+    check_loss(o["z_loss"].item(), r["z_loss"], tag + " z_loss")
+    assert o["n_valid"].item() == r["n_valid"] and o["status"].item() == r["n_bad"], tag
+    check(o["dlogits"].cpu(), r["dlogits"], dt, tag + " dlogits", single_rounding=True)
+
+
+@pytest.mark.parametrize("seed,dt", cases(24, 6))
+def test_distillation(gpu, seed, dt):
+    g = np.random.default_rng(seed)
+    T = int(g.integers(1, 32))
+    V = int(g.choice([g.integers(1, 600), g.integers(600, 20000), g.integers(20000, 70000)]))
+    z, zh = view(g, T, V, dt, 3.0)
+    zt, zth = view(g, T, V, dt, 2.0)
+    mask = torch.from_numpy((g.random(T) > 0.2).astype(np.uint8))
+    o = gpu.fo_distill_fwd_bwd(z, zt, mask.to(DEV), 1.3)
+    torch.cuda.synchronize()
+    r = oracle.distill_fwd_bwd(zh, zth, mask, 1.3)
+    tag = f"distill seed={seed} {dt} T={T} V={V}"
+    assert o["n_valid"].item() == r["n_valid"], tag
+    check_loss(o["loss"].item(), r["loss"], tag + " loss")
+    check_loss(o["kl"].item(), r["kl"], tag + " kl")
+    keep = mask.numpy() != 0
+    n = max(1, int(keep.sum()))
+    check_softmax_diff(o["dlogits"].cpu(), r["dlogits"], softmax_sum(zh, zth, keep, 1.3 / n),
+                       tag + " dlogits", rounded_out=dt == "bf16")
+
+
+@pytest.mark.parametrize("seed", [int(s) for s in np.random.default_rng(7).integers(0, 2**31, 12)])
+def test_fused_linear_cross_entropy(gpu, seed):
+    from tolerance import check_bf16, check_product_grad
+    g = np.random.default_rng(seed)
+    T = int(g.integers(1, 160))
+    H = 8 * int(g.integers(1, 40))
+    V = int(g.choice([g.integers(1, 300), g.integers(300, 5000)]))
+    chunk = int(g.choice([0, 16, 64, 100]))
+    zc = float(g.choice([0.0, 1e-4]))
+    h = torch.from_numpy(g.standard_normal((T, H))).to(torch.bfloat16)
+    w = torch.from_numpy(0.05 * g.standard_normal((V, H))).to(torch.bfloat16)
+    t = torch.from_numpy(g.integers(0, V, T)).long()
+    t[torch.from_numpy(g.random(T) < 0.15)] = IGN
+    o = gpu.fo_flce_fwd_bwd(h.to(DEV), w.to(DEV), t.to(DEV), IGN, zc, 1.0, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    r = oracle.flce_fwd_bwd(h, w, t, IGN, zc, 1.0, abs_products=True)
+    tag = f"flce seed={seed} T={T} H={H} V={V} chunk={chunk}"
+    check_loss(o["loss"].item(), r["loss"], tag + " loss")
+    check_loss(o["z_loss"].item(), r["z_loss"], tag + " z_loss")
+    assert o["n_valid"].item() == r["n_valid"], tag
+    check_bf16(o["dhidden"].cpu(), r["dhidden"], tag + " dhidden")
+    check_product_grad(o["dhidden"].cpu(), r["dhidden"], r["dhidden_abs"], tag + " dhidden")
+    check_product_grad(o["dweight"].cpu(), r["dweight"], r["dweight_abs"], tag + " dweight",
+                       rounded_out=False)
