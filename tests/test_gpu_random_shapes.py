@@ -182,3 +182,60 @@ def test_fused_linear_cross_entropy(gpu, seed):
     check_product_grad(o["dhidden"].cpu(), r["dhidden"], r["dhidden_abs"], tag + " dhidden")
     check_product_grad(o["dweight"].cpu(), r["dweight"], r["dweight_abs"], tag + " dweight",
                        rounded_out=False)
+
+
+@pytest.mark.parametrize("seed,dt", cases(24, 8))
+def test_mlp_activations(gpu, seed, dt):
+    g = np.random.default_rng(seed)
+    act = str(g.choice(["silu", "gelu", "relu"]))
+    T, F = int(g.integers(1, 200)), width(g)
+    gate, gh = view(g, T, F, dt, 2.0)
+    up, uh = view(g, T, F, dt)
+    dh, dhh = view(g, T, F, dt)
+    tag = f"{act} seed={seed} {dt} T={T} F={F}"
+    h = gpu.fo_glu_fwd(act, gate, up)
+    dg, du = gpu.fo_glu_bwd(act, dh, gate, up)
+    y = gpu.fo_act_fwd(act, gate)
+    dx = gpu.fo_act_bwd(act, dh, gate)
+    torch.cuda.synchronize()
+    rg, ru = oracle.glu_bwd(dhh, gh, uh, act)
+    check(h.cpu(), oracle.glu_fwd(gh, uh, act), dt, tag + " glu h", single_rounding=True)
+    check(dg.cpu(), rg, dt, tag + " glu dgate", single_rounding=True)
+    check(du.cpu(), ru, dt, tag + " glu dup", single_rounding=True)
+    check(y.cpu(), oracle.act_fwd(gh, act), dt, tag + " act y", single_rounding=True)
+    check(dx.cpu(), oracle.act_bwd(dhh, gh, act), dt, tag + " act dx", single_rounding=True)
+
+
+@pytest.mark.parametrize("seed", [int(s) for s in np.random.default_rng(9).integers(0, 2**31, 10)])
+def test_adamw(gpu, seed):
+    from tolerance import check_f32
+    g = np.random.default_rng(seed)
+    n = int(g.integers(1, 40))
+    sizes = [int(g.choice([g.integers(1, 9), g.integers(9, 5000), g.integers(5000, 70000)]))
+             for _ in range(n)]
+    lr, b1, b2, wd, step = 3e-4, 0.9, 0.95, 0.1, int(g.integers(1, 1000))
+    ss, bc, df = oracle.adamw_scalars(lr, b1, b2, wd, step)
+    f = lambda x: float(np.float32(x))  # noqa: E731
+    sc = dict(step_size=f(ss), beta1=f(b1), beta2=f(b2), bias_correction=f(bc),
+              decay_factor=f(df), eps=f(1e-8))
+    host = {k: [torch.from_numpy(g.standard_normal(s) * sd).float() for s in sizes]
+            for k, sd in (("p", 1.0), ("g", 0.1), ("m", 0.01))}
+    host["v"] = [torch.from_numpy(np.abs(g.standard_normal(s)) * 1e-4).float() for s in sizes]
+    dev = {}
+    for k, ts in host.items():  # each tensor 0-3 elements into its buffer (misaligned views)
+        dev[k] = []
+        for t in ts:
+            o = int(g.integers(0, 4))
+            buf = torch.empty(t.numel() + o, dtype=torch.float32, device=DEV)
+            buf[o:].copy_(t.to(DEV))
+            dev[k].append(buf[o:])
+    gpu.fo_adamw_step(dev["p"], dev["g"], dev["m"], dev["v"], **sc)
+    torch.cuda.synchronize()
+    for i in range(n):
+        rp, rm, rv = oracle.adamw_step(host["p"][i], host["g"][i], host["m"][i], host["v"][i],
+                                       sc["step_size"], sc["beta1"], sc["beta2"],
+                                       sc["bias_correction"], sc["decay_factor"], sc["eps"])
+        tag = f"adamw seed={seed} tensor {i} of {n}, {sizes[i]} elements"
+        check_f32(dev["p"][i].cpu(), rp, tag + " p")
+        check_f32(dev["m"][i].cpu(), rm, tag + " m")
+        check_f32(dev["v"][i].cpu(), rv, tag + " v")
