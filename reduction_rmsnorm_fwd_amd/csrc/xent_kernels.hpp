@@ -637,11 +637,20 @@ hipError_t launch_rows(const RowArgs& a, const Tin* z, Tout* dz, hipStream_t st,
       else row_reg<Tin, Tout, 4, 256><<<grid, 256, 0, st>>>(a, z, dz);
       return hipGetLastError();
     }
+    // rows of up to 3072 vectors: 8 vectors per thread in 256- or 512-thread workgroups,
+    // so that 3-7 rows share a CU where 1024-thread workgroups of 2-4 vectors fit two
+    // (T 8192: V 16384 135 -> 104 us, V 24000 162 -> 146 us)
+    if (nvec <= 256 * 8) {
+      row_reg<Tin, Tout, 8, 256><<<grid, 256, 0, st>>>(a, z, dz);
+      return hipGetLastError();
+    }
+    if (nvec <= 384 * 8) {
+      row_reg<Tin, Tout, 8, 512><<<grid, 512, 0, st>>>(a, z, dz);
+      return hipGetLastError();
+    }
     const int64_t per = ceil_div(nvec, 1024);
     switch (per) {
-      case 1: row_reg<Tin, Tout, 1, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
-      case 2: row_reg<Tin, Tout, 2, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
-      case 3: case 4: row_reg<Tin, Tout, 4, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      case 1: case 2: case 3: case 4: row_reg<Tin, Tout, 4, 1024><<<grid, 1024, 0, st>>>(a, z, dz); break;
       // 512-thread workgroups of 16 vectors per thread (114 VGPRs): two rows per CU,
       // where 1024 threads of 8 (71 VGPRs) fit one (T 16384, V 49152: 607 -> 520 us)
       case 5: case 6: case 7: case 8: row_reg<Tin, Tout, 16, 512><<<grid, 512, 0, st>>>(a, z, dz); break;
@@ -672,10 +681,16 @@ hipError_t launch_rows(const RowArgs& a, const Tin* z, Tout* dz, hipStream_t st,
       else row_reg<Tin, Tout, 4, 256, true><<<grid, 256, 0, st>>>(a, z, dz);
       return hipGetLastError();
     }
+    if (nvec <= 256 * 8) {
+      row_reg<Tin, Tout, 8, 256, true><<<grid, 256, 0, st>>>(a, z, dz);
+      return hipGetLastError();
+    }
+    if (nvec <= 384 * 8) {
+      row_reg<Tin, Tout, 8, 512, true><<<grid, 512, 0, st>>>(a, z, dz);
+      return hipGetLastError();
+    }
     switch (ceil_div(nvec, 1024)) {
-      case 1: row_reg<Tin, Tout, 1, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
-      case 2: row_reg<Tin, Tout, 2, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
-      case 3: case 4: row_reg<Tin, Tout, 4, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
+      case 1: case 2: case 3: case 4: row_reg<Tin, Tout, 4, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
       case 5: case 6: case 7: case 8: row_reg<Tin, Tout, 16, 512, true><<<grid, 512, 0, st>>>(a, z, dz); break;
       case 9: case 10: case 11: case 12: row_reg<Tin, Tout, 12, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;
       default: row_reg<Tin, Tout, 16, 1024, true><<<grid, 1024, 0, st>>>(a, z, dz); break;

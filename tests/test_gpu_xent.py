@@ -55,12 +55,13 @@ def test_config1_as_stated(gpu):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("V", [4097, 7, 8, 1000, 20000, 32001, 50257, 65536, 65544, 131072,
-                               131080, 151936, 163840, 81920, 200000])
+@pytest.mark.parametrize("V", [4097, 7, 8, 1000, 12000, 12001, 16384, 20000, 32001, 50257,
+                               65536, 65544, 131072, 131080, 151936, 163840, 81920, 200000])
 def test_vocab_sizes(gpu, dtype, V):
-    # rows off the 16-byte grid (4097, 7, 32001, 50257: every row starts at another
-    # alignment), tiny and register-resident rows (fp32 20000, bf16 65536: the 512-thread
-    # form, the latter filling its 16 vectors per thread; 65544 one vector past it),
+    # rows off the 16-byte grid (4097, 7, 12001, 32001, 50257: every row starts at another
+    # alignment), tiny and register-resident rows (bf16 12000 and 16384: 256 threads of 8
+    # vectors, the latter full; bf16 20000 and fp32 12000: 512 threads of 8; fp32 20000,
+    # bf16 65536: 512 threads of 16, the latter full; 65544 one vector past it),
     # rows split between registers and LDS (bf16 131080: 17 vectors per thread, 151936:
     # 19, 163840: 20, the most; fp32 81920: 20) and streaming rows (longer)
     g = torch.Generator().manual_seed(V)
