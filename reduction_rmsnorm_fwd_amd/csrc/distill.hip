@@ -13,11 +13,11 @@
 // D/s_t + (m_z - m_t) + log(s_z/s_t): a sum of terms of the size of the KL itself,
 // where the difference of the two cross-entropies would cancel two logsumexp-sized
 // values.  A second sweep over the same values writes dz.  A workgroup per row streams
-// both rows with several 16-byte loads of each in flight per thread; for rows longer
-// than 8192 vectors (512 threads per row then, two rows per CU) the first 8 vectors per
-// thread of each row stay in registers between the sweeps, and the second sweep
-// re-reads the rest, mostly from L2 and the Infinity Cache, so HBM sees each input
-// about once and dz once (3 T V b).  Unaligned rows
+// both rows with several 16-byte loads of each in flight per thread; each thread keeps
+// up to 8 vectors of each row in registers between the sweeps (rows of up to 2048
+// vectors whole, in 256-thread workgroups; longer rows in 512-thread workgroups, two per
+// CU), and the second sweep re-reads the rest, mostly from L2 and the Infinity Cache,
+// so HBM sees each input about once and dz once (3 T V b).  Unaligned rows
 // still move their full vectors as 16-byte accesses.
 #include "xent_kernels.hpp"
 
@@ -331,13 +331,15 @@ int distill_impl(const DistillArgs& a0, const T* z, const T* zt, T* dz, float* l
     const int64_t nvec = a.V / VEC;
     const dim3 grid((unsigned)a.T), block(kRowThreads);
     if (vec) {
-      // both rows streamed; beyond 8 vectors per 1024 threads the first 8 of each row
-      // stay in registers between the sweeps (T 8192, bf16: V 4096 329 -> 181 us, 32000
-      // 474 -> 398, 128256 1525 -> 1324 against rows held on chip, one per CU), in
-      // 512-thread workgroups: at 127 VGPRs two rows then share a CU, where 1024 threads
-      // fit one (V 128256: 1303 -> 1268 us)
-      if (nvec <= 4 * 256) soft_stream_u<T, 4, 0, 256><<<grid, dim3(256), 0, st>>>(a, z, zt, dz);
-      else if (nvec <= 8 * kRowThreads) soft_stream_u<T, 4, 0><<<grid, block, 0, st>>>(a, z, zt, dz);
+      // Each thread keeps up to 8 vectors of each row in registers between the sweeps:
+      // rows of up to 2048 vectors whole in 256-thread workgroups (several rows per CU),
+      // longer rows in 512-thread workgroups (two per CU at 127 VGPRs) with their first
+      // 4096 vectors kept and the rest streamed twice, 4 loads of each row in flight per
+      // thread.  T 8192, bf16, against 1024 threads that kept nothing up to 8192 vectors:
+      // V 16384 296 -> 219 us, 32000 418 -> 347, 65536 725 -> 646; 512 against 1024
+      // threads keeping 8 at V 128256: 1303 -> 1268 us.
+      if (nvec <= 4 * 256) soft_stream_u<T, 4, 4, 256><<<grid, dim3(256), 0, st>>>(a, z, zt, dz);
+      else if (nvec <= 8 * 256) soft_stream_u<T, 4, 8, 256><<<grid, dim3(256), 0, st>>>(a, z, zt, dz);
       else soft_stream_u<T, 4, 8, 512><<<grid, dim3(512), 0, st>>>(a, z, zt, dz);
     } else if (reinterpret_cast<uintptr_t>(z) % sizeof(T) == 0 &&
                reinterpret_cast<uintptr_t>(zt) % sizeof(T) == 0 &&
