@@ -7,19 +7,21 @@
 //   dx = r (w*dy) - r^3 x mean_j(w_j dy_j x_j),  dw[j] = sum_t dy[t,j] x[t,j] r[t]
 //
 // Fast path (16-byte aligned rows whose length is a multiple of the vector): the
-// forward gives one wave64 per row and holds the row in registers between the sum of
-// squares and the write, so x is read from HBM exactly once.  The backward gives each
-// row RW waves (RW grows with d so a lane holds at most 16 elements per operand); every
-// lane owns a fixed set of columns and accumulates their dw contribution in registers
-// across all the rows its workgroup visits.  The waves of a workgroup are folded
-// through LDS in a fixed order into one fp32 partial row per workgroup (at most 512
-// workgroups, so the partials stay a few MB), and a second small kernel sums the
-// partial rows in a fixed order.  Rows that start off a 16-byte boundary or whose
+// forward gives each row RW wave64s (one up to 8 vectors per lane, 2-16 for longer rows,
+// the row sums then combined through LDS) and holds the row in registers between the
+// sum of squares and the write, so x is read from HBM exactly once.  The backward gives
+// each row RW waves (RW grows with d so a lane holds at most 16 elements per operand,
+// up to 16 waves); every lane owns a fixed set of columns and accumulates their dw
+// contribution in registers across all the rows its workgroup visits.  The waves of a
+// workgroup are folded through LDS in a fixed order into one fp32 partial row per
+// workgroup (a workgroup of one row group writes it from registers), at most 512
+// workgroups, and a second small kernel sums the partial rows in a fixed order.  Rows that start off a 16-byte boundary or whose
 // length is not a multiple of the vector take the same kernels (template flag UA):
 // their full vectors are still moved as 16-byte accesses at element-aligned addresses,
 // and the d % VEC elements past the last full vector go to the first lanes of the row's
-// first wave, one element each.  Rows too long for the registers take a
-// workgroup-per-row path that reads the row twice (the second read from L2).
+// first wave, one element each.  Rows too long for the registers (beyond 131072 bf16 /
+// 65536 fp32 elements forward, 16384 backward) take a workgroup-per-row path that
+// reads the row twice (the second read from L2).
 #include <initializer_list>
 #include <type_traits>
 
@@ -28,8 +30,11 @@
 namespace fo {
 namespace {
 
-constexpr int kFwdWaves = 4;     // rows (waves) per workgroup, forward
-constexpr int kBwdWaves = 8;     // waves per workgroup, backward
+constexpr int kFwdWaves = 4;     // waves per workgroup, forward (rows of one wave)
+constexpr int kBwdWaves = 8;     // waves per workgroup, backward (rows of <= 8 waves)
+constexpr int kMaxRowWaves = 16;  // waves per row at most (one 1024-thread workgroup)
+constexpr int kFwdMaxNV = 8;     // vectors per lane before a row takes more waves
+constexpr size_t kMaxLds = 160 * 1024;  // LDS of one workgroup on gfx950
 constexpr int kMaxPartials = 512;  // dw partial rows (workgroups of the backward)
 constexpr int kGenericThreads = 256;
 
@@ -62,26 +67,59 @@ __device__ __forceinline__ float centred(float w, float g, float m) {
 }
 
 // ----------------------------------------------------------------- forward, fast
-// LN: LayerNorm (mean subtracted before the variance, bias added); the row is still
-// read once: mean and centred variance are two sweeps over the registers.
-// nvec: full vectors per row (d / VEC); UA: lanes k < d % VEC also own tail element k.
-template <typename T, int NV, bool LN, bool UA>
-__global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
+// Sum over the RW waves of a row, combined in wave order; every lane of the row gets
+// the total.  With RW > 1 every wave of the workgroup must call it (two barriers).
+template <int RW>
+__device__ __forceinline__ float row_sum(float v, float* part) {
+  v = wave_sum(v);
+  if constexpr (RW > 1) {
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) part[wave] = v;
+    __syncthreads();
+    const int base = wave - wave % RW;
+    v = 0.f;
+#pragma unroll
+    for (int k = 0; k < RW; ++k) v += part[base + k];
+    __syncthreads();  // the slots are rewritten by the next sum
+  }
+  return v;
+}
+
+// threads of a forward (backward) workgroup whose rows take RW waves each
+constexpr int fwd_threads(int RW) { return (RW > kFwdWaves ? RW : kFwdWaves) * kWave; }
+constexpr int bwd_threads(int RW) { return (RW > kBwdWaves ? RW : kBwdWaves) * kWave; }
+
+// A row takes RW waves (RW = 1 up to rows of kFwdMaxNV vectors per lane, more for
+// longer rows); lane (wr, l) of a row holds the vectors (wr*64 + l) + i*RW*64, i < NV,
+// in registers between the sums and the write, so x is read from HBM exactly once.
+// LN: LayerNorm (mean subtracted before the variance, bias added); mean and centred
+// variance are two sweeps over the registers.
+// nvec: full vectors per row (d / VEC); UA: lanes k < d % VEC of the row's first wave
+// also own tail element k.
+template <typename T, int NV, int RW, bool LN, bool UA>
+__global__ __launch_bounds__(fwd_threads(RW)) void rmsnorm_fwd_wave(
     int64_t T_, int nvec, int d, const T* __restrict__ x, int64_t ldx,
     const T* __restrict__ w, const T* __restrict__ b, float eps, T* y, int64_t ldy,
     float* __restrict__ mean, float* __restrict__ rstd) {
   constexpr int VEC = Vec<T>::N;
+  constexpr int RG = fwd_threads(RW) / kWave / RW;  // rows per workgroup
+  __shared__ float part[RW > 1 ? fwd_threads(RW) / kWave : 1];
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * kFwdWaves + (threadIdx.x / kWave);
-  if (row >= T_) return;
-  const T* xr = x + row * ldx;
-  const int tcol = nvec * VEC + lane;  // this lane's tail element (UA)
-  const bool tl = UA && tcol < d;
+  const int wave = threadIdx.x / kWave;
+  const int wr = wave % RW;
+  const int64_t row = (int64_t)blockIdx.x * RG + wave / RW;
+  // a one-wave row leaves at once; waves of wider rows stay for the barriers
+  if (RW == 1 && row >= T_) return;
+  const bool live = row < T_;
+  const int vbase = wr * kWave + lane;
+  const T* xr = x + (live ? row : 0) * ldx;
+  const int tcol = nvec * VEC + lane;  // this lane's tail element (UA, first wave)
+  const bool tl = UA && live && wr == 0 && tcol < d;
   Pack<T> xv[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int v = lane + i * kWave;
-    if (v < nvec) xv[i] = ld_vec<T, true>(xr, v);
+    const int v = vbase + i * RW * kWave;
+    if (live && v < nvec) xv[i] = ld_vec<T, true>(xr, v);
     else xv[i].raw = u32x4{0, 0, 0, 0};
   }
   const float xt = tl ? to_f32(xr[tcol]) : 0.f;
@@ -92,7 +130,7 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
     for (int i = 0; i < NV; ++i)
 #pragma unroll
       for (int j = 0; j < VEC; ++j) s += to_f32(xv[i].v[j]);
-    mu = wave_sum(UA ? s + xt : s) / (float)d;
+    mu = row_sum<RW>(UA ? s + xt : s, part) / (float)d;
     // re-widen for the variance sweep instead of holding fp32 copies (as below)
 #pragma unroll
     for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(xv[i].raw));
@@ -106,14 +144,16 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
         const float f = to_f32(xv[i].v[j]) - mu;
         // unused slots hold 0, not mu.  (Aligned rows test per element: the same set,
         // and measured 9% faster at T 8192, d 4096 bf16 than the per-vector test.)
-        if (UA ? lane + i * kWave < nvec : (lane + i * kWave) * VEC + j < d) ss = fmaf(f, f, ss);
+        const int v = vbase + i * RW * kWave;
+        if (UA ? v < nvec : v * VEC + j < d) ss = fmaf(f, f, ss);
       } else {
         const float f = to_f32(xv[i].v[j]);
         ss = fmaf(f, f, ss);
       }
     }
   if (tl) ss = fmaf(xt - mu, xt - mu, ss);
-  ss = wave_sum(ss);
+  ss = row_sum<RW>(ss, part);
+  if (!live) return;
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
   T* yr = y + row * ldy;
   // re-widen from the packed row instead of holding fp32 copies: fewer VGPRs, more
@@ -122,7 +162,7 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
   for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(xv[i].raw));
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int v = lane + i * kWave;
+    const int v = vbase + i * RW * kWave;
     if (v < nvec) {
       const Pack<T> wv = ld_vec<T, false>(w, v);
       Pack<T> o;
@@ -142,7 +182,7 @@ __global__ __launch_bounds__(kFwdWaves * kWave) void rmsnorm_fwd_wave(
     if constexpr (LN) yr[tcol] = from_f32<T>(fmaf((xt - mu) * r, to_f32(w[tcol]), to_f32(b[tcol])));
     else yr[tcol] = from_f32<T>(xt * r * to_f32(w[tcol]));
   }
-  if (lane == 0) {
+  if (lane == 0 && wr == 0) {
     if (rstd != nullptr) rstd[row] = r;
     if constexpr (LN) {
       if (mean != nullptr) mean[row] = mu;
@@ -218,15 +258,16 @@ __global__ __launch_bounds__(kGenericThreads) void rmsnorm_fwd_block(
 // nvec: full vectors per row (d / VEC); UA: lanes k < d % VEC of each row group's first
 // wave also own tail element k, held as scalars beside the vectors.
 template <typename T, int NV, int RW, bool LN, bool UA>
-__global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
+__global__ __launch_bounds__(bwd_threads(RW)) void rmsnorm_bwd_wave(
     int64_t T_, int nvec, int d, const T* dy, int64_t lddy, const T* x, int64_t ldx,
     const T* __restrict__ w, const float* __restrict__ mean, const float* __restrict__ rstd,
-    float eps, T* dx, int64_t lddx, float* __restrict__ partial) {
+    float eps, T* dx, int64_t lddx, float* __restrict__ partial, int direct) {
   constexpr int VEC = Vec<T>::N;
-  constexpr int RG = kBwdWaves / RW;  // rows in flight per workgroup
+  constexpr int NW = bwd_threads(RW) / kWave;  // waves per workgroup
+  constexpr int RG = NW / RW;         // rows in flight per workgroup
   constexpr int NB = LN ? NV : 1;     // db accumulators (LayerNorm only)
   extern __shared__ float fold[];     // [d], or [2d] for LN
-  __shared__ float xdot[kBwdWaves], xss[kBwdWaves];
+  __shared__ float xdot[NW], xss[NW];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rg = wave / RW, wr = wave % RW;
@@ -382,6 +423,41 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
     gt = gtn;
     xt = xtn;
   }
+  constexpr int kCols = LN ? 2 : 1;
+  float* out = partial + (int64_t)blockIdx.x * kCols * d;
+  if constexpr (RG == 1) {
+    if (direct != 0) {
+      // one row group: every column belongs to one lane, which writes it from its
+      // registers (direct 2: as 16-byte stores, the partial row being 16-byte aligned)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int v = vbase + i * RW * kWave;
+        if (v < nvec) {
+          if (!UA && direct == 2) {
+#pragma unroll
+            for (int j = 0; j < VEC; j += 4) {
+              *reinterpret_cast<float4*>(out + v * VEC + j) =
+                  make_float4(acc[i][j], acc[i][j + 1], acc[i][j + 2], acc[i][j + 3]);
+              if constexpr (LN)
+                *reinterpret_cast<float4*>(out + d + v * VEC + j) =
+                    make_float4(accb[i][j], accb[i][j + 1], accb[i][j + 2], accb[i][j + 3]);
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+              out[v * VEC + j] = acc[i][j];
+              if constexpr (LN) out[d + v * VEC + j] = accb[i][j];
+            }
+          }
+        }
+      }
+      if (tl) {
+        out[tcol] = acct;
+        if constexpr (LN) out[d + tcol] = accbt;
+      }
+      return;
+    }
+  }
   // fold the row groups' column partials in order 0,1,2,... (RW waves of a group own
   // disjoint columns, so they write their slots in the same step)
   for (int s = 0; s < RG; ++s) {
@@ -408,8 +484,6 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void rmsnorm_bwd_wave(
     }
     __syncthreads();
   }
-  constexpr int kCols = LN ? 2 : 1;
-  float* out = partial + (int64_t)blockIdx.x * kCols * d;
   for (int j = threadIdx.x; j < kCols * d; j += blockDim.x) out[j] = fold[j];
 }
 
@@ -566,23 +640,31 @@ bool vector_ok(int64_t d, const void* a, int64_t lda, const void* b, int64_t ldb
   constexpr int VEC = Vec<T>::N;
   return d % VEC == 0 && lda % VEC == 0 && ldb % VEC == 0 && ldc % VEC == 0 &&
          aligned16(a) && aligned16(b) && aligned16(c) && aligned16(w) &&
-         d <= 16 * kWave * VEC;
+         d / VEC <= (int64_t)kMaxRowWaves * kWave * 16;
 }
 
 // Rows of any alignment and length that still fit the registers of the wave kernels
-// (UA = true there): element-aligned pointers, at most 16 full vectors per lane (the
-// tail of fewer than VEC elements rides on scalar registers beside them).
+// (UA = true there): element-aligned pointers, at most 16 full vectors per lane of
+// kMaxRowWaves waves (the tail of fewer than VEC elements rides on scalar registers
+// beside them).  The backward fits fewer (bwd_fits).
 template <typename T>
 bool unaligned_ok(int64_t d, std::initializer_list<const void*> ptrs) {
-  bool ok = d / Vec<T>::N <= 16 * kWave;
+  bool ok = d / Vec<T>::N <= (int64_t)kMaxRowWaves * kWave * 16;
   for (const void* p : ptrs) ok = ok && reinterpret_cast<uintptr_t>(p) % sizeof(T) == 0;
   return ok;
 }
 
-// vectors per lane of the forward wave kernel for rows of nvec vectors
-inline int nv_for(int64_t nvec) {
-  const int64_t per = ceil_div(nvec, kWave);
-  return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
+// Launch plan of the forward: waves per row (rw, the fewest that keep a lane at
+// kFwdMaxNV vectors, up to kMaxRowWaves) and vectors per lane (nv).
+struct FwdPlan {
+  int rw, nv;
+};
+inline FwdPlan fwd_plan(int64_t nvec) {
+  FwdPlan p{1, 1};
+  while (p.rw < kMaxRowWaves && ceil_div(nvec, (int64_t)p.rw * kWave) > kFwdMaxNV) p.rw *= 2;
+  const int64_t per = ceil_div(nvec, (int64_t)p.rw * kWave);
+  p.nv = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
+  return p;
 }
 
 template <typename T, bool LN>
@@ -595,28 +677,53 @@ int fwd_impl(int64_t T_, int64_t d, const void* x, int64_t ldx, const void* w, c
   const bool aligned = vector_ok<T>(d, x, ldx, y, ldy, x, ldx, w) && (!LN || aligned16(b));
   if (aligned || unaligned_ok<T>(d, {x, y, w, LN ? b : x})) {
     const int nvec = (int)(d / Vec<T>::N);  // full vectors; the rest is the tail (UA)
-    const dim3 grid((unsigned)ceil_div(T_, kFwdWaves));
-    const dim3 block(kFwdWaves * kWave);
-    auto go = [&](auto ua) {
-      constexpr bool UA = decltype(ua)::value;
-#define FO_FWD(NV_) \
-  rmsnorm_fwd_wave<T, NV_, LN, UA><<<grid, block, 0, st>>>(T_, nvec, (int)d, xp, ldx, wp, bp, eps, yp, ldy, mean, rstd)
-      switch (nv_for(nvec)) {
-        case 1: FO_FWD(1); break;
-        case 2: FO_FWD(2); break;
-        case 4: FO_FWD(4); break;
-        case 8: FO_FWD(8); break;
-        default: FO_FWD(16); break;
-      }
-#undef FO_FWD
+    const FwdPlan p = fwd_plan(nvec);
+    auto go = [&](auto nv_c, auto rw_c, auto ua) {
+      constexpr int NV = decltype(nv_c)::value, RW = decltype(rw_c)::value;
+      constexpr int NT = fwd_threads(RW);
+      const dim3 grid((unsigned)ceil_div(T_, (int64_t)(NT / kWave / RW)));
+      rmsnorm_fwd_wave<T, NV, RW, LN, decltype(ua)::value><<<grid, dim3(NT), 0, st>>>(
+          T_, nvec, (int)d, xp, ldx, wp, bp, eps, yp, ldy, mean, rstd);
     };
-    if (aligned) go(std::false_type{});
-    else go(std::true_type{});
+    // a row of one wave takes 1, 2, 4 or kFwdMaxNV vectors per lane; a row of more
+    // waves has more than kFwdMaxNV / 2 per lane, so it takes kFwdMaxNV (16 where
+    // kMaxRowWaves waves still need more)
+    static_assert(kFwdMaxNV == 8, "the one-wave cases below list 1, 2, 4, 8");
+    auto go_rw = [&](auto ua) {
+      using I = std::integral_constant<int, kFwdMaxNV>;
+      using One = std::integral_constant<int, 1>;
+      switch (p.rw) {
+        case 1:
+          switch (p.nv) {
+            case 1: go(std::integral_constant<int, 1>{}, One{}, ua); break;
+            case 2: go(std::integral_constant<int, 2>{}, One{}, ua); break;
+            case 4: go(std::integral_constant<int, 4>{}, One{}, ua); break;
+            default: go(I{}, One{}, ua); break;
+          }
+          break;
+        case 2: go(I{}, std::integral_constant<int, 2>{}, ua); break;
+        case 4: go(I{}, std::integral_constant<int, 4>{}, ua); break;
+        case 8: go(I{}, std::integral_constant<int, 8>{}, ua); break;
+        default:
+          if (p.nv <= kFwdMaxNV) go(I{}, std::integral_constant<int, 16>{}, ua);
+          else go(std::integral_constant<int, 16>{}, std::integral_constant<int, 16>{}, ua);
+          break;
+      }
+    };
+    if (aligned) go_rw(std::false_type{});
+    else go_rw(std::true_type{});
   } else {
     rmsnorm_fwd_block<T, LN><<<dim3((unsigned)T_), dim3(kGenericThreads), 0, st>>>(
         T_, d, xp, ldx, wp, bp, eps, yp, ldy, mean, rstd);
   }
   return launch_status();
+}
+
+// Rows the backward wave kernel holds: at most 16 elements per operand per lane of
+// kMaxRowWaves waves.
+template <typename T>
+bool bwd_fits(int64_t d) {
+  return d / Vec<T>::N <= (int64_t)kMaxRowWaves * kWave * (16 / Vec<T>::N);
 }
 
 // Upper bound of the dw partial rows of either backward path (workspace sizing).
@@ -634,10 +741,10 @@ BwdPlan bwd_plan(int64_t T_, int nvec) {
   // fewest waves per row that keep each lane at <= 16 elements per operand
   constexpr int kMaxNV = 16 / Vec<T>::N;
   BwdPlan p{1, 1, 0};
-  while (p.rw < kBwdWaves && ceil_div(nvec, (int64_t)p.rw * kWave) > kMaxNV) p.rw *= 2;
+  while (p.rw < kMaxRowWaves && ceil_div(nvec, (int64_t)p.rw * kWave) > kMaxNV) p.rw *= 2;
   const int64_t per = ceil_div(nvec, (int64_t)p.rw * kWave);
   p.nv = per <= 1 ? 1 : per <= 2 ? 2 : kMaxNV;
-  const int64_t rows_in_flight = kBwdWaves / p.rw;
+  const int64_t rows_in_flight = bwd_threads(p.rw) / kWave / p.rw;
   p.groups = ceil_div(T_, rows_in_flight);
   if (p.groups > kMaxPartials) p.groups = kMaxPartials;
   return p;
@@ -647,9 +754,18 @@ template <typename T, int NV, int RW, bool LN, bool UA>
 void launch_bwd(const BwdPlan& p, int64_t T_, int nvec, int d, const T* dy, int64_t lddy,
                 const T* x, int64_t ldx, const T* w, const float* mean, const float* rstd,
                 float eps, T* dx, int64_t lddx, float* partial, hipStream_t st) {
+  // the LDS fold of the row groups' dw partials (none with one row group)
+  constexpr int RG = bwd_threads(RW) / kWave / RW;
+  const size_t fold = (size_t)(LN ? 2 : 1) * d * sizeof(float);
+  // One row group (RG 1) writes its partial row from registers: as 16-byte stores
+  // where the row is 16-byte aligned (direct 2); otherwise through the LDS fold, which
+  // measured faster than scattered 4-byte stores, or scalar stores (direct 1) past
+  // the LDS of a workgroup.
+  const bool vec_out = !UA && reinterpret_cast<uintptr_t>(partial) % 16 == 0;
+  const int direct = RG != 1 ? 0 : vec_out ? 2 : fold > kMaxLds ? 1 : 0;
+  const size_t lds = direct ? 0 : fold;
   rmsnorm_bwd_wave<T, NV, RW, LN, UA>
-      <<<dim3((unsigned)p.groups), dim3(kBwdWaves * kWave), (size_t)(LN ? 2 : 1) * d * sizeof(float),
-         st>>>(T_, nvec, d, dy, lddy, x, ldx, w, mean, rstd, eps, dx, lddx, partial);
+      <<<dim3((unsigned)p.groups), dim3(bwd_threads(RW)), lds, st>>>(T_, nvec, d, dy, lddy, x, ldx, w, mean, rstd, eps, dx, lddx, partial, direct);
 }
 
 // LN: mean and rstd are the forward's saved statistics (required); db receives the
@@ -665,8 +781,9 @@ int bwd_impl(int64_t T_, int64_t d, const void* dy, int64_t lddy, const void* x,
   float* partial = static_cast<float*>(ws);
   constexpr int64_t kCols = LN ? 2 : 1;  // partial row: dw (and db) columns
   int64_t G;
-  const bool aligned = vector_ok<T>(d, dy, lddy, x, ldx, dx, lddx, w);
-  if (aligned || unaligned_ok<T>(d, {dy, x, dx, w})) {
+  const bool fits = bwd_fits<T>(d);
+  const bool aligned = fits && vector_ok<T>(d, dy, lddy, x, ldx, dx, lddx, w);
+  if (aligned || (fits && unaligned_ok<T>(d, {dy, x, dx, w}))) {
     const int nvec = (int)(d / Vec<T>::N);  // full vectors; the rest is the tail (UA)
     const BwdPlan p = bwd_plan<T>(T_, nvec);
     G = p.groups;
@@ -685,7 +802,8 @@ int bwd_impl(int64_t T_, int64_t d, const void* dy, int64_t lddy, const void* x,
         case 1: go_nv(std::integral_constant<int, 1>{}, ua); break;
         case 2: go_nv(std::integral_constant<int, 2>{}, ua); break;
         case 4: go_nv(std::integral_constant<int, 4>{}, ua); break;
-        default: go_nv(std::integral_constant<int, 8>{}, ua); break;
+        case 8: go_nv(std::integral_constant<int, 8>{}, ua); break;
+        default: go_nv(std::integral_constant<int, 16>{}, ua); break;
       }
     };
     if (aligned) go_rw(std::false_type{});

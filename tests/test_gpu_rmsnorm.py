@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from reduction_rmsnorm_fwd_amd import synth
-from tolerance import check
+from tolerance import check, norm_dx_terms
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -26,7 +26,8 @@ def compare(x, w, dy, eps, dt, got, rows=None):
     sel = slice(None) if rows is None else rows
     check(y[sel], ry[sel], dt, "y", single_rounding=True)
     check(rstd[sel], rr[sel], "f32", "rstd")
-    check(dx[sel], rdx[sel], dt, "dx", single_rounding=True)
+    terms = norm_dx_terms(dy, x, w, eps, False)
+    check(dx[sel], rdx[sel], dt, "dx", single_rounding=True, scale=terms[sel])
     # dw is an fp32 output: the products of exact inputs summed in fp32
     check(dw, rdw, "f32", "dw")
 
@@ -50,15 +51,22 @@ def test_config1_as_stated(gpu):
     compare(i["x"], i["w"], i["dy"], cfg.eps, cfg.dtype, run(gpu, i["x"], i["w"], i["dy"], cfg.eps))
 
 
+# Row widths at the launch-plan boundaries (VEC = 8 bf16 / 4 fp32 elements per vector):
+# tail-only rows (3, 5); vectors plus a tail; the forward's one-wave rows end at 512
+# vectors (4096 bf16, 2048 fp32), then 2, 4, 8, 16 waves per row up to 16384 vectors
+# (131072 bf16, 65536 fp32; + a tail of VEC - 1: 131079, 65539), past which (131080,
+# 65540) the workgroup-per-row kernel takes the row; the backward holds up to 2048 bf16 /
+# 4096 fp32 vectors (16384 elements; 16391 bf16 and 16387 fp32 with the longest tail)
+# in up to 16 waves and takes the workgroup kernel past that (16388 fp32, 16392 bf16).
+WIDE = (3, 5, 13, 1000, 1025, 2049, 4096, 4097, 4099, 4100, 4104, 8, 8191, 8199, 8200, 12288,
+        16387, 16388, 16391, 16392, 24577, 65539, 65540, 131072, 131079, 131080)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("T,d", [(37, d) for d in (3, 5, 13, 1000, 1025, 2049, 4097, 4099, 4100,
-                                                   8, 8191, 8199, 8200, 12288)] + [(5000, 1027)])
+@pytest.mark.parametrize("T,d", [(37, d) for d in WIDE] + [(5000, 1027), (300, 12289)])
 def test_unaligned_and_wide_rows(gpu, dtype, T, d):
-    # rows shorter than one vector (3, 5: tail only), vectors plus a tail (4099 fp32 and
-    # 8199 bf16: the 1024 full vectors the wave kernels hold at most, and the longest
-    # tail), just past that bound (4100 fp32, 8200 bf16) and far past it (12288), and a
-    # batch whose backward workgroups each take several rounds of rows with a tail
-    # (T 5000, d 1027)
+    # every width of WIDE, and batches whose backward workgroups each take several
+    # rounds of rows with a tail (T 5000, d 1027; T 300, d 12289 at 16 waves per row)
     cfg = synth.Config(0, "odd", dtype, T=T, d=d, n_q=1, n_kv=1, head_dim=2, F=1, V=2,
                        eps=1e-5, theta=1e4, logit_std=1, z_loss=0, ignore_frac=0,
                        packed=False, doc_lengths=(T,), seed=11)
