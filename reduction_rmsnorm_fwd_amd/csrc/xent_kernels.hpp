@@ -17,7 +17,8 @@
 // the workgroup in a fixed order; the gradient is then formed from the registers and
 // written.  The row is read from HBM once, also when it starts off the 16-byte grid or
 // its length is not a multiple of the vector (full vectors are still 16-byte accesses).
-// Rows too long for the registers take the streaming form, which makes the same online
+// Rows up to 8 vectors per thread longer than the registers hold keep the rest in LDS
+// (still one read); longer rows take the streaming form, which makes the same online
 // pass and then reads the row a second time for the gradient.
 #pragma once
 
@@ -462,6 +463,116 @@ __global__ __launch_bounds__(kPfThreads) void row_pf(RowArgs a, const Tin* z, To
   wait_vm_n<0>();
 }
 
+// Register-resident row kernel with an LDS extension, for rows of 16 + NS vectors per
+// thread (1024 threads; bf16 V up to 163840 with NS 4, 196608 with NS 8): vectors
+// t + i*1024 of thread t sit in registers for i < NV and in LDS for NV <= i < NV + NS,
+// so the row is read from HBM once.  The LDS part is copied by buffer_load ... lds into
+// the thread's own 16-byte slots (slot i*1024 + t, 16 consecutive bytes per lane) and
+// read back by the same lane after its wave's loads have landed, so no barrier orders
+// it.  Requires V % VEC == 0 and 16-byte aligned rows; the whole byte offset of a
+// vector goes in the lane's offset register, so the buffer's range check (the row's
+// bytes) returns zeros for vectors past the row, which are skipped.
+template <typename Tin, typename Tout, int NV, int NS>
+__global__ __launch_bounds__(1024) void row_ls(RowArgs a, const Tin* z, Tout* dz) {
+  constexpr int NT = 1024;
+  constexpr int VEC = Vec<Tin>::N;
+  constexpr int kFlags = 0x00020000;  // raw buffer, 32-bit data format
+  static_assert(Vec<Tout>::N == VEC, "same element width in and out");
+  __shared__ __attribute__((aligned(16))) u32x4 ext[NS * NT];
+  __shared__ float shm[NT / kWave], shs[NT / kWave];
+  __shared__ float sh_zy;
+  const int64_t row = blockIdx.x;
+  const long long y = a.tg[row];
+  const int64_t nvec = a.V / VEC;
+  if (!row_valid(y, a.V, a.ignore)) {
+    if (dz != nullptr) zero_row<Tout, VEC, NT>(dz + row * a.ldd, nvec);
+    if (threadIdx.x == 0) { a.row_loss[row] = 0.f; a.row_z[row] = 0.f; }
+    return;
+  }
+  const Tin* zr = z + row * a.ldz;
+  if (threadIdx.x == 0) sh_zy = to_f32(zr[y]);  // read before any gradient write
+  const int wave = threadIdx.x / kWave;
+  {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)zr, (short)0, (int)(a.V * (int64_t)sizeof(Tin)), kFlags);
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_vptr)(ext + i * NT + wave * kWave), 16,
+                                               (threadIdx.x + (uint32_t)(NV + i) * NT) * 16u, 0, 0, 0);
+  }
+  Pack<Tin> xv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t v = threadIdx.x + (int64_t)i * NT;
+    if (v < nvec) xv[i] = load_pack(zr + v * VEC);
+  }
+  float m = -INFINITY, s = 0.f;
+  auto fold = [&](const Pack<Tin>& p) {
+    float vm = to_f32(p.v[0]);
+#pragma unroll
+    for (int j = 1; j < VEC; ++j) vm = fmaxf(vm, to_f32(p.v[j]));
+    if (vm > m) { s *= ex<Tin>(m - vm); m = vm; }
+    const float nb = nl2e<Tin>(m);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) s += exs<Tin>(to_f32(p.v[j]), nb);
+  };
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (threadIdx.x + (int64_t)i * NT < nvec) fold(xv[i]);
+  wait_vm_n<0>();  // this wave's LDS copies have landed
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    if (threadIdx.x + (int64_t)(NV + i) * NT < nvec) {
+      Pack<Tin> p;
+      p.raw = ext[i * NT + threadIdx.x];
+      fold(p);
+    }
+  }
+  const float lse = block_lse<NT>(m, s, shm, shs);
+  if (threadIdx.x == 0) {
+    const float zt = a.zc * lse * lse;
+    a.row_loss[row] = (lse - sh_zy) + zt;
+    a.row_z[row] = zt;
+  }
+  if (dz == nullptr) return;
+  const float scale = a.dloss / (float)a.cnt->n_valid;
+  const float coef = scale * fmaf(2.f * a.zc, lse, 1.f);
+  Tout* dr = dz + row * a.ldd;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(xv[i].raw));
+  const int64_t yv = y / VEC;
+  const int yj = (int)(y - yv * VEC);
+  const float nl = nl2e<Tin>(lse);
+  auto grad = [&](const Pack<Tin>& p, int64_t v) {
+    float g[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) g[j] = coef * exs<Tin>(to_f32(p.v[j]), nl);
+    if (v == yv) {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j)
+        if (j == yj) g[j] -= scale;
+    }
+    Pack<Tout> o;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) o.v[j] = from_f32<Tout>(g[j]);
+    store_pack(dr + v * VEC, o);
+  };
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t v = threadIdx.x + (int64_t)i * NT;
+    if (v < nvec) grad(xv[i], v);
+  }
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int64_t v = threadIdx.x + (int64_t)(NV + i) * NT;
+    if (v < nvec) {
+      Pack<Tin> p;
+      p.raw = ext[i * NT + threadIdx.x];
+      grad(p, v);
+    }
+  }
+}
+
 // Streaming row kernel: any V, any alignment (VEC = 1) or aligned vectors (VEC > 1), for
 // rows longer than the register-resident kernels hold.  With vectors, each thread keeps
 // its first KEEP vectors of the row in registers from the first pass to the second (as
@@ -664,10 +775,21 @@ hipError_t launch_rows(const RowArgs& a, const Tin* z, Tout* dz, hipStream_t st,
           row_reg<Tin, Tout, 16, 1024><<<grid, 1024, 0, st>>>(a, z, dz);
         }
         break;
+      // 16 vectors per thread in registers, the rest (4 or 8) in LDS: one read of the row
+      // (T 4096, V 151936: 572 -> 526 us against the streaming kernel, T 8192, V 196608:
+      // 1341 -> 1309 us)
+      case 17: case 18: case 19: case 20: case 21: case 22: case 23: case 24:
+        if constexpr (Vec<Tout>::N == VEC) {
+          if (per <= 20) row_ls<Tin, Tout, 16, 4><<<grid, 1024, 0, st>>>(a, z, dz);
+          else row_ls<Tin, Tout, 16, 8><<<grid, 1024, 0, st>>>(a, z, dz);
+          break;
+        }
+        [[fallthrough]];
       default:
-        // longer rows: the first 16 vectors per thread stay in registers between the
-        // passes, the rest is read twice, 4 vectors in flight per thread (V 151936 at
-        // T 8192: 1389 -> 1093 us against one vector in flight and nothing kept)
+        // longer rows (and fp32 rows of bf16 gradients past 16 vectors per thread): the
+        // first 16 vectors per thread stay in registers between the passes, the rest is
+        // read twice, 4 vectors in flight per thread (V 151936 at T 8192: 1389 -> 1093 us
+        // against one vector in flight and nothing kept)
         row_stream<Tin, Tout, VEC, 1024, 16, 4><<<grid, 1024, 0, st>>>(a, z, dz);
         break;
     }

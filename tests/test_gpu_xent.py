@@ -56,14 +56,17 @@ def test_config1_as_stated(gpu):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V", [4097, 7, 8, 1000, 12000, 12001, 16384, 20000, 32001, 50257,
-                               65536, 65544, 131072, 131080, 151936, 163840, 81920, 200000])
+                               65536, 65544, 131072, 131080, 151936, 163840, 163848, 196608,
+                               196616, 81920, 98304, 98312, 200000])
 def test_vocab_sizes(gpu, dtype, V):
     # rows off the 16-byte grid (4097, 7, 12001, 32001, 50257: every row starts at another
     # alignment), tiny and register-resident rows (bf16 12000 and 16384: 256 threads of 8
     # vectors, the latter full; bf16 20000 and fp32 12000: 512 threads of 8; fp32 20000,
     # bf16 65536: 512 threads of 16, the latter full; 65544 one vector past it),
-    # rows split between registers and LDS (bf16 131080: 17 vectors per thread, 151936:
-    # 19, 163840: 20, the most; fp32 81920: 20) and streaming rows (longer)
+    # rows split between registers and LDS (16 vectors per thread in registers and 4 in
+    # LDS: bf16 131080, 17 vectors per thread, 151936: 19, 163840: 20; and 8 in LDS:
+    # bf16 163848, 21, 196608: 24, the most; fp32 81920: 20, 98304: 24) and streaming
+    # rows (longer: bf16 196616, 200000, fp32 98312)
     g = torch.Generator().manual_seed(V)
     T = 9
     z = (2 * torch.randn(T, V, generator=g)).to(synth.torch_dtype(dtype))
