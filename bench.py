@@ -77,6 +77,8 @@ def parse():
     p.add_argument("--no-isolated", action="store_true")
     p.add_argument("--no-configs", action="store_true",
                    help="skip the per-(config, op) records of configs 1-4")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the graph-replayed step of each config record")
     p.add_argument("--config", default="1,2,3,4",
                    help="comma list of the configs (1-4) the per-(config, op) records cover")
     p.add_argument("--only", default="", help="comma list of ops to run (profiling)")
@@ -457,7 +459,32 @@ def iso_times(torch, stream, fn, reps, scratch):
 LAUNCH_BOUND_US = 7.0  # ops whose bytes take less than this at 70% of peak: launch-bound
 
 
-def config_lines(fo, synth, torch, stream, med, reps, copy_gbs, cids=(1, 2, 3, 4)):
+def graph_step(torch, stream, cases, reps, scratch, med):
+    """The config's seven layer-op calls as one step, timed eagerly (seven launches from
+    the host) and as one captured HIP graph replayed (torch.cuda.graph; the calls use
+    preallocated outputs and workspaces, so capture records kernels only), caches flushed
+    before each step as for the isolated ops."""
+    def eager():
+        for _, fn, _ in cases:
+            fn()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        eager()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        eager()
+    torch.cuda.synchronize()
+    te = med(iso_times(torch, stream, eager, reps, scratch))
+    tg = med(iso_times(torch, stream, g.replay, reps, scratch))
+    del g
+    return {"ops": [n for n, _, _ in cases], "step_ms_eager": round(te, 4),
+            "step_ms_graph": round(tg, 4), "graph_speedup": round(te / tg, 3)}
+
+
+def config_lines(fo, synth, torch, stream, med, reps, copy_gbs, cids=(1, 2, 3, 4), graph=True):
     """One record per (config, op) for the layer-op configs: the tiny fp32 block (T 256),
     the Qwen2.5-0.5B shapes (T 4096, vocabulary 151936), the Llama-3-8B shapes (T 8192,
     vocabulary 128256, z-loss) and the packed 16k batch (document-reset positions, 25%
@@ -539,6 +566,8 @@ def config_lines(fo, synth, torch, stream, med, reps, copy_gbs, cids=(1, 2, 3, 4
                            "frac_hbm_peak": round(byt / t / 1e9 / HBM_PEAK_GBS, 4),
                            "launch_bound": f_["launch_bound"] and b_["launch_bound"]}
         ent["fwd_bwd"] = pairs
+        if graph:
+            ent["step_graph"] = graph_step(torch, stream, cases, reps, scratch, med)
         out[f"cfg{cid}"] = ent
         del x, w, dy, y, rstd, dx, dw, rws, q, k, dq, dk, pos, g, u, dh, h, dg, du, lg, tg, dlg, xws
         torch.cuda.empty_cache()
@@ -697,7 +726,8 @@ def gpu_bench(args):
     unaligned = None if args.no_probes or only else unaligned_lines(fo, synth, torch, stream, med)
     configs = (None if args.no_configs or only or not args.cids
                else config_lines(fo, synth, torch, stream, med, args.iso_reps,
-                                 peaks["copy_GBps"] if peaks else None, args.cids))
+                                 peaks["copy_GBps"] if peaks else None, args.cids,
+                                 graph=not args.no_graph))
     next_ops = None
     if not (args.no_next or only):
         cg = peaks["copy_GBps"] if peaks else None
