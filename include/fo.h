@@ -103,7 +103,8 @@ int fo_rmsnorm_bwd(int dtype, int64_t T, int64_t d, const void* dy, int64_t lddy
  *   dtype, strides and aliasing as fo_rmsnorm_fwd; w [d] and b [d] of the same dtype;
  *   mean [T] and rstd [T] fp32, each may be NULL (the saved statistics of the backward).
  *   The row stays in registers between the mean and the centred variance (two sweeps
- *   over registers, one read of x).
+ *   over registers, one read of x) for rows of up to 131072 bf16 / 65536 fp32 elements;
+ *   longer rows are read twice.
  */
 int fo_layernorm_fwd(int dtype, int64_t T, int64_t d, const void* x, int64_t ldx,
                      const void* w, const void* b, float eps, void* y, int64_t ldy,

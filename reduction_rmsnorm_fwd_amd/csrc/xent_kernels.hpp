@@ -791,10 +791,9 @@ hipError_t launch_rows(const RowArgs& a, const Tin* z, Tout* dz, hipStream_t st,
         }
         [[fallthrough]];
       default:
-        // longer rows (and fp32 rows of bf16 gradients past 16 vectors per thread): the
-        // first 16 vectors per thread stay in registers between the passes, the rest is
-        // read twice, 4 vectors in flight per thread (V 151936 at T 8192: 1389 -> 1093 us
-        // against one vector in flight and nothing kept)
+        // longer rows: the first 16 vectors per thread stay in registers between the
+        // passes, the rest is read twice, 4 vectors in flight per thread (V 151936 at
+        // T 8192: 1389 -> 1093 us against one vector in flight and nothing kept)
         row_stream<Tin, Tout, VEC, 1024, 16, 4><<<grid, 1024, 0, st>>>(a, z, dz);
         break;
     }
