@@ -125,13 +125,11 @@ __device__ __forceinline__ void masked_row(const DistillArgs& a, int64_t row, T*
   if (threadIdx.x == 0) { a.row_ce[row] = 0.f; a.row_kl[row] = 0.f; }
 }
 
-// Any row length and alignment: the second sweep re-reads both rows.  dz may alias z
-// (each element is read by the thread that writes it; the merge barrier separates the
-// first sweep's reads from the writes).  UA (rows of any element alignment and length,
-// VEC > 1): full vectors are 16-byte accesses at element-aligned addresses (gfx950
-// serves global memory in unaligned mode), the partial last vector goes element by
-// element, read as -inf padding past the row.
-template <typename T, int VEC, bool UA = false>
+// Element path, for rows whose pointers are not even element-aligned: one element per
+// thread and step, the second sweep re-reading both rows.  dz may alias z (each element
+// is read by the thread that writes it; the merge barrier separates the first sweep's
+// reads from the writes).
+template <typename T>
 __global__ __launch_bounds__(kRowThreads) void soft_stream(DistillArgs a, const T* z,
                                                           const T* zt, T* dz) {
   __shared__ Stats sh[kRowThreads / kWave];
@@ -140,59 +138,23 @@ __global__ __launch_bounds__(kRowThreads) void soft_stream(DistillArgs a, const 
     masked_row<T>(a, row, dz);
     return;
   }
-  // vectors (VEC = 1: elements); UA: the last one partial
-  const int64_t n = UA ? ceil_div(a.V, (int64_t)VEC) : a.V / VEC;
   const T* zr = z + row * a.ldz;
   const T* tr = zt + row * a.ldt;
-  auto vec_at = [&](const T* p, int64_t v, bool cached) {
-    if (!UA || (v + 1) * VEC <= a.V) return cached ? load_pack_cached(p + v * VEC) : load_pack(p + v * VEC);
-    Pack<T> r;
-#pragma unroll
-    for (int j = 0; j < VEC; ++j)
-      r.v[j] = v * VEC + j < a.V ? p[v * VEC + j] : from_f32<T>(-INFINITY);
-    return r;
-  };
   Stats s;
   stats_init(s);
-  for (int64_t v = threadIdx.x; v < n; v += kRowThreads) {
-    float zf[VEC], tf[VEC];
-    if constexpr (VEC > 1) {
-      const Pack<T> zp = vec_at(zr, v, true), tp = vec_at(tr, v, true);
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) { zf[j] = to_f32(zp.v[j]); tf[j] = to_f32(tp.v[j]); }
-    } else {
-      zf[0] = to_f32(zr[v]);
-      tf[0] = to_f32(tr[v]);
-    }
-    stats_add<T, VEC, UA>(s, zf, tf);
+  for (int64_t v = threadIdx.x; v < a.V; v += kRowThreads) {
+    const float zf = to_f32(zr[v]), tf = to_f32(tr[v]);
+    stats_add<T, 1>(s, &zf, &tf);
   }
   const Stats r = block_stats<kRowThreads>(s, sh);
   float lse_z, lse_t;
   row_terms(a, row, r, lse_z, lse_t);
   if (dz == nullptr) return;
   const float scale = a.dloss / (float)a.cnt->n_valid;
-  const float nz = xent::nl2e<T>(lse_z), nt = xent::nl2e<T>(lse_t);
   T* dr = dz + row * a.ldd;
-  for (int64_t v = threadIdx.x; v < n; v += kRowThreads) {
-    if constexpr (VEC > 1) {
-      const Pack<T> zp = vec_at(zr, v, false), tp = vec_at(tr, v, false);
-      Pack<T> o;
-#pragma unroll
-      for (int j = 0; j < VEC; ++j)
-        o.v[j] = from_f32<T>(scale * (xent::exs<T>(to_f32(zp.v[j]), nz) -
-                                      xent::exs<T>(to_f32(tp.v[j]), nt)));
-      if (!UA || (v + 1) * VEC <= a.V) {
-        store_pack(dr + v * VEC, o);
-      } else {
-#pragma unroll
-        for (int j = 0; j < VEC; ++j)
-          if (v * VEC + j < a.V) dr[v * VEC + j] = o.v[j];
-      }
-    } else {
-      dr[v] = from_f32<T>(scale * (xent::ex<T>(to_f32(zr[v]) - lse_z) -
-                                   xent::ex<T>(to_f32(tr[v]) - lse_t)));
-    }
-  }
+  for (int64_t v = threadIdx.x; v < a.V; v += kRowThreads)
+    dr[v] = from_f32<T>(scale * (xent::ex<T>(to_f32(zr[v]) - lse_z) -
+                                 xent::ex<T>(to_f32(tr[v]) - lse_t)));
 }
 
 // Aligned rows of any length (V % VEC == 0), streamed: each thread keeps its first KS
@@ -205,7 +167,10 @@ __global__ __launch_bounds__(kRowThreads) void soft_stream(DistillArgs a, const 
 // non-temporal hint; only the first sweep's streamed loads, whose lines the second sweep
 // wants back, are plain (T 8192, V 16384: 214 -> 146 us; V 128256: 1269 -> 1227 us
 // against plain loads throughout).
-template <typename T, int U, int KS, int NT = kRowThreads>
+// UA (rows of any element alignment and length): full vectors are still 16-byte
+// accesses at element-aligned addresses, the partial last vector of a row goes element by
+// element, read as -inf padding past the row (a zero teacher weight adds nothing).
+template <typename T, int U, int KS, int NT = kRowThreads, bool UA = false>
 __global__ __launch_bounds__(NT) void soft_stream_u(DistillArgs a, const T* z, const T* zt,
                                                    T* dz) {
   constexpr int VEC = Vec<T>::N;
@@ -216,10 +181,19 @@ __global__ __launch_bounds__(NT) void soft_stream_u(DistillArgs a, const T* z, c
     masked_row<T>(a, row, dz);
     return;
   }
-  const int64_t n = a.V / VEC;
+  const int64_t n = UA ? ceil_div(a.V, (int64_t)VEC) : a.V / VEC;
   const T* zr = z + row * a.ldz;
   const T* tr = zt + row * a.ldt;
   const int64_t tid = threadIdx.x;
+  // vector v of a row; nt: the non-temporal hint (a value read once)
+  auto ld = [&](const T* p, int64_t v, bool nt) {
+    if (!UA || (v + 1) * VEC <= a.V) return nt ? load_pack(p + v * VEC) : load_pack_cached(p + v * VEC);
+    Pack<T> r;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+      r.v[j] = v * VEC + j < a.V ? p[v * VEC + j] : from_f32<T>(-INFINITY);
+    return r;
+  };
   Pack<T> kz[KR], kt[KR];
   Stats s;
   stats_init(s);
@@ -227,13 +201,13 @@ __global__ __launch_bounds__(NT) void soft_stream_u(DistillArgs a, const T* z, c
     float zf[VEC], tf[VEC];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) { zf[j] = to_f32(zp.v[j]); tf[j] = to_f32(tp.v[j]); }
-    stats_add<T, VEC>(s, zf, tf);
+    stats_add<T, VEC, UA>(s, zf, tf);
   };
   if constexpr (KS > 0) {
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
       const int64_t v = tid + (int64_t)i * NT;
-      if (v < n) { kz[i] = load_pack(zr + v * VEC); kt[i] = load_pack(tr + v * VEC); }
+      if (v < n) { kz[i] = ld(zr, v, true); kt[i] = ld(tr, v, true); }
     }
 #pragma unroll
     for (int i = 0; i < KS; ++i)
@@ -245,7 +219,7 @@ __global__ __launch_bounds__(NT) void soft_stream_u(DistillArgs a, const T* z, c
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t v = v0 + u * NT;
-      if (v < n) { zp[u] = load_pack_cached(zr + v * VEC); tp[u] = load_pack_cached(tr + v * VEC); }
+      if (v < n) { zp[u] = ld(zr, v, false); tp[u] = ld(tr, v, false); }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -264,14 +238,20 @@ __global__ __launch_bounds__(NT) void soft_stream_u(DistillArgs a, const T* z, c
     for (int j = 0; j < VEC; ++j)
       o.v[j] = from_f32<T>(scale * (xent::exs<T>(to_f32(zp.v[j]), nz) -
                                     xent::exs<T>(to_f32(tp.v[j]), nt)));
-    store_pack(dr + v * VEC, o);
+    if (!UA || (v + 1) * VEC <= a.V) {
+      store_pack(dr + v * VEC, o);
+    } else {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j)
+        if (v * VEC + j < a.V) dr[v * VEC + j] = o.v[j];
+    }
   };
   for (int64_t v0 = tail0; v0 < n; v0 += (int64_t)U * NT) {
     Pack<T> zp[U], tp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t v = v0 + u * NT;
-      if (v < n) { zp[u] = load_pack(zr + v * VEC); tp[u] = load_pack(tr + v * VEC); }
+      if (v < n) { zp[u] = ld(zr, v, true); tp[u] = ld(tr, v, true); }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -348,10 +328,17 @@ int distill_impl(const DistillArgs& a0, const T* z, const T* zt, T* dz, float* l
     } else if (reinterpret_cast<uintptr_t>(z) % sizeof(T) == 0 &&
                reinterpret_cast<uintptr_t>(zt) % sizeof(T) == 0 &&
                reinterpret_cast<uintptr_t>(dz) % sizeof(T) == 0) {
-      // element-aligned rows of any alignment and length: 16-byte accesses still
-      soft_stream<T, VEC, true><<<grid, block, 0, st>>>(a, z, zt, dz);
+      // element-aligned rows of any alignment and length: the same streaming form, 16-byte
+      // accesses at element-aligned addresses and the partial last vector element-wise,
+      // in register-lean plans (at most 128 VGPRs, so that two 512-thread rows share a
+      // CU).  T 8192, against one vector per thread and step and nothing kept: V 8199
+      // 241 -> 151 us, 16389 322 -> 258, 50257 749 -> 662, 128257 1904 -> 1748.
+      const int64_t nv = ceil_div(a.V, (int64_t)VEC);
+      if (nv <= 4 * 256) soft_stream_u<T, 4, 4, 256, true><<<grid, dim3(256), 0, st>>>(a, z, zt, dz);
+      else if (nv <= 6 * 256) soft_stream_u<T, 4, 6, 256, true><<<grid, dim3(256), 0, st>>>(a, z, zt, dz);
+      else soft_stream_u<T, 2, 8, 512, true><<<grid, dim3(512), 0, st>>>(a, z, zt, dz);
     } else {
-      soft_stream<T, 1><<<grid, block, 0, st>>>(a, z, zt, dz);
+      soft_stream<T><<<grid, block, 0, st>>>(a, z, zt, dz);
     }
   }
   xent::finalize<<<1, 1024, 0, st>>>(a.T, a.row_ce, a.row_kl, cnt, loss, kl, n_valid, nullptr);

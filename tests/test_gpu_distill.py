@@ -52,13 +52,17 @@ def cfg_of(dtype, T, V, seed=31, logit_std=3.0):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("V", [100, 1000, 4096, 12000, 16384, 49152, 50257, 128256, 151936])
+@pytest.mark.parametrize("V", [100, 1000, 4096, 8199, 12000, 12001, 16384, 16389, 49152, 50257,
+                               128256, 151936])
 def test_vocab_paths(gpu, dtype, V):
-    # V 100 and 50257 (rows off the 16-byte grid: 16-byte accesses at element-aligned
-    # addresses, the partial last vector element by element), 1000/4096 (whole rows in
-    # 256 threads of up to 4 vectors), 12000/16384 (whole rows in 256 threads of up to 8;
-    # fp32 16384 and the longer ones: 512 threads keeping 8 vectors per thread of each
-    # row and streaming the rest twice)
+    # Rows off the 16-byte grid (V 100, 8199, 12001, 16389, 50257: 16-byte accesses at
+    # element-aligned addresses, the partial last vector element by element) in each of
+    # their plans: whole rows in 256 threads keeping up to 4 vectors (bf16 100) or 6
+    # (bf16 8199 and 12001), longer rows in 512 threads keeping 8 and streaming the rest
+    # (bf16 16389 and up, fp32 8199 and up); aligned rows: 1000/4096
+    # (whole rows in 256 threads of up to 4 vectors), 12000/16384 (whole rows in 256
+    # threads of up to 8; fp32 16384 and the longer ones: 512 threads keeping 8 vectors
+    # per thread of each row and streaming the rest twice)
     T = 6 if V > 50000 else 23
     i = synth.distill_inputs(cfg_of(dtype, T, V))
     o = run(gpu, i["logits"], i["teacher"], i["row_mask"])
