@@ -167,9 +167,25 @@ __global__ __launch_bounds__(kRowThreads) void soft_stream(DistillArgs a, const 
 // non-temporal hint; only the first sweep's streamed loads, whose lines the second sweep
 // wants back, are plain (T 8192, V 16384: 214 -> 146 us; V 128256: 1269 -> 1227 us
 // against plain loads throughout).
-// UA (rows of any element alignment and length): full vectors are still 16-byte
-// accesses at element-aligned addresses, the partial last vector of a row goes element by
-// element, read as -inf padding past the row (a zero teacher weight adds nothing).
+// Vector v of a row of V elements.  UA (rows of any element alignment and length): full
+// vectors are still 16-byte accesses at element-aligned addresses, the partial last
+// vector goes element by element, read as -inf padding past the row (a zero teacher
+// weight adds nothing).  NTH: the non-temporal hint, for a value read once.  (The hint is
+// a template argument: one function with both loads behind a runtime flag compiles to a
+// single plain load, the two merged.)
+template <typename T, bool UA, bool NTH>
+__device__ __forceinline__ Pack<T> row_ld(const T* p, int64_t v, int64_t V) {
+  constexpr int VEC = Vec<T>::N;
+  if (!UA || (v + 1) * VEC <= V) {
+    if constexpr (NTH) return load_pack(p + v * VEC);
+    else return load_pack_cached(p + v * VEC);
+  }
+  Pack<T> r;
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) r.v[j] = v * VEC + j < V ? p[v * VEC + j] : from_f32<T>(-INFINITY);
+  return r;
+}
+
 template <typename T, int U, int KS, int NT = kRowThreads, bool UA = false>
 __global__ __launch_bounds__(NT) void soft_stream_u(DistillArgs a, const T* z, const T* zt,
                                                    T* dz) {
@@ -185,15 +201,6 @@ __global__ __launch_bounds__(NT) void soft_stream_u(DistillArgs a, const T* z, c
   const T* zr = z + row * a.ldz;
   const T* tr = zt + row * a.ldt;
   const int64_t tid = threadIdx.x;
-  // vector v of a row; nt: the non-temporal hint (a value read once)
-  auto ld = [&](const T* p, int64_t v, bool nt) {
-    if (!UA || (v + 1) * VEC <= a.V) return nt ? load_pack(p + v * VEC) : load_pack_cached(p + v * VEC);
-    Pack<T> r;
-#pragma unroll
-    for (int j = 0; j < VEC; ++j)
-      r.v[j] = v * VEC + j < a.V ? p[v * VEC + j] : from_f32<T>(-INFINITY);
-    return r;
-  };
   Pack<T> kz[KR], kt[KR];
   Stats s;
   stats_init(s);
@@ -207,7 +214,7 @@ __global__ __launch_bounds__(NT) void soft_stream_u(DistillArgs a, const T* z, c
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
       const int64_t v = tid + (int64_t)i * NT;
-      if (v < n) { kz[i] = ld(zr, v, true); kt[i] = ld(tr, v, true); }
+      if (v < n) { kz[i] = row_ld<T, UA, true>(zr, v, a.V); kt[i] = row_ld<T, UA, true>(tr, v, a.V); }
     }
 #pragma unroll
     for (int i = 0; i < KS; ++i)
@@ -219,7 +226,7 @@ __global__ __launch_bounds__(NT) void soft_stream_u(DistillArgs a, const T* z, c
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t v = v0 + u * NT;
-      if (v < n) { zp[u] = ld(zr, v, false); tp[u] = ld(tr, v, false); }
+      if (v < n) { zp[u] = row_ld<T, UA, false>(zr, v, a.V); tp[u] = row_ld<T, UA, false>(tr, v, a.V); }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -251,7 +258,7 @@ __global__ __launch_bounds__(NT) void soft_stream_u(DistillArgs a, const T* z, c
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t v = v0 + u * NT;
-      if (v < n) { zp[u] = ld(zr, v, true); tp[u] = ld(tr, v, true); }
+      if (v < n) { zp[u] = row_ld<T, UA, true>(zr, v, a.V); tp[u] = row_ld<T, UA, true>(tr, v, a.V); }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -332,7 +339,7 @@ int distill_impl(const DistillArgs& a0, const T* z, const T* zt, T* dz, float* l
       // accesses at element-aligned addresses and the partial last vector element-wise,
       // in register-lean plans (at most 128 VGPRs, so that two 512-thread rows share a
       // CU).  T 8192, against one vector per thread and step and nothing kept: V 8199
-      // 241 -> 151 us, 16389 322 -> 258, 50257 749 -> 662, 128257 1904 -> 1748.
+      // 257 -> 124 us, 50257 766 -> 650, 128257 1908 -> 1694.
       const int64_t nv = ceil_div(a.V, (int64_t)VEC);
       if (nv <= 4 * 256) soft_stream_u<T, 4, 4, 256, true><<<grid, dim3(256), 0, st>>>(a, z, zt, dz);
       else if (nv <= 6 * 256) soft_stream_u<T, 4, 6, 256, true><<<grid, dim3(256), 0, st>>>(a, z, zt, dz);
