@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void gather_rows(const bf16* __restrict__ Hm, 
   bf16* dst = Hv + j * H;
   for (int64_t v = threadIdx.x; v < H / 8; v += 256)
     *reinterpret_cast<u32x4*>(dst + v * 8) =
-        live ? *reinterpret_cast<const u32x4*>(src + v * 8) : u32x4{0, 0, 0, 0};
+        live ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + v * 8)) : u32x4{0, 0, 0, 0};
 }
 
 // dH[t] = dHv[pos_of[t]], or zeros for a row whose target was ignored or bad.
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void scatter_rows(const bf16* __restrict__ dHv
   const bf16* src = p >= 0 ? dHv + (int64_t)p * H : nullptr;
   for (int64_t v = threadIdx.x; v < H / 8; v += 256)
     *reinterpret_cast<u32x4*>(dst + v * 8) =
-        p >= 0 ? *reinterpret_cast<const u32x4*>(src + v * 8) : u32x4{0, 0, 0, 0};
+        p >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + v * 8)) : u32x4{0, 0, 0, 0};
 }
 
 // Cross-entropy of one chunk from what the logits product left: per row its
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kApplyThreads) void ce_apply(
   for (int64_t v = (int64_t)threadIdx.x * 8; v < V8; v += kApplyThreads * 8) {
     const float f = coef * __expf(sp[v / kCols].x - lse);
     union { u32x4 raw; bf16 e[8]; } o;
-    o.raw = *reinterpret_cast<const u32x4*>(dr + v);
+    o.raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dr + v));
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float g = v + j == y ? gy : f * to_f32(o.e[j]);
