@@ -12,9 +12,12 @@
 // each output written once with 16-byte vector accesses, the gate and up reads of an
 // element issued together so one pass produces the output.  Rows may have their own
 // strides (halves of a [T, 2F] tensor work); fully contiguous operands are walked as
-// one flat row.  bf16 rows off the 16-byte grid (odd F, or halves of a [T, 2F] tensor
+// one flat row, and rows of several blocks whose last block would be partial as one
+// flat space of blocks that run on into the next row.  bf16 rows off the 16-byte grid (odd F, or halves of a [T, 2F] tensor
 // with odd F) still move their full vectors as 16-byte accesses at element-aligned
 // addresses, the partial last vector of a row element by element.
+#include <type_traits>
+
 #include "fo_common.hpp"
 
 namespace fo {
@@ -50,7 +53,7 @@ __device__ __forceinline__ float act_d(float x) {
   }
 }
 
-// Index space: rows x nvr vectors (VEC elements each); nb column blocks per row.
+// Index space: rows x nvr vectors (VEC elements each), walked as one flat space.
 // GATED: h = act(g) u; otherwise h = act(g) (u unused).
 // Vector v of a row of nel elements.  UA (rows of any element alignment and length):
 // a full vector is one 16-byte access at its element-aligned address (gfx950 serves
@@ -76,31 +79,78 @@ __device__ __forceinline__ void st_v(T* p, int64_t v, int64_t nel, const Pack<T>
   }
 }
 
-// nel: elements per row (= nvr * VEC unless UA, where the last vector may be partial)
-template <typename T, int VEC, int ACT, bool GATED, bool UA = false>
-__global__ __launch_bounds__(kThreads) void swiglu_fwd_k(int64_t nvr, int64_t nb, int64_t nel,
-                                                         const T* g, int64_t ldg, const T* u,
-                                                         int64_t ldu, T* h, int64_t ldh) {
-  const int64_t row = blockIdx.x / nb;
-  const int64_t cb = blockIdx.x - row * nb;
-  const T* gr = g + row * ldg;
-  const T* ur = GATED ? u + row * ldu : nullptr;
-  T* hr = h + row * ldh;
-  const int64_t v0 = cb * (kThreads * kUnroll) + threadIdx.x;
+// The (row, vector) pairs of all rows form one flat index space, cut into blocks of
+// kThreads * kUnroll consecutive pairs, so a block may run on into the next row and
+// every block but the last is full whatever the row length.  Slot i of thread t takes
+// pair f = block * kThreads * kUnroll + i * kThreads + t: row f / nvr (inv = 1 / nvr in
+// fp64, then corrected by one where the product rounds across an integer), vector
+// f - row * nvr.
+__device__ __forceinline__ void flat_pair(int64_t f, int64_t nvr, double inv, int64_t& row,
+                                          int64_t& v) {
+  row = (int64_t)((double)f * inv);
+  v = f - row * nvr;
+  if (v < 0) { --row; v += nvr; }
+  else if (v >= nvr) { ++row; v -= nvr; }
+}
+// The (row, vector) pairs of a thread's kUnroll slots, kThreads apart, and whether each
+// exists.  FLAT: blocks over the flat space (rows of at least kThreads vectors step from
+// the first slot, crossing at most one row boundary per step; shorter rows divide per
+// slot).  Otherwise nb blocks per row, none crossing a row, as for one contiguous run:
+// measured faster for rows that fill their blocks or take one (F 4864 halves: 42.0
+// against 44.3 us flat), slower for rows of several blocks with a partial last one (F
+// 14336 halves: forward 125.1 against 119.7 us flat, backward 215.1 against 205.1 us).
+template <bool FLAT>
+__device__ __forceinline__ void slot_pairs(int64_t total, int64_t nvr, double inv, int64_t nb,
+                                           int64_t* row, int64_t* v, bool* ok) {
+  if constexpr (FLAT) {
+    const int64_t f0 = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+    flat_pair(f0, nvr, inv, row[0], v[0]);
+#pragma unroll
+    for (int i = 1; i < kUnroll; ++i) {
+      if (nvr >= kThreads) {
+        row[i] = row[i - 1];
+        v[i] = v[i - 1] + kThreads;
+        if (v[i] >= nvr) { v[i] -= nvr; ++row[i]; }
+      } else {
+        flat_pair(f0 + i * kThreads, nvr, inv, row[i], v[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) ok[i] = f0 + i * kThreads < total;
+  } else {
+    const int64_t r = blockIdx.x / nb;
+    const int64_t v0 = (blockIdx.x - r * nb) * (kThreads * kUnroll) + threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      row[i] = r;
+      v[i] = v0 + i * kThreads;
+      ok[i] = v[i] < nvr;
+    }
+  }
+}
+
+// nel: elements per row (= nvr * VEC unless UA, where the last vector may be partial);
+// total = rows * nvr pairs
+template <typename T, int VEC, int ACT, bool GATED, bool UA = false, bool FLAT = false>
+__global__ __launch_bounds__(kThreads) void swiglu_fwd_k(int64_t total, int64_t nvr, double inv,
+                                                         int64_t nb, int64_t nel, const T* g,
+                                                         int64_t ldg, const T* u, int64_t ldu,
+                                                         T* h, int64_t ldh) {
+  int64_t rw[kUnroll], vv[kUnroll];
+  bool ok[kUnroll];
+  slot_pairs<FLAT>(total, nvr, inv, nb, rw, vv, ok);
   if constexpr (VEC > 1) {
     Pack<T> gv[kUnroll], uv[kUnroll];
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const int64_t v = v0 + i * kThreads;
-      if (v < nvr) {
-        gv[i] = ld_v<T, UA>(gr, v, nel);
-        if constexpr (GATED) uv[i] = ld_v<T, UA>(ur, v, nel);
+      if (ok[i]) {
+        gv[i] = ld_v<T, UA>(g + rw[i] * ldg, vv[i], nel);
+        if constexpr (GATED) uv[i] = ld_v<T, UA>(u + rw[i] * ldu, vv[i], nel);
       }
     }
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const int64_t v = v0 + i * kThreads;
-      if (v < nvr) {
+      if (ok[i]) {
         Pack<T> o;
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
@@ -108,16 +158,17 @@ __global__ __launch_bounds__(kThreads) void swiglu_fwd_k(int64_t nvr, int64_t nb
           if constexpr (GATED) o.v[j] = from_f32<T>(act_f<ACT>(gf) * to_f32(uv[i].v[j]));
           else o.v[j] = from_f32<T>(act_f<ACT>(gf));
         }
-        st_v<T, UA>(hr, v, nel, o);
+        st_v<T, UA>(h + rw[i] * ldh, vv[i], nel, o);
       }
     }
   } else {
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const int64_t v = v0 + i * kThreads;
-      if (v < nvr) {
-        const float gf = to_f32(gr[v]);
-        if constexpr (GATED) hr[v] = from_f32<T>(act_f<ACT>(gf) * to_f32(ur[v]));
+      if (ok[i]) {
+        const int64_t v = vv[i];
+        const float gf = to_f32(g[rw[i] * ldg + v]);
+        T* hr = h + rw[i] * ldh;
+        if constexpr (GATED) hr[v] = from_f32<T>(act_f<ACT>(gf) * to_f32(u[rw[i] * ldu + v]));
         else hr[v] = from_f32<T>(act_f<ACT>(gf));
       }
     }
@@ -125,35 +176,31 @@ __global__ __launch_bounds__(kThreads) void swiglu_fwd_k(int64_t nvr, int64_t nb
 }
 
 // GATED: dg = dh u act'(g), du = dh act(g); otherwise dg = dh act'(g) (u, du unused).
-template <typename T, int VEC, int ACT, bool GATED, bool UA = false>
-__global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t nvr, int64_t nb, int64_t nel,
-                                                         const T* dh, int64_t lddh,
-                                                         const T* g, int64_t ldg, const T* u,
-                                                         int64_t ldu, T* dg, int64_t lddg,
-                                                         T* du, int64_t lddu) {
-  const int64_t row = blockIdx.x / nb;
-  const int64_t cb = blockIdx.x - row * nb;
-  const T* dhr = dh + row * lddh;
-  const T* gr = g + row * ldg;
-  const T* ur = GATED ? u + row * ldu : nullptr;
-  T* dgr = dg + row * lddg;
-  T* dur = GATED ? du + row * lddu : nullptr;
-  const int64_t v0 = cb * (kThreads * kUnroll) + threadIdx.x;
+template <typename T, int VEC, int ACT, bool GATED, bool UA = false, bool FLAT = false>
+__global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t total, int64_t nvr, double inv,
+                                                         int64_t nb, int64_t nel, const T* dh,
+                                                         int64_t lddh, const T* g, int64_t ldg,
+                                                         const T* u, int64_t ldu, T* dg,
+                                                         int64_t lddg, T* du, int64_t lddu) {
+  int64_t rw[kUnroll], vv[kUnroll];
+  bool ok[kUnroll];
+  slot_pairs<FLAT>(total, nvr, inv, nb, rw, vv, ok);
   if constexpr (VEC > 1) {
     Pack<T> hv[kUnroll], gv[kUnroll], uv[kUnroll];
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const int64_t v = v0 + i * kThreads;
-      if (v < nvr) {
-        hv[i] = ld_v<T, UA>(dhr, v, nel);
-        gv[i] = ld_v<T, UA>(gr, v, nel);
-        if constexpr (GATED) uv[i] = ld_v<T, UA>(ur, v, nel);
+      if (ok[i]) {
+        hv[i] = ld_v<T, UA>(dh + rw[i] * lddh, vv[i], nel);
+        gv[i] = ld_v<T, UA>(g + rw[i] * ldg, vv[i], nel);
+        if constexpr (GATED) uv[i] = ld_v<T, UA>(u + rw[i] * ldu, vv[i], nel);
       }
     }
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const int64_t v = v0 + i * kThreads;
-      if (v < nvr) {
+      if (ok[i]) {
+        const int64_t v = vv[i];
+        T* dgr = dg + rw[i] * lddg;
+        T* dur = GATED ? du + rw[i] * lddu : nullptr;
         Pack<T> og, ou;
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
@@ -180,8 +227,13 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t nvr, int64_t nb
   } else {
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const int64_t v = v0 + i * kThreads;
-      if (v < nvr) {
+      if (ok[i]) {
+        const int64_t v = vv[i];
+        const T* gr = g + rw[i] * ldg;
+        const T* dhr = dh + rw[i] * lddh;
+        const T* ur = GATED ? u + rw[i] * ldu : nullptr;
+        T* dgr = dg + rw[i] * lddg;
+        T* dur = GATED ? du + rw[i] * lddu : nullptr;
         const float gf = to_f32(gr[v]), hf = to_f32(dhr[v]);
         if constexpr (GATED && ACT == kSilu) {
           const float uf = to_f32(ur[v]);
@@ -203,9 +255,12 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_k(int64_t nvr, int64_t nb
 // Launch geometry: rows x vectors-per-row; one flat row when every operand is a
 // single contiguous [T*F] run.
 struct Geo {
-  int64_t rows, nvr, nb, nel;
-  bool vec;  // 16-byte vectors on the 16-byte grid
-  bool ua;   // otherwise, bf16: 16-byte vectors at element-aligned addresses
+  int64_t rows, nvr, nel;
+  int64_t nb;    // blocks per row, or (flat) blocks over the whole (row, vector) space
+  int64_t grid;  // workgroups
+  bool vec;      // 16-byte vectors on the 16-byte grid
+  bool ua;       // otherwise, bf16: 16-byte vectors at element-aligned addresses
+  bool flat;     // rows of several blocks whose last one is partial: one flat space
 };
 
 template <typename T>
@@ -228,7 +283,10 @@ Geo plan(int64_t T_, int64_t F, int n, const void* const* ptr, const int64_t* ld
   g.ua = !g.vec && sizeof(T) == 2 && elem;
   g.nel = per_row;
   g.nvr = g.vec ? per_row / VEC : g.ua ? ceil_div(per_row, (int64_t)VEC) : per_row;
-  g.nb = ceil_div(g.nvr, kThreads * kUnroll);
+  constexpr int64_t kSpan = kThreads * kUnroll;
+  g.flat = g.rows > 1 && g.nvr > kSpan && g.nvr % kSpan != 0;
+  g.nb = g.flat ? ceil_div(g.rows * g.nvr, kSpan) : ceil_div(g.nvr, kSpan);
+  g.grid = g.flat ? g.nb : g.rows * g.nb;
   return g;
 }
 
@@ -239,16 +297,26 @@ int fwd_impl(int64_t T_, int64_t F, const void* g, int64_t ldg, const void* u, i
   const void* p[3] = {g, h, u};
   const int64_t l[3] = {ldg, ldh, ldu};
   const Geo geo = plan<T>(T_, F, GATED ? 3 : 2, p, l);
-  const dim3 grid((unsigned)(geo.rows * geo.nb)), block(kThreads);
+  const dim3 grid((unsigned)geo.grid), block(kThreads);
+  const int64_t total = geo.rows * geo.nvr;
+  const double inv = 1.0 / (double)geo.nvr;
   const T* gp = static_cast<const T*>(g);
   const T* up = static_cast<const T*>(u);
   T* hp = static_cast<T*>(h);
-  if (geo.vec)
-    swiglu_fwd_k<T, Vec<T>::N, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, geo.nel, gp, ldg, up, ldu, hp, ldh);
-  else if (geo.ua)
-    swiglu_fwd_k<T, Vec<T>::N, ACT, GATED, true><<<grid, block, 0, st>>>(geo.nvr, geo.nb, geo.nel, gp, ldg, up, ldu, hp, ldh);
-  else
-    swiglu_fwd_k<T, 1, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, geo.nel, gp, ldg, up, ldu, hp, ldh);
+  auto go = [&](auto flat) {
+    constexpr bool FL = decltype(flat)::value;
+    if (geo.vec)
+      swiglu_fwd_k<T, Vec<T>::N, ACT, GATED, false, FL><<<grid, block, 0, st>>>(
+          total, geo.nvr, inv, geo.nb, geo.nel, gp, ldg, up, ldu, hp, ldh);
+    else if (geo.ua)
+      swiglu_fwd_k<T, Vec<T>::N, ACT, GATED, true, FL><<<grid, block, 0, st>>>(
+          total, geo.nvr, inv, geo.nb, geo.nel, gp, ldg, up, ldu, hp, ldh);
+    else
+      swiglu_fwd_k<T, 1, ACT, GATED, false, FL><<<grid, block, 0, st>>>(
+          total, geo.nvr, inv, geo.nb, geo.nel, gp, ldg, up, ldu, hp, ldh);
+  };
+  if (geo.flat) go(std::true_type{});
+  else go(std::false_type{});
   return launch_status();
 }
 
@@ -259,21 +327,28 @@ int bwd_impl(int64_t T_, int64_t F, const void* dh, int64_t lddh, const void* g,
   const void* p[5] = {dh, g, dg, u, du};
   const int64_t l[5] = {lddh, ldg, lddg, ldu, lddu};
   const Geo geo = plan<T>(T_, F, GATED ? 5 : 3, p, l);
-  const dim3 grid((unsigned)(geo.rows * geo.nb)), block(kThreads);
+  const dim3 grid((unsigned)geo.grid), block(kThreads);
+  const int64_t total = geo.rows * geo.nvr;
+  const double inv = 1.0 / (double)geo.nvr;
   const T* dhp = static_cast<const T*>(dh);
   const T* gp = static_cast<const T*>(g);
   const T* up = static_cast<const T*>(u);
   T* dgp = static_cast<T*>(dg);
   T* dup = static_cast<T*>(du);
-  if (geo.vec)
-    swiglu_bwd_k<T, Vec<T>::N, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, geo.nel, dhp, lddh, gp, ldg,
-                                                                   up, ldu, dgp, lddg, dup, lddu);
-  else if (geo.ua)
-    swiglu_bwd_k<T, Vec<T>::N, ACT, GATED, true><<<grid, block, 0, st>>>(geo.nvr, geo.nb, geo.nel, dhp, lddh, gp,
-                                                                         ldg, up, ldu, dgp, lddg, dup, lddu);
-  else
-    swiglu_bwd_k<T, 1, ACT, GATED><<<grid, block, 0, st>>>(geo.nvr, geo.nb, geo.nel, dhp, lddh, gp, ldg, up, ldu,
-                                                           dgp, lddg, dup, lddu);
+  auto go = [&](auto flat) {
+    constexpr bool FL = decltype(flat)::value;
+    if (geo.vec)
+      swiglu_bwd_k<T, Vec<T>::N, ACT, GATED, false, FL><<<grid, block, 0, st>>>(
+          total, geo.nvr, inv, geo.nb, geo.nel, dhp, lddh, gp, ldg, up, ldu, dgp, lddg, dup, lddu);
+    else if (geo.ua)
+      swiglu_bwd_k<T, Vec<T>::N, ACT, GATED, true, FL><<<grid, block, 0, st>>>(
+          total, geo.nvr, inv, geo.nb, geo.nel, dhp, lddh, gp, ldg, up, ldu, dgp, lddg, dup, lddu);
+    else
+      swiglu_bwd_k<T, 1, ACT, GATED, false, FL><<<grid, block, 0, st>>>(
+          total, geo.nvr, inv, geo.nb, geo.nel, dhp, lddh, gp, ldg, up, ldu, dgp, lddg, dup, lddu);
+  };
+  if (geo.flat) go(std::true_type{});
+  else go(std::false_type{});
   return launch_status();
 }
 

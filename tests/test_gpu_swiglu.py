@@ -53,10 +53,13 @@ def test_unaligned_widths(gpu, dtype, F):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("F", [1408, 1409, 14337])
+@pytest.mark.parametrize("F", [1408, 1409, 8192, 8200, 14336, 14337])
 def test_halves_of_fused_projection(gpu, dtype, F):
     # gate and up as the two halves of one [T, 2F] tensor (row stride 2F); with an odd F
-    # every row of the up half, and every other row of both, starts off the 16-byte grid
+    # every row of the up half, and every other row of both, starts off the 16-byte grid.
+    # Rows of one block or whole blocks (1408, 1409, bf16 8192) take blocks per row; rows
+    # of several blocks with a partial last one (bf16 8200, 14336, 14337, fp32 from 8192)
+    # one flat space of blocks that run on into the next row
     T = 77 if F < 10000 else 9
     g = torch.Generator().manual_seed(1)
     td = synth.torch_dtype(dtype)
