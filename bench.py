@@ -567,7 +567,11 @@ def config_lines(fo, synth, torch, stream, med, reps, copy_gbs, cids=(1, 2, 3, 4
                            "launch_bound": f_["launch_bound"] and b_["launch_bound"]}
         ent["fwd_bwd"] = pairs
         if graph:
-            ent["step_graph"] = graph_step(torch, stream, cases, reps, scratch, med)
+            try:
+                ent["step_graph"] = graph_step(torch, stream, cases, reps, scratch, med)
+            except Exception as e:  # a capture failure must not cost the rest of the line
+                torch.cuda.synchronize()
+                ent["step_graph"] = {"error": f"{type(e).__name__}: {e}"[:300]}
         out[f"cfg{cid}"] = ent
         del x, w, dy, y, rstd, dx, dw, rws, q, k, dq, dk, pos, g, u, dh, h, dg, du, lg, tg, dlg, xws
         torch.cuda.empty_cache()
