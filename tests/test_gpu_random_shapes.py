@@ -145,6 +145,57 @@ def test_cross_entropy(gpu, seed, dt):
     check(o["dlogits"].cpu(), r["dlogits"], dt, tag + " dlogits", single_rounding=True)
 
 
+def wide_rows(g, T, dt, scale):
+    """Rows of a large vocabulary: half the cases contiguous with V a multiple of 8 (on the
+    16-byte grid: the register-and-LDS and streaming row kernels), the others views off
+    the grid with row padding (the element-aligned paths)."""
+    if g.random() < 0.5:
+        V = 8 * int(g.integers(100000 // 8, 200000 // 8))
+        host = torch.from_numpy(g.standard_normal((T, V)) * scale).float().to(TD[dt])
+        return host.to(DEV), host, V
+    V = int(g.integers(100000, 200000))
+    dev_view, host = view(g, T, V, dt, scale)
+    return dev_view, host, V
+
+
+@pytest.mark.parametrize("seed,dt", cases(10, 8))
+def test_cross_entropy_wide_vocab(gpu, seed, dt):
+    g = np.random.default_rng(seed)
+    T = int(g.integers(1, 9))
+    z, zh, V = wide_rows(g, T, dt, 2.0)
+    zc = float(g.choice([0.0, 1e-4]))
+    t = torch.from_numpy(g.integers(0, V, T)).long()
+    t[torch.from_numpy(g.random(T) < 0.2)] = IGN
+    o = gpu.fo_xent_fwd_bwd(z, t.to(DEV), IGN, zc, 0.7)
+    torch.cuda.synchronize()
+    r = oracle.xent_fwd_bwd(zh, t, IGN, zc, 0.7)
+    tag = f"xent wide seed={seed} {dt} T={T} V={V}"
+    check_loss(o["loss"].item(), r["loss"], tag + " loss")
+    check_loss(o["z_loss"].item(), r["z_loss"], tag + " z_loss")
+    assert o["n_valid"].item() == r["n_valid"] and o["status"].item() == r["n_bad"], tag
+    check(o["dlogits"].cpu(), r["dlogits"], dt, tag + " dlogits", single_rounding=True)
+
+
+@pytest.mark.parametrize("seed,dt", cases(8, 9))
+def test_distillation_wide_vocab(gpu, seed, dt):
+    g = np.random.default_rng(seed)
+    T = int(g.integers(1, 7))
+    z, zh, V = wide_rows(g, T, dt, 3.0)
+    zt_h = torch.from_numpy(g.standard_normal((T, V)) * 2.0).float().to(TD[dt])
+    mask = torch.from_numpy((g.random(T) > 0.2).astype(np.uint8))
+    o = gpu.fo_distill_fwd_bwd(z, zt_h.to(DEV), mask.to(DEV), 1.3)
+    torch.cuda.synchronize()
+    r = oracle.distill_fwd_bwd(zh, zt_h, mask, 1.3)
+    tag = f"distill wide seed={seed} {dt} T={T} V={V}"
+    assert o["n_valid"].item() == r["n_valid"], tag
+    check_loss(o["loss"].item(), r["loss"], tag + " loss")
+    check_loss(o["kl"].item(), r["kl"], tag + " kl")
+    keep = mask.numpy() != 0
+    n = max(1, int(keep.sum()))
+    check_softmax_diff(o["dlogits"].cpu(), r["dlogits"], softmax_sum(zh, zt_h, keep, 1.3 / n),
+                       tag + " dlogits", rounded_out=dt == "bf16")
+
+
 @pytest.mark.parametrize("seed,dt", cases(24, 6))
 def test_distillation(gpu, seed, dt):
     g = np.random.default_rng(seed)
