@@ -166,3 +166,25 @@ def test_unaligned_full_size_sampled(gpu):
         rdw += oracle.rmsnorm_bwd(i["dy"][r0:r0 + 2048], i["x"][r0:r0 + 2048], w, cfg.eps)[1]
     check(dw, rdw, "f32", "dw")
 
+
+
+def test_widest_llama_rows_full_size_sampled(gpu):
+    # the widest Llama-style layer: T 8192, d 16384 (bf16), whose rows the forward spreads
+    # over 4 waves of 8 vectors and the backward over 16 waves (1024-thread workgroups,
+    # one row each, dw partials written from registers); sampled rows, dw over every row
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS[3], d=16384)
+    i = synth.rmsnorm_inputs(cfg)
+    y, rstd, dx, dw = run(gpu, i["x"], i["w"], i["dy"], cfg.eps)
+    rows = np.unique(np.concatenate([[0, 1, cfg.T - 1],
+                                     np.random.default_rng(16384).integers(0, cfg.T, 29)]))
+    x, w, dy = i["x"][rows], i["w"], i["dy"][rows]
+    ry, rr = oracle.rmsnorm_fwd(x, w, cfg.eps)
+    rdx, _ = oracle.rmsnorm_bwd(dy, x, w, cfg.eps)
+    check(y[rows], ry, cfg.dtype, "y", single_rounding=True)
+    check(rstd[rows], rr, "f32", "rstd")
+    check(dx[rows], rdx, cfg.dtype, "dx", single_rounding=True)
+    rdw = np.zeros(cfg.d)
+    for r0 in range(0, cfg.T, 1024):
+        rdw += oracle.rmsnorm_bwd(i["dy"][r0:r0 + 1024], i["x"][r0:r0 + 1024], w, cfg.eps)[1]
+    check(dw, rdw, "f32", "dw")
