@@ -628,24 +628,62 @@ def unaligned_lines(fo, synth, torch, stream, med):
                                                            ws=xws, out=xo),
          (2 * (T - n_ign) + n_ign) * V * b + 8 * T),
     ]
+    res = time_cases(torch, stream, med, cases)
+    print("# unaligned lines done", file=sys.stderr, flush=True)
+    return res
+
+
+def time_cases(torch, stream, med, cases, reps=20):
+    """Isolated medians (caches flushed before each call) of (name, fn, bytes) cases."""
     scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     res = {}
     for name, fn, byt in cases:
-        fn()
-        ts = []
-        for _ in range(20):
-            scratch.fill_(1.0)
-            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            e.record(stream)
-            e.synchronize()
-            ts.append(a.elapsed_time(e))
-        t = med(ts)
+        t = med(iso_times(torch, stream, fn, reps, scratch))
         res[name] = {"ms_isolated_median": round(t, 4), "algorithmic_MB": round(byt / 1e6, 3),
                      "GBps": round(byt / (t * 1e-3) / 1e9, 1),
                      "frac_hbm_peak": round(byt / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    print("# unaligned lines done", file=sys.stderr, flush=True)
+    del scratch
+    return res
+
+
+def layout_lines(fo, synth, torch, stream, med):
+    """Two layouts of real models at the Llama-3-8B token count, reported apart: RMSNorm
+    at the widest Llama width (d 16384, rows over several waves), and SwiGLU on the two
+    halves of one fused [T, 2F] gate/up projection (F 14336: strided rows on the 16-byte
+    grid)."""
+    import dataclasses
+    c3 = synth.CONFIGS[3]
+    cw = dataclasses.replace(c3, d=16384)
+    r = synth.rmsnorm_inputs(cw)
+    x, w, dy = (r[k].to("cuda") for k in ("x", "w", "dy"))
+    del r
+    T, d = x.shape
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    dw = torch.empty(d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(fo.fo_rmsnorm_bwd_workspace(T, d), dtype=torch.uint8, device="cuda")
+    s = synth.swiglu_inputs(c3)
+    g, u, dh = (s[k].to("cuda") for k in ("gate", "up", "dh"))
+    del s
+    F = g.shape[1]
+    gu = torch.cat([g, u], dim=1)
+    del g, u
+    g2, u2 = gu[:, :F], gu[:, F:]
+    h = torch.empty(T, F, dtype=gu.dtype, device="cuda")
+    dgu = torch.empty_like(gu)
+    b = 2
+    cases = [
+        ("rmsnorm_fwd_d16384", lambda: fo.fo_rmsnorm_fwd(x, w, cw.eps, y=y, rstd=rstd),
+         2 * T * d * b + d * b + 4 * T),
+        ("rmsnorm_bwd_d16384", lambda: fo.fo_rmsnorm_bwd(dy, x, w, rstd, cw.eps, dx=dx, dw=dw, ws=ws),
+         3 * T * d * b + d * b + 4 * T + 4 * d),
+        ("swiglu_fwd_halves_F14336", lambda: fo.fo_swiglu_fwd(g2, u2, h=h), 3 * T * F * b),
+        ("swiglu_bwd_halves_F14336", lambda: fo.fo_swiglu_bwd(dh, g2, u2, dgate=dgu[:, :F],
+                                                               dup=dgu[:, F:]), 5 * T * F * b),
+    ]
+    fo.fo_rmsnorm_fwd(x, w, cw.eps, y=y, rstd=rstd)
+    res = time_cases(torch, stream, med, cases)
+    print("# layout lines done", file=sys.stderr, flush=True)
     return res
 
 
@@ -728,6 +766,7 @@ def gpu_bench(args):
     same = (None if args.no_probes or not hbm_bytes
             else same_size_copies(fo, torch, stream, med, hbm_bytes, args.iso_reps))
     unaligned = None if args.no_probes or only else unaligned_lines(fo, synth, torch, stream, med)
+    layouts = None if args.no_probes or only else layout_lines(fo, synth, torch, stream, med)
     configs = (None if args.no_configs or only or not args.cids
                else config_lines(fo, synth, torch, stream, med, args.iso_reps,
                                  peaks["copy_GBps"] if peaks else None, args.cids,
@@ -818,6 +857,8 @@ def gpu_bench(args):
         out["next_ops"] = next_ops
     if unaligned is not None:
         out["unaligned"] = unaligned
+    if layouts is not None:
+        out["layouts"] = layouts
     if configs is not None:
         out["configs"] = configs
     # dominant op of the step: the fused linear cross-entropy (MFMA-bound)
