@@ -17,8 +17,10 @@
 // up to 8 vectors of each row in registers between the sweeps (rows of up to 2048
 // vectors whole, in 256-thread workgroups; longer rows in 512-thread workgroups, two per
 // CU), and the second sweep re-reads the rest, mostly from L2 and the Infinity Cache,
-// so HBM sees each input about once and dz once (3 T V b).  Unaligned rows
-// still move their full vectors as 16-byte accesses.
+// so HBM sees each input about once and dz once (3 T V b).  Unaligned rows take the
+// same streaming form, their full vectors still 16-byte accesses at element-aligned
+// addresses, in register-lean plans that keep two rows per CU; only rows whose pointers
+// are not element-aligned go element by element.
 #include "xent_kernels.hpp"
 
 namespace fo {
