@@ -4,11 +4,12 @@ Every kernel forms row and element offsets in 64 bits (buffer resources are buil
 row, per operand panel or per K slice, so their 32-bit ranges stay small whatever the
 tensor's size).  These cases put rows on both sides of the 2^31-element mark and at the
 very end of such tensors, and check them against the fp64 oracle; the reductions over
-every row (the cross-entropy and distillation losses, RMSNorm's dw) are checked against
+every row (the cross-entropy and distillation losses, the norms' dw and db) are checked against
 the oracle over row blocks.  One case per kernel family: cross-entropy (in place),
-distillation, RMSNorm forward and backward, SwiGLU on contiguous operands and on the
-halves of a [T, 2F] tensor, and the fused linear cross-entropy with an lm-head weight
-of more than 2^31 elements (its fp32 dW past 8 GiB)."""
+distillation, RMSNorm and LayerNorm forward and backward, RoPE forward and backward,
+SwiGLU on contiguous operands and on the halves of a [T, 2F] tensor, the plain GeLU, an
+AdamW step over a tensor of more than 2^31 elements, and the fused linear cross-entropy
+with an lm-head weight of more than 2^31 elements (its fp32 dW past 8 GiB)."""
 import dataclasses
 
 import numpy as np
@@ -202,3 +203,96 @@ def test_flce_weight_past_2g_elements(gpu):
     check_product_grad(gw, r["dweight"], r["dweight_abs"], "dweight", rounded_out=False)
     ign = np.nonzero(tn == IGN)[0]
     assert torch.all(on_host(o["dhidden"], ign).view(torch.int16) == 0)
+
+
+def test_layernorm_forward_backward(gpu):
+    # LayerNorm over the same 524800 x 4096 bf16 rows (x ~ N(1, 1)); dw and db sum every row
+    cfg = dataclasses.replace(synth.CONFIGS[3], T=524800, doc_lengths=(524800,))
+    i = synth.layernorm_inputs(cfg)
+    x, w, b, dy, eps = i["x"], i["w"], i["b"], i["dy"], cfg.eps
+    assert x.numel() > BIG
+    xg, dyg = x.to(DEV), dy.to(DEV)
+    y, mean, rstd = gpu.fo_layernorm_fwd(xg, w.to(DEV), b.to(DEV), eps)
+    dx, dw, db = gpu.fo_layernorm_bwd(dyg, xg, w.to(DEV), mean, rstd)
+    torch.cuda.synchronize()
+    del xg, dyg
+    rows = sample_rows(cfg.d, cfg.T, 4097)
+    ry, rm, rr = oracle.layernorm_fwd(x[rows], w, b, eps)
+    rdx, _, _ = oracle.layernorm_bwd(dy[rows], x[rows], w, eps)
+    check(on_host(y, rows), ry, "bf16", "y", single_rounding=True)
+    check(on_host(mean, rows), rm, "f32", "mean")
+    check(on_host(rstd, rows), rr, "f32", "rstd")
+    check(on_host(dx, rows), rdx, "bf16", "dx", single_rounding=True,
+          scale=norm_dx_terms(dy[rows], x[rows], w, eps, True))
+    parts = map_blocks(lambda r0, r1: oracle.layernorm_bwd(dy[r0:r1], x[r0:r1], w, eps)[1:],
+                       cfg.T, 4096)
+    check(dw.cpu(), sum(p[0] for p in parts), "f32", "dw")
+    check(db.cpu(), sum(p[1] for p in parts), "f32", "db")
+
+
+def test_rope_forward_backward(gpu):
+    # Llama-3-8B heads (32 query / 8 key-value heads of 128) over 524800 tokens at
+    # positions 0 .. 524799: q of 2.15e9 bf16 elements, rotated in place
+    cfg = dataclasses.replace(synth.CONFIGS[3], T=524800, doc_lengths=(524800,))
+    i = synth.rope_inputs(cfg)
+    q, k, dq, dk, pos = i["q"], i["k"], i["dq"], i["dk"], i["pos"]
+    assert q.numel() > BIG
+    pg = pos.to(DEV)
+    qg, kg = q.to(DEV), k.to(DEV)
+    gpu.fo_rope_fwd(qg, kg, pg, cfg.theta)
+    rows = sample_rows(cfg.n_q * cfg.head_dim, cfg.T, 5)
+    torch.cuda.synchronize()
+    rq, rk = oracle.rope_fwd(q[rows], k[rows], pos[rows], cfg.theta)
+    check(on_host(qg, rows), rq, "bf16", "q", single_rounding=True)
+    check(on_host(kg, rows), rk, "bf16", "k", single_rounding=True)
+    del qg, kg
+    dqg, dkg = dq.to(DEV), dk.to(DEV)
+    gpu.fo_rope_bwd(dqg, dkg, pg, cfg.theta)
+    torch.cuda.synchronize()
+    oq, ok = oracle.rope_bwd(dq[rows], dk[rows], pos[rows], cfg.theta)
+    check(on_host(dqg, rows), oq, "bf16", "dq", single_rounding=True)
+    check(on_host(dkg, rows), ok, "bf16", "dk", single_rounding=True)
+
+
+def test_plain_gelu_forward_backward(gpu):
+    # the plain (ungated) GeLU over 149800 x 14336 bf16 (2.1475e9 elements per operand)
+    cfg = dataclasses.replace(synth.CONFIGS[3], T=149800, doc_lengths=(149800,))
+    i = synth.swiglu_inputs(cfg)
+    x, dy = i["gate"], i["dh"]
+    assert x.numel() > BIG
+    xg = x.to(DEV)
+    y = gpu.fo_act_fwd("gelu", xg)
+    dx = gpu.fo_act_bwd("gelu", dy.to(DEV), xg)
+    torch.cuda.synchronize()
+    rows = sample_rows(cfg.F, cfg.T, 6)
+    check(on_host(y, rows), oracle.act_fwd(x[rows], "gelu"), "bf16", "y", single_rounding=True)
+    check(on_host(dx, rows), oracle.act_bwd(dy[rows], x[rows], "gelu"), "bf16", "dx",
+          single_rounding=True)
+
+
+def test_adamw_tensor_past_2g_elements(gpu):
+    # one fp32 tensor of 2^31 + 4099 elements (8.6 GB per array; its last chunk ragged)
+    # beside a small one, in one call; sampled elements on both sides of 2^31 and at the end
+    sizes = [BIG + 4099, 5000]
+    i = synth.adamw_inputs(sizes, 11)
+    d = {k: [t.to(DEV) for t in v] for k, v in i.items()}
+    ss, bc, df = oracle.adamw_scalars(3e-4, 0.9, 0.95, 0.1, 10)
+    f = lambda v: float(np.float32(v))  # noqa: E731  (the fp32 values the kernel receives)
+    sc = dict(step_size=f(ss), beta1=f(0.9), beta2=f(0.95), bias_correction=f(bc),
+              decay_factor=f(df), eps=f(1e-8))
+    gpu.fo_adamw_step(d["params"], d["grads"], d["exp_avgs"], d["exp_avg_sqs"],
+                      sc["step_size"], sc["beta1"], sc["beta2"], sc["bias_correction"],
+                      sc["decay_factor"], sc["eps"])
+    torch.cuda.synchronize()
+    g = np.random.default_rng(12)
+    for k, n in enumerate(sizes):
+        idx = np.unique(np.concatenate([[0, n - 1, n - 4099, min(n - 1, BIG - 1), min(n - 1, BIG)],
+                                        g.integers(0, n, 4000)]))
+        ti = torch.from_numpy(idx)
+        rp, rm, rv = oracle.adamw_step(i["params"][k][ti], i["grads"][k][ti], i["exp_avgs"][k][ti],
+                                       i["exp_avg_sqs"][k][ti], sc["step_size"], sc["beta1"],
+                                       sc["beta2"], sc["bias_correction"], sc["decay_factor"],
+                                       sc["eps"])
+        check(d["params"][k][ti.to(DEV)].cpu(), rp, "f32", f"p[{k}]")
+        check(d["exp_avgs"][k][ti.to(DEV)].cpu(), rm, "f32", f"m[{k}]")
+        check(d["exp_avg_sqs"][k][ti.to(DEV)].cpu(), rv, "f32", f"v[{k}]")
