@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from reduction_rmsnorm_fwd_amd import synth
-from tolerance import check, check_loss
+from tolerance import check, check_loss, xent_dz_terms
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -96,9 +96,12 @@ def test_swiglu_single_unit(gpu, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V", [1, 2])
-def test_xent_one_and_two_classes(gpu, dtype, V):
-    # V 1: p = 1 and lse = z, so the loss is the z-loss alone and dz = 2 c lse / N
-    T, zc = 17, 1e-3
+@pytest.mark.parametrize("zc", [1e-3, 0.0])
+def test_xent_one_and_two_classes(gpu, dtype, V, zc):
+    # V 1: p = 1 and lse = z, so the loss is the z-loss alone and dz = 2 c lse / N (with no
+    # z-loss, dz = 0: the difference of p = 1 and the one-hot, exact only to the size of
+    # those terms, hence the term-size bound)
+    T = 17
     z = randn((T, V), V, dtype, 2.0)
     t = torch.randint(0, V, (T,), generator=torch.Generator().manual_seed(V))
     t[4] = IGN
@@ -108,7 +111,8 @@ def test_xent_one_and_two_classes(gpu, dtype, V):
     assert o["n_valid"].item() == r["n_valid"] == T - 1
     check_loss(o["loss"].item(), r["loss"])
     check_loss(o["z_loss"].item(), r["z_loss"], "z_loss")
-    check(o["dlogits"].cpu(), r["dlogits"], dtype, "dlogits", single_rounding=True)
+    check(o["dlogits"].cpu(), r["dlogits"], dtype, "dlogits", single_rounding=True,
+          scale=xent_dz_terms(z, t.numpy(), t != IGN, r["lse"], zc, 1.0, r["n_valid"]))
     assert torch.all(o["dlogits"][4].cpu().float() == 0)
 
 

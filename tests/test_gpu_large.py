@@ -20,7 +20,7 @@ import oracle
 from reduction_rmsnorm_fwd_amd import synth
 from blockwise import map_blocks
 from tolerance import (check, check_bf16, check_loss, check_product_grad, check_softmax_diff,
-                       norm_dx_terms)
+                       layernorm_dw_terms, norm_dx_terms, xent_dz_terms)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -224,9 +224,14 @@ def test_layernorm_forward_backward(gpu):
     check(on_host(rstd, rows), rr, "f32", "rstd")
     check(on_host(dx, rows), rdx, "bf16", "dx", single_rounding=True,
           scale=norm_dx_terms(dy[rows], x[rows], w, eps, True))
-    parts = map_blocks(lambda r0, r1: oracle.layernorm_bwd(dy[r0:r1], x[r0:r1], w, eps)[1:],
-                       cfg.T, 4096)
-    check(dw.cpu(), sum(p[0] for p in parts), "f32", "dw")
+    def one(r0, r1):
+        _, a, c = oracle.layernorm_bwd(dy[r0:r1], x[r0:r1], w, eps)
+        return a, c, layernorm_dw_terms(dy[r0:r1], x[r0:r1], eps)
+
+    parts = map_blocks(one, cfg.T, 4096)
+    # the blocks' centring term sizes combine as their root sum of squares
+    check(dw.cpu(), sum(p[0] for p in parts), "f32", "dw",
+          scale=np.sqrt(sum(p[2] ** 2 for p in parts)))
     check(db.cpu(), sum(p[1] for p in parts), "f32", "db")
 
 

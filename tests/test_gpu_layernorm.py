@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from reduction_rmsnorm_fwd_amd import synth
-from tolerance import check, norm_dx_terms
+from tolerance import check, layernorm_dw_terms, norm_dx_terms
 from test_gpu_rmsnorm import WIDE
 
 pytestmark = pytest.mark.gpu
@@ -29,7 +29,7 @@ def compare(x, w, b, dy, eps, dt, got):
     check(rstd, rr, "f32", "rstd")
     check(dx, rdx, dt, "dx", single_rounding=True,
           scale=norm_dx_terms(dy, x, w, eps, True))
-    check(dw, rdw, "f32", "dw")
+    check(dw, rdw, "f32", "dw", scale=layernorm_dw_terms(dy, x, eps))
     check(db, rdb, "f32", "db")
 
 
@@ -135,5 +135,5 @@ def test_full_size_sampled(gpu, cid):
         _, a, c = oracle.layernorm_bwd(i["dy"][r0:r0 + 2048], i["x"][r0:r0 + 2048], w, cfg.eps)
         rdw += a
         rdb += c
-    check(dw, rdw, "f32", "dw")
+    check(dw, rdw, "f32", "dw", scale=layernorm_dw_terms(i["dy"], i["x"], cfg.eps))
     check(db, rdb, "f32", "db")

@@ -7,7 +7,7 @@ import torch
 import oracle
 from reduction_rmsnorm_fwd_amd import synth
 from blockwise import map_blocks
-from tolerance import check, check_loss
+from tolerance import check, check_loss, xent_dz_terms
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -28,7 +28,10 @@ def compare(z, t, zc, dt, o, dloss=1.0):
     assert o["n_valid"].item() == r["n_valid"]
     assert o["status"].item() == r["n_bad"]
     if o["dlogits"] is not None:
-        check(o["dlogits"], r["dlogits"], dt, "dlogits", single_rounding=True)
+        V = z.shape[1]
+        check(o["dlogits"], r["dlogits"], dt, "dlogits", single_rounding=True,
+              scale=xent_dz_terms(z, t.numpy(), (t != IGN) & (t >= 0) & (t < V), r["lse"], zc,
+                                  dloss, r["n_valid"]))
     return r
 
 

@@ -36,6 +36,19 @@ A = (|r (g - c)| + |r^3 xc mean(g xc)|) (1 + 0.1 r max|x|):
 
 For rows that do not cancel, A is |r| or close to it.
 
+LayerNorm's dw = sum_t dy xc r sums terms whose xc carries that centring error, an
+absolute error of up to 16 units of 2^-24 |dy| r max|x| per row (the same sixteen units);
+the rows round independently, so, in the root-sum-square sense in which the fp32 bound
+already takes the rounding of its sums, dw_j takes the term sizes
+A_j = 0.1 sqrt(sum_t (dy_tj r_t max_k |x_tk|)^2) (layernorm_dw_terms): negligible unless
+some row's values nearly agree, where r max|x| reaches 1/sqrt(eps).
+
+The cross-entropy gradient's target column, s (p (1 + 2 c lse) - 1) with s = dloss/N, is
+the difference of two terms of size |s| when p is near 1 (a confident row; a one-class
+row has p = 1, and with no z-loss the exact result is 0).  Its fp32 evaluation is within a
+few units of 2^-24 of those terms, not of their difference, so the single-rounding bound
+takes A = |s| (p |1 + 2 c lse| + [column = target]) (xent_dz_terms); elsewhere A = |r|.
+
 The fused linear cross-entropy's weight and hidden gradients are products dZ X of the
 logit gradient with an exact bf16 operand X (W for dH, H for dW).  The kernel's dZ
 carries two bf16 roundings (exp(z - m) stored in bf16, then dZ itself), each at most
@@ -87,6 +100,32 @@ def norm_dx_terms(dy, x, w, eps, layer):
     if layer:
         a = a * (1.0 + 0.1 * r * np.abs(x).max(axis=1, keepdims=True))
     return a
+
+
+def layernorm_dw_terms(dy, x, eps):
+    """Per column, 0.1 sqrt(sum_t (dy_tj r_t max_k |x_tk|)^2): the term sizes of LayerNorm's
+    dw that the centring of each row by an fp32 mean adds (r = 1/sqrt(var + eps))."""
+    dy, x = _np(dy), _np(x)
+    xc = x - x.mean(axis=1, keepdims=True)
+    r = 1.0 / np.sqrt((xc * xc).mean(axis=1, keepdims=True) + eps)
+    e = dy * (r * np.abs(x).max(axis=1, keepdims=True))
+    return 0.1 * np.sqrt(np.sum(e * e, axis=0))
+
+
+def xent_dz_terms(z, targets, valid, lse, z_loss, dloss, n_valid):
+    """Per element, |s| (p |1 + 2 c lse| + [column = target]) on valid rows (0 elsewhere),
+    s = dloss / n_valid, p = exp(z - lse) from the oracle's lse: the sizes of the terms the
+    cross-entropy gradient is the difference of."""
+    z, lse = _np(z), _np(lse).reshape(-1, 1)
+    tg = np.asarray(targets, dtype=np.int64)
+    valid = np.asarray(valid, dtype=bool)
+    if n_valid <= 0:
+        return np.zeros_like(z)
+    s = abs(dloss / n_valid)
+    a = s * np.exp(z - lse) * np.abs(1.0 + 2.0 * z_loss * lse)
+    rows = np.nonzero(valid)[0]
+    a[rows, tg[rows]] += s
+    return np.where(valid[:, None], a, 0.0)
 
 
 def check_bf16(g, r, name="out", single_rounding=False, scale=None):
