@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from reduction_rmsnorm_fwd_amd import synth
-from tolerance import check, check_loss, xent_dz_terms
+from tolerance import check, check_loss, layernorm_y_terms, norm_dw_terms, xent_dz_terms
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -36,7 +36,7 @@ def test_rmsnorm_tiny_rows(gpu, dtype, d):
     check(y.cpu(), ry, dtype, "y", single_rounding=True)
     check(rstd.cpu(), rr, "f32", "rstd")
     check(dx.cpu(), rdx, dtype, "dx", single_rounding=True)
-    check(dw.cpu(), rdw, "f32", "dw")
+    check(dw.cpu(), rdw, "f32", "dw", scale=norm_dw_terms(dy, x, eps, False))
     assert torch.all(y[3].cpu() == 0)
 
 
@@ -134,11 +134,11 @@ def test_layernorm_tiny_rows(gpu, dtype, d):
     torch.cuda.synchronize()
     ry, rmu, rr = oracle.layernorm_fwd(x, w, b, eps)
     rdx, rdw, rdb = oracle.layernorm_bwd(dy, x, w, eps)
-    check(y.cpu(), ry, dtype, "y", single_rounding=True)
+    check(y.cpu(), ry, dtype, "y", single_rounding=True, scale=layernorm_y_terms(x, w, b, eps))
     check(mean.cpu(), rmu, "f32", "mean")
     check(rstd.cpu(), rr, "f32", "rstd")
     check(dx.cpu(), rdx, dtype, "dx", single_rounding=True)
-    check(dw.cpu(), rdw, "f32", "dw")
+    check(dw.cpu(), rdw, "f32", "dw", scale=norm_dw_terms(dy, x, eps, True))
     check(db.cpu(), rdb, "f32", "db")
     if d == 1:
         assert torch.equal(y.cpu(), b.expand(T, 1))

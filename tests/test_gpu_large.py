@@ -20,7 +20,7 @@ import oracle
 from reduction_rmsnorm_fwd_amd import synth
 from blockwise import map_blocks
 from tolerance import (check, check_bf16, check_loss, check_product_grad, check_softmax_diff,
-                       layernorm_dw_terms, norm_dx_terms, xent_dz_terms)
+                       layernorm_y_terms, norm_dw_terms, norm_dx_terms)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -134,9 +134,14 @@ def test_rmsnorm_forward_backward(gpu):
     check(on_host(rstd, rows), rr, "f32", "rstd")
     check(on_host(dx, rows), rdx, "bf16", "dx", single_rounding=True,
           scale=norm_dx_terms(dy[rows], x[rows], w, eps, False))
-    rdw = sum(map_blocks(lambda r0, r1: oracle.rmsnorm_bwd(dy[r0:r1], x[r0:r1], w, eps)[1],
-                         cfg.T, 4096))
-    check(dw.cpu(), rdw, "f32", "dw")
+    def one(r0, r1):
+        return (oracle.rmsnorm_bwd(dy[r0:r1], x[r0:r1], w, eps)[1],
+                norm_dw_terms(dy[r0:r1], x[r0:r1], eps, False))
+
+    parts = map_blocks(one, cfg.T, 4096)
+    # the blocks' term sizes combine as their root sum of squares
+    check(dw.cpu(), sum(p[0] for p in parts), "f32", "dw",
+          scale=np.sqrt(sum(p[1] ** 2 for p in parts)))
 
 
 @pytest.mark.parametrize("halves", [False, True])
@@ -219,14 +224,15 @@ def test_layernorm_forward_backward(gpu):
     rows = sample_rows(cfg.d, cfg.T, 4097)
     ry, rm, rr = oracle.layernorm_fwd(x[rows], w, b, eps)
     rdx, _, _ = oracle.layernorm_bwd(dy[rows], x[rows], w, eps)
-    check(on_host(y, rows), ry, "bf16", "y", single_rounding=True)
+    check(on_host(y, rows), ry, "bf16", "y", single_rounding=True,
+          scale=layernorm_y_terms(x[rows], w, b, eps))
     check(on_host(mean, rows), rm, "f32", "mean")
     check(on_host(rstd, rows), rr, "f32", "rstd")
     check(on_host(dx, rows), rdx, "bf16", "dx", single_rounding=True,
           scale=norm_dx_terms(dy[rows], x[rows], w, eps, True))
     def one(r0, r1):
         _, a, c = oracle.layernorm_bwd(dy[r0:r1], x[r0:r1], w, eps)
-        return a, c, layernorm_dw_terms(dy[r0:r1], x[r0:r1], eps)
+        return a, c, norm_dw_terms(dy[r0:r1], x[r0:r1], eps, True)
 
     parts = map_blocks(one, cfg.T, 4096)
     # the blocks' centring term sizes combine as their root sum of squares

@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from reduction_rmsnorm_fwd_amd import synth
-from tolerance import check, layernorm_dw_terms, norm_dx_terms
+from tolerance import check, layernorm_y_terms, norm_dw_terms, norm_dx_terms
 from test_gpu_rmsnorm import WIDE
 
 pytestmark = pytest.mark.gpu
@@ -24,12 +24,12 @@ def compare(x, w, b, dy, eps, dt, got):
     y, mean, rstd, dx, dw, db = got
     ry, rm, rr = oracle.layernorm_fwd(x, w, b, eps)
     rdx, rdw, rdb = oracle.layernorm_bwd(dy, x, w, eps)
-    check(y, ry, dt, "y", single_rounding=True)
+    check(y, ry, dt, "y", single_rounding=True, scale=layernorm_y_terms(x, w, b, eps))
     check(mean, rm, "f32", "mean")
     check(rstd, rr, "f32", "rstd")
     check(dx, rdx, dt, "dx", single_rounding=True,
           scale=norm_dx_terms(dy, x, w, eps, True))
-    check(dw, rdw, "f32", "dw", scale=layernorm_dw_terms(dy, x, eps))
+    check(dw, rdw, "f32", "dw", scale=norm_dw_terms(dy, x, eps, True))
     check(db, rdb, "f32", "db")
 
 
@@ -125,15 +125,18 @@ def test_full_size_sampled(gpu, cid):
     x, w, b, dy = i["x"][rows], i["w"], i["b"], i["dy"][rows]
     ry, rm, rr = oracle.layernorm_fwd(x, w, b, cfg.eps)
     rdx, _, _ = oracle.layernorm_bwd(dy, x, w, cfg.eps)
-    check(y[rows], ry, cfg.dtype, "y", single_rounding=True)
+    check(y[rows], ry, cfg.dtype, "y", single_rounding=True,
+          scale=layernorm_y_terms(x, w, b, cfg.eps))
     check(mean[rows], rm, "f32", "mean")
     check(rstd[rows], rr, "f32", "rstd")
     check(dx[rows], rdx, cfg.dtype, "dx", single_rounding=True)
     # dw and db need every row: oracle over all T in row blocks
-    rdw, rdb = np.zeros(cfg.d), np.zeros(cfg.d)
+    rdw, rdb, a2 = np.zeros(cfg.d), np.zeros(cfg.d), np.zeros(cfg.d)
     for r0 in range(0, cfg.T, 2048):
-        _, a, c = oracle.layernorm_bwd(i["dy"][r0:r0 + 2048], i["x"][r0:r0 + 2048], w, cfg.eps)
+        xb, dyb = i["x"][r0:r0 + 2048], i["dy"][r0:r0 + 2048]
+        _, a, c = oracle.layernorm_bwd(dyb, xb, w, cfg.eps)
         rdw += a
         rdb += c
-    check(dw, rdw, "f32", "dw", scale=layernorm_dw_terms(i["dy"], i["x"], cfg.eps))
+        a2 += norm_dw_terms(dyb, xb, cfg.eps, True) ** 2
+    check(dw, rdw, "f32", "dw", scale=np.sqrt(a2))
     check(db, rdb, "f32", "db")

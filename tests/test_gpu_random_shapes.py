@@ -7,8 +7,8 @@ import pytest
 import torch
 
 import oracle
-from tolerance import (check, check_loss, check_softmax_diff, layernorm_dw_terms, norm_dx_terms,
-                       xent_dz_terms)
+from tolerance import (check, check_loss, check_softmax_diff, layernorm_y_terms, norm_dw_terms,
+                       norm_dx_terms, xent_dz_terms)
 from test_gpu_distill import softmax_sum
 
 pytestmark = pytest.mark.gpu
@@ -60,7 +60,7 @@ def test_rmsnorm(gpu, seed, dt):
     check(rstd.cpu(), rr, "f32", tag + " rstd")
     check(dx.cpu(), rdx, dt, tag + " dx", single_rounding=True,
           scale=norm_dx_terms(dyh, xh, wh[0], eps, False))
-    check(dw.cpu(), rdw, "f32", tag + " dw")
+    check(dw.cpu(), rdw, "f32", tag + " dw", scale=norm_dw_terms(dyh, xh, eps, False))
 
 
 @pytest.mark.parametrize("seed,dt", cases(30, 2))
@@ -77,12 +77,13 @@ def test_layernorm(gpu, seed, dt):
     ry, rm, rr = oracle.layernorm_fwd(xh, wh[0], bh[0], 1e-5)
     rdx, rdw, rdb = oracle.layernorm_bwd(dyh, xh, wh[0], 1e-5)
     tag = f"layernorm seed={seed} {dt} T={T} d={d}"
-    check(y.cpu(), ry, dt, tag + " y", single_rounding=True)
+    check(y.cpu(), ry, dt, tag + " y", single_rounding=True,
+          scale=layernorm_y_terms(xh, wh[0], bh[0], 1e-5))
     check(mean.cpu(), rm, "f32", tag + " mean")
     check(rstd.cpu(), rr, "f32", tag + " rstd")
     check(dx.cpu(), rdx, dt, tag + " dx", single_rounding=True,
           scale=norm_dx_terms(dyh, xh, wh[0], 1e-5, True))
-    check(dw.cpu(), rdw, "f32", tag + " dw", scale=layernorm_dw_terms(dyh, xh, 1e-5))
+    check(dw.cpu(), rdw, "f32", tag + " dw", scale=norm_dw_terms(dyh, xh, 1e-5, True))
     check(db.cpu(), rdb, "f32", tag + " db")
 
 

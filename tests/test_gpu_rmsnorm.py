@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from reduction_rmsnorm_fwd_amd import synth
-from tolerance import check, norm_dx_terms
+from tolerance import check, norm_dw_terms, norm_dx_terms
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -29,7 +29,7 @@ def compare(x, w, dy, eps, dt, got, rows=None):
     terms = norm_dx_terms(dy, x, w, eps, False)
     check(dx[sel], rdx[sel], dt, "dx", single_rounding=True, scale=terms[sel])
     # dw is an fp32 output: the products of exact inputs summed in fp32
-    check(dw, rdw, "f32", "dw")
+    check(dw, rdw, "f32", "dw", scale=norm_dw_terms(dy, x, eps, False))
 
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4])
@@ -140,10 +140,12 @@ def test_full_size_sampled(gpu, cid):
     check(rstd[rows], rr, "f32", "rstd")
     check(dx[rows], rdx, cfg.dtype, "dx", single_rounding=True)
     # dw needs every row: oracle over all T in row blocks
-    rdw = np.zeros(cfg.d)
+    rdw, a2 = np.zeros(cfg.d), np.zeros(cfg.d)
     for r0 in range(0, cfg.T, 2048):
-        rdw += oracle.rmsnorm_bwd(i["dy"][r0:r0 + 2048], i["x"][r0:r0 + 2048], w, cfg.eps)[1]
-    check(dw, rdw, "f32", "dw")
+        xb, dyb = i["x"][r0:r0 + 2048], i["dy"][r0:r0 + 2048]
+        rdw += oracle.rmsnorm_bwd(dyb, xb, w, cfg.eps)[1]
+        a2 += norm_dw_terms(dyb, xb, cfg.eps, False) ** 2
+    check(dw, rdw, "f32", "dw", scale=np.sqrt(a2))
 
 
 def test_unaligned_full_size_sampled(gpu):
@@ -161,10 +163,12 @@ def test_unaligned_full_size_sampled(gpu):
     check(y[rows], ry, cfg.dtype, "y", single_rounding=True)
     check(rstd[rows], rr, "f32", "rstd")
     check(dx[rows], rdx, cfg.dtype, "dx", single_rounding=True)
-    rdw = np.zeros(cfg.d)
+    rdw, a2 = np.zeros(cfg.d), np.zeros(cfg.d)
     for r0 in range(0, cfg.T, 2048):
-        rdw += oracle.rmsnorm_bwd(i["dy"][r0:r0 + 2048], i["x"][r0:r0 + 2048], w, cfg.eps)[1]
-    check(dw, rdw, "f32", "dw")
+        xb, dyb = i["x"][r0:r0 + 2048], i["dy"][r0:r0 + 2048]
+        rdw += oracle.rmsnorm_bwd(dyb, xb, w, cfg.eps)[1]
+        a2 += norm_dw_terms(dyb, xb, cfg.eps, False) ** 2
+    check(dw, rdw, "f32", "dw", scale=np.sqrt(a2))
 
 
 
@@ -184,7 +188,9 @@ def test_widest_llama_rows_full_size_sampled(gpu):
     check(y[rows], ry, cfg.dtype, "y", single_rounding=True)
     check(rstd[rows], rr, "f32", "rstd")
     check(dx[rows], rdx, cfg.dtype, "dx", single_rounding=True)
-    rdw = np.zeros(cfg.d)
+    rdw, a2 = np.zeros(cfg.d), np.zeros(cfg.d)
     for r0 in range(0, cfg.T, 1024):
-        rdw += oracle.rmsnorm_bwd(i["dy"][r0:r0 + 1024], i["x"][r0:r0 + 1024], w, cfg.eps)[1]
-    check(dw, rdw, "f32", "dw")
+        xb, dyb = i["x"][r0:r0 + 1024], i["dy"][r0:r0 + 1024]
+        rdw += oracle.rmsnorm_bwd(dyb, xb, w, cfg.eps)[1]
+        a2 += norm_dw_terms(dyb, xb, cfg.eps, False) ** 2
+    check(dw, rdw, "f32", "dw", scale=np.sqrt(a2))

@@ -36,12 +36,18 @@ A = (|r (g - c)| + |r^3 xc mean(g xc)|) (1 + 0.1 r max|x|):
 
 For rows that do not cancel, A is |r| or close to it.
 
-LayerNorm's dw = sum_t dy xc r sums terms whose xc carries that centring error, an
-absolute error of up to 16 units of 2^-24 |dy| r max|x| per row (the same sixteen units);
-the rows round independently, so, in the root-sum-square sense in which the fp32 bound
-already takes the rounding of its sums, dw_j takes the term sizes
-A_j = 0.1 sqrt(sum_t (dy_tj r_t max_k |x_tk|)^2) (layernorm_dw_terms): negligible unless
-some row's values nearly agree, where r max|x| reaches 1/sqrt(eps).
+The same centring moves LayerNorm's output y = xc r w + b by up to 16 units of
+2^-24 |w| r max|x|, and y is itself a sum that can cancel (xc r w against b), so y takes
+A = |xc r w| + |b| + 0.1 |w| r max|x| (layernorm_y_terms).
+
+The weight gradients dw_j = sum_t dy_tj xc_tj r_t (RMSNorm: xc = x) are sums over the
+rows of terms of either sign; their fp32 rounding, and their size, go with the root sum
+of squares of the terms, which a sum that cancels (a one-column row's terms are about
++-|dy|) can fall far below.  So dw takes A_j = sqrt(sum_t (dy_tj xc_tj r_t)^2) beside |r|
+and rms(r); for LayerNorm plus 0.1 sqrt(sum_t (dy_tj r_t max_k |x_tk|)^2), the centring
+error of each row's term (16 units of 2^-24 |dy| r max|x|, rows rounding independently)
+(norm_dw_terms).  For a sum that does not cancel, A_j is about |dw_j|; the centring part
+is negligible unless some row's values nearly agree, where r max|x| reaches 1/sqrt(eps).
 
 The cross-entropy gradient's target column, s (p (1 + 2 c lse) - 1) with s = dloss/N, is
 the difference of two terms of size |s| when p is near 1 (a confident row; a one-class
@@ -102,14 +108,28 @@ def norm_dx_terms(dy, x, w, eps, layer):
     return a
 
 
-def layernorm_dw_terms(dy, x, eps):
-    """Per column, 0.1 sqrt(sum_t (dy_tj r_t max_k |x_tk|)^2): the term sizes of LayerNorm's
-    dw that the centring of each row by an fp32 mean adds (r = 1/sqrt(var + eps))."""
+def norm_dw_terms(dy, x, eps, layer):
+    """Per column, sqrt(sum_t (dy_tj xc_tj r_t)^2), and for LayerNorm (layer True) plus
+    0.1 sqrt(sum_t (dy_tj r_t max_k |x_tk|)^2): the term sizes of the weight gradient of
+    RMSNorm (xc = x) or LayerNorm (xc = x - mean(x)), r = 1/sqrt(mean(xc^2) + eps)."""
     dy, x = _np(dy), _np(x)
+    xc = x - x.mean(axis=1, keepdims=True) if layer else x
+    r = 1.0 / np.sqrt((xc * xc).mean(axis=1, keepdims=True) + eps)
+    t = dy * xc * r
+    a = np.sqrt(np.sum(t * t, axis=0))
+    if layer:
+        e = dy * (r * np.abs(x).max(axis=1, keepdims=True))
+        a = a + 0.1 * np.sqrt(np.sum(e * e, axis=0))
+    return a
+
+
+def layernorm_y_terms(x, w, b, eps):
+    """Per element, |xc r w| + |b| + 0.1 |w| r max|x|: the term sizes of LayerNorm's
+    output, the last one the centring of the row by an fp32 mean."""
+    x, w, b = _np(x), _np(w).reshape(1, -1), _np(b).reshape(1, -1)
     xc = x - x.mean(axis=1, keepdims=True)
     r = 1.0 / np.sqrt((xc * xc).mean(axis=1, keepdims=True) + eps)
-    e = dy * (r * np.abs(x).max(axis=1, keepdims=True))
-    return 0.1 * np.sqrt(np.sum(e * e, axis=0))
+    return np.abs(xc * r * w) + np.abs(b) + 0.1 * np.abs(w) * r * np.abs(x).max(axis=1, keepdims=True)
 
 
 def xent_dz_terms(z, targets, valid, lse, z_loss, dloss, n_valid):
