@@ -1,6 +1,7 @@
 // SwiGLU forward and backward for gfx950, and the other MLP activations of the same
 // page: gated or plain, SiLU / GeLU / ReLU ("支持的 MLP 变体": dense MLPs gated or not,
-// with SiLU, GeLU or ReLU; GeLU taken as the exact x Phi(x)).
+// with SiLU, GeLU or ReLU; GeLU taken as the exact x Phi(x), Phi from the complementary
+// error function below).
 //
 // Definition ("Fast-LLM: 高效大语言模型训练框架", 三 技术架构: gated MLP with SiLU in the
 // Transformer Block 结构 table, and mlp gated: true / activation: silu in 训练配置示例;
@@ -34,10 +35,41 @@ __device__ __forceinline__ float sigmoid_f(float g) {
 // derivative in fp32.
 enum Act { kSilu = FO_ACT_SILU, kGelu = FO_ACT_GELU, kRelu = FO_ACT_RELU };
 
+// The complementary error function (Press et al., Numerical Recipes, section 6.2, erfcc):
+// erfc(|z|) = t exp(-z^2 + P(t)), t = 1/(1 + |z|/2), with P a Chebyshev-fitted polynomial
+// of degree 9; fractional error below 1.2e-7 for every z; erfc(-z) = 2 - erfc(z).
+__device__ __forceinline__ float erfc_poly(float t) {
+  float p = 0.17087277f;
+  p = fmaf(p, t, -0.82215223f);
+  p = fmaf(p, t, 1.48851587f);
+  p = fmaf(p, t, -1.13520398f);
+  p = fmaf(p, t, 0.27886807f);
+  p = fmaf(p, t, -0.18628806f);
+  p = fmaf(p, t, 0.09678418f);
+  p = fmaf(p, t, 0.37409196f);
+  p = fmaf(p, t, 1.00002368f);
+  return fmaf(p, t, -1.26551223f);
+}
+__device__ __forceinline__ float erfc_f(float z) {
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, az, 1.0f));
+  const float r = t * __expf(fmaf(-az, az, erfc_poly(t)));
+  return z >= 0.f ? r : 2.0f - r;
+}
+// The same, with exp(-z^2) returned beside it in e2 (the normal density's exponential,
+// shared with the derivative of GeLU).
+__device__ __forceinline__ float erfc_e2(float z, float& e2) {
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, az, 1.0f));
+  e2 = __expf(-az * az);
+  const float r = t * e2 * __expf(erfc_poly(t));
+  return z >= 0.f ? r : 2.0f - r;
+}
+
 template <int ACT>
 __device__ __forceinline__ float act_f(float x) {
   if constexpr (ACT == kSilu) return x * sigmoid_f(x);
-  else if constexpr (ACT == kGelu) return x * (0.5f * (1.0f + erff(x * 0.70710678118654752f)));
+  else if constexpr (ACT == kGelu) return x * (0.5f * erfc_f(x * -0.70710678118654752f));
   else return x > 0.f ? x : 0.f;
 }
 template <int ACT>
@@ -46,8 +78,9 @@ __device__ __forceinline__ float act_d(float x) {
     const float s = sigmoid_f(x);
     return s * fmaf(x, 1.0f - s, 1.0f);
   } else if constexpr (ACT == kGelu) {
-    return fmaf(x * 0.39894228040143268f, __expf(-0.5f * x * x),
-                0.5f * (1.0f + erff(x * 0.70710678118654752f)));
+    float e2;  // exp(-x^2 / 2)
+    const float phi = 0.5f * erfc_e2(x * -0.70710678118654752f, e2);
+    return fmaf(x * 0.39894228040143268f, e2, phi);
   } else {
     return x > 0.f ? 1.f : 0.f;
   }
