@@ -7,7 +7,7 @@ import torch
 import oracle
 from reduction_rmsnorm_fwd_amd import synth
 from blockwise import map_blocks
-from tolerance import check_bf16, check_loss, check_product_grad
+from tolerance import check_bf16, check_loss, check_product_grad, flce_target_terms
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -27,11 +27,14 @@ def compare(h, w, t, zc, o, dloss=1.0):
     check_loss(o["z_loss"].item(), r["z_loss"], "z_loss")
     assert o["n_valid"].item() == r["n_valid"]
     assert o["status"].item() == r["n_bad"]
+    tn = t.numpy()
     check_bf16(o["dhidden"], r["dhidden"], "dhidden")
-    check_product_grad(o["dhidden"], r["dhidden"], r["dhidden_abs"], "dhidden")
+    check_product_grad(o["dhidden"], r["dhidden"], r["dhidden_abs"], "dhidden",
+                       target=flce_target_terms(w, tn, r["n_valid"], dloss, np.arange(len(tn)), "dh"))
     check_bf16(o["dweight"], r["dweight"], "dweight")
     check_product_grad(o["dweight"], r["dweight"], r["dweight_abs"], "dweight",
-                       rounded_out=o["dweight"].dtype == torch.bfloat16)
+                       rounded_out=o["dweight"].dtype == torch.bfloat16,
+                       target=flce_target_terms(h, tn, r["n_valid"], dloss, np.arange(w.shape[0]), "dw"))
     ign = (t == IGN).nonzero().flatten()
     assert torch.all(o["dhidden"][ign].view(torch.int16) == 0)
     return r
@@ -154,19 +157,22 @@ def test_full_size_against_oracle(gpu):
     check_loss(o["z_loss"].item(), r["z_loss"], "z_loss")
     assert o["n_valid"].item() == r["n_valid"] and o["status"].item() == r["n_bad"] == 0
     check_bf16(o["dhidden"][dh_rows], r["dhidden"], "dhidden")
-    check_product_grad(o["dhidden"][dh_rows], r["dhidden"], r["dhidden_abs"], "dhidden")
+    bh = flce_target_terms(w, tn, r["n_valid"], 1.0, dh_rows, "dh")
+    bw = flce_target_terms(h, tn, r["n_valid"], 1.0, dw_rows, "dw")
+    check_product_grad(o["dhidden"][dh_rows], r["dhidden"], r["dhidden_abs"], "dhidden", target=bh)
     check_bf16(o["dweight"][dw_rows], r["dweight"], "dweight")
     check_product_grad(o["dweight"][dw_rows], r["dweight"], r["dweight_abs"], "dweight",
-                       rounded_out=False)
+                       rounded_out=False, target=bw)
     ign = torch.from_numpy(ign_rows)
     assert torch.all(o["dhidden"][ign].view(torch.int16) == 0)
     # another chunk size (other split-K slices of dH, more dW accumulations): the same
     # loss, and outputs within the same bounds
     o1 = run(gpu, h, w, t, cfg.z_loss, chunk=1024)
     check_loss(o1["loss"].item(), o["loss"].item(), rel=1e-6)
-    check_product_grad(o1["dhidden"][dh_rows], r["dhidden"], r["dhidden_abs"], "dhidden c1024")
+    check_product_grad(o1["dhidden"][dh_rows], r["dhidden"], r["dhidden_abs"], "dhidden c1024",
+                       target=bh)
     check_product_grad(o1["dweight"][dw_rows], r["dweight"], r["dweight_abs"], "dweight c1024",
-                       rounded_out=False)
+                       rounded_out=False, target=bw)
 
 
 def test_bad_targets_are_counted_and_ignored(gpu):

@@ -20,7 +20,8 @@ import oracle
 from reduction_rmsnorm_fwd_amd import synth
 from blockwise import map_blocks
 from tolerance import (check, check_bf16, check_loss, check_product_grad, check_softmax_diff,
-                       layernorm_y_terms, norm_dw_terms, norm_dx_terms)
+                       adamw_terms, flce_target_terms, layernorm_y_terms, norm_dw_terms,
+                       norm_dx_terms)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -203,9 +204,11 @@ def test_flce_weight_past_2g_elements(gpu):
     assert o["n_valid"].item() == r["n_valid"] and o["status"].item() == r["n_bad"] == 0
     gh, gw = on_host(o["dhidden"], dh_rows), on_host(o["dweight"], dw_rows)
     check_bf16(gh, r["dhidden"], "dhidden")
-    check_product_grad(gh, r["dhidden"], r["dhidden_abs"], "dhidden")
+    check_product_grad(gh, r["dhidden"], r["dhidden_abs"], "dhidden",
+                       target=flce_target_terms(w, tn, r["n_valid"], 1.0, dh_rows, "dh"))
     check_bf16(gw, r["dweight"], "dweight")
-    check_product_grad(gw, r["dweight"], r["dweight_abs"], "dweight", rounded_out=False)
+    check_product_grad(gw, r["dweight"], r["dweight_abs"], "dweight", rounded_out=False,
+                       target=flce_target_terms(h, tn, r["n_valid"], 1.0, dw_rows, "dw"))
     ign = np.nonzero(tn == IGN)[0]
     assert torch.all(on_host(o["dhidden"], ign).view(torch.int16) == 0)
 
@@ -304,6 +307,9 @@ def test_adamw_tensor_past_2g_elements(gpu):
                                        i["exp_avg_sqs"][k][ti], sc["step_size"], sc["beta1"],
                                        sc["beta2"], sc["bias_correction"], sc["decay_factor"],
                                        sc["eps"])
-        check(d["params"][k][ti.to(DEV)].cpu(), rp, "f32", f"p[{k}]")
-        check(d["exp_avgs"][k][ti.to(DEV)].cpu(), rm, "f32", f"m[{k}]")
+        ap, am = adamw_terms(i["params"][k][ti], i["grads"][k][ti], i["exp_avgs"][k][ti],
+                             i["exp_avg_sqs"][k][ti], sc["step_size"], sc["beta1"], sc["beta2"],
+                             sc["bias_correction"], sc["decay_factor"], sc["eps"])
+        check(d["params"][k][ti.to(DEV)].cpu(), rp, "f32", f"p[{k}]", scale=ap)
+        check(d["exp_avgs"][k][ti.to(DEV)].cpu(), rm, "f32", f"m[{k}]", scale=am)
         check(d["exp_avg_sqs"][k][ti.to(DEV)].cpu(), rv, "f32", f"v[{k}]")

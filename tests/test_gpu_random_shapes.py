@@ -223,7 +223,7 @@ def test_distillation(gpu, seed, dt):
 
 @pytest.mark.parametrize("seed", [int(s) for s in np.random.default_rng(7).integers(0, 2**31, 12)])
 def test_fused_linear_cross_entropy(gpu, seed):
-    from tolerance import check_bf16, check_product_grad
+    from tolerance import check_bf16, check_product_grad, flce_target_terms
     g = np.random.default_rng(seed)
     T = int(g.integers(1, 160))
     H = 8 * int(g.integers(1, 40))
@@ -242,9 +242,12 @@ def test_fused_linear_cross_entropy(gpu, seed):
     check_loss(o["z_loss"].item(), r["z_loss"], tag + " z_loss")
     assert o["n_valid"].item() == r["n_valid"], tag
     check_bf16(o["dhidden"].cpu(), r["dhidden"], tag + " dhidden")
-    check_product_grad(o["dhidden"].cpu(), r["dhidden"], r["dhidden_abs"], tag + " dhidden")
+    tn = t.numpy()
+    check_product_grad(o["dhidden"].cpu(), r["dhidden"], r["dhidden_abs"], tag + " dhidden",
+                       target=flce_target_terms(w, tn, r["n_valid"], 1.0, np.arange(T), "dh"))
     check_product_grad(o["dweight"].cpu(), r["dweight"], r["dweight_abs"], tag + " dweight",
-                       rounded_out=False)
+                       rounded_out=False,
+                       target=flce_target_terms(h, tn, r["n_valid"], 1.0, np.arange(V), "dw"))
 
 
 @pytest.mark.parametrize("seed,dt", cases(24, 8))
@@ -271,7 +274,7 @@ def test_mlp_activations(gpu, seed, dt):
 
 @pytest.mark.parametrize("seed", [int(s) for s in np.random.default_rng(9).integers(0, 2**31, 10)])
 def test_adamw(gpu, seed):
-    from tolerance import check_f32
+    from tolerance import adamw_terms, check_f32
     g = np.random.default_rng(seed)
     n = int(g.integers(1, 40))
     sizes = [int(g.choice([g.integers(1, 9), g.integers(9, 5000), g.integers(5000, 70000)]))
@@ -299,6 +302,9 @@ def test_adamw(gpu, seed):
                                        sc["step_size"], sc["beta1"], sc["beta2"],
                                        sc["bias_correction"], sc["decay_factor"], sc["eps"])
         tag = f"adamw seed={seed} tensor {i} of {n}, {sizes[i]} elements"
-        check_f32(dev["p"][i].cpu(), rp, tag + " p")
-        check_f32(dev["m"][i].cpu(), rm, tag + " m")
+        ap, am = adamw_terms(host["p"][i], host["g"][i], host["m"][i], host["v"][i],
+                             sc["step_size"], sc["beta1"], sc["beta2"], sc["bias_correction"],
+                             sc["decay_factor"], sc["eps"])
+        check_f32(dev["p"][i].cpu(), rp, tag + " p", scale=ap)
+        check_f32(dev["m"][i].cpu(), rm, tag + " m", scale=am)
         check_f32(dev["v"][i].cpu(), rv, tag + " v")

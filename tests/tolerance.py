@@ -66,6 +66,22 @@ values (the oracle returns it):
   product gradient:  |g - r| <= (2^-7 + 2^-9) A + [output rounded to bf16] (2^-8 + 3e-5) |r|
                                 + 1e-6 rms(A)
 
+In the fused linear cross-entropy the same target column, s (p (1 + 2 c lse) - 1), is formed
+in fp32 before dZ is rounded; its error is a few units of 2^-24 of terms of size at most
+3 |s| (for c |lse| <= 1/2), not of |dz|, and it reaches dH through the target's row of W
+and dW through the rows of H that target it.  The product bound therefore adds
+2^-20 B, B = 3 |s| |W[target]| for a dH row and the sum of 3 |s| |H[r]| over the rows r
+that target the entry for a dW row (flce_target_terms); a single-class head, where every
+dz is that column and p = 1, needs it.
+
+The AdamW moment update m' = beta1 m + (1 - beta1) g' is a sum of two terms of either
+sign, exact only to a few units of 2^-24 of |beta1 m| + |(1 - beta1) g'|, and the
+parameter update p' = decay p - step m' / (sqrt(v')/bc + eps) carries that error of m'
+beside its own two terms; a tensor of one element has no rms floor to absorb a cancelling
+one.  So m' takes A = |beta1 m| + |(1 - beta1) g'| and p' takes
+A = |decay p| + |step| A_m / (sqrt(v')/bc + eps) (adamw_terms); v' is a sum of two
+non-negative terms.
+
 The distillation gradient dz = s (q - p) (s = dloss/N) is the difference of two fp32
 softmax values, each within a few 1e-6 relative of the exact one (fp32 exponentials of
 arguments up to ~40 in size, fp32 logsumexps), then rounded once:
@@ -166,7 +182,46 @@ def check_bf16(g, r, name="out", single_rounding=False, scale=None):
     return float(np.max(d)) if d.size else 0.0
 
 
-def check_product_grad(g, r, absprod, name="out", rounded_out=True):
+def flce_target_terms(X, targets, n_valid, dloss, rows, kind):
+    """B of the fused linear cross-entropy's product bound for the requested rows:
+    kind "dh": 3 |s| |W[t_r]| for each token row r (X = W; 0 for rows that are ignored);
+    kind "dw": the sum over valid rows r with t_r = v of 3 |s| |H[r]| for each vocabulary
+    row v (X = H); s = dloss / n_valid."""
+    X = np.abs(_np(X))
+    tg = np.asarray(targets, dtype=np.int64).reshape(-1)
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    out = np.zeros((len(rows), X.shape[1]))
+    if n_valid <= 0:
+        return out
+    s3 = 3.0 * abs(dloss / n_valid)
+    if kind == "dh":
+        V = X.shape[0]
+        for i, r in enumerate(rows):
+            if 0 <= tg[r] < V:
+                out[i] = s3 * X[tg[r]]
+    else:
+        at = {int(v): i for i, v in enumerate(rows)}
+        for r in range(len(tg)):
+            i = at.get(int(tg[r]))
+            if i is not None:
+                out[i] += s3 * X[r]
+    return out
+
+
+def adamw_terms(p, g, m, v, step_size, beta1, beta2, bias_correction, decay_factor, eps,
+                grad_scale=1.0):
+    """(A_p, A_m): the term sizes of the AdamW parameter and first-moment updates."""
+    p, g, m, v = _np(p), _np(g), _np(m), _np(v)
+    gs = grad_scale * g
+    a_m = np.abs(beta1 * m) + np.abs((1.0 - beta1) * gs)
+    v1 = beta2 * v + (1.0 - beta2) * gs * gs
+    den = np.sqrt(v1) / bias_correction + eps
+    a_p = np.abs(decay_factor * p) + abs(step_size) * a_m / den
+    return a_p, a_m
+
+
+def check_product_grad(g, r, absprod, name="out", rounded_out=True, target=None):
+    """target: B of the target column's fp32 error (flce_target_terms), if any."""
     g, r, a = _np(g), _np(r), _np(absprod)
     assert g.shape == r.shape == a.shape, (name, g.shape, r.shape, a.shape)
     assert np.all(np.isfinite(g)), f"{name}: non-finite GPU output"
@@ -174,6 +229,8 @@ def check_product_grad(g, r, absprod, name="out", rounded_out=True):
         return 0.0
     d = np.abs(g - r)
     bound = (2.0 ** -7 + 2.0 ** -9) * a + 1e-6 * np.sqrt(np.mean(a * a))
+    if target is not None:
+        bound = bound + 2.0 ** -20 * _np(target)
     if rounded_out:
         bound = bound + (2.0 ** -8 + 3e-5) * np.abs(r)
     assert np.all(d <= bound), _report(name + " [product of rounded dZ]", d > bound, g, r, bound)
