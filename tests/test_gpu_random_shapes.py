@@ -2,13 +2,15 @@
 16-byte grid, padded row strides, odd head counts and vocabularies, against the fp64
 oracle under the same bounds as the targeted tests.  Every case prints its parameters in
 the assertion message."""
+import sys
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from tolerance import (check, check_loss, check_softmax_diff, layernorm_y_terms, norm_dw_terms,
-                       norm_dx_terms, xent_dz_terms)
+from tolerance import (check, check_loss, check_softmax_diff, kl_terms, layernorm_y_terms,
+                       norm_dw_terms, norm_dx_terms, xent_dz_terms)
 from test_gpu_distill import softmax_sum
 
 pytestmark = pytest.mark.gpu
@@ -29,9 +31,17 @@ def norm_width(g):
     return width(g) if g.random() < 0.75 else int(g.integers(9000, 40000))
 
 
+# operand magnitudes: None, or factors one of which scales each operand (drawn per view)
+MAGS = None
+
+
 def view(g, T, n, dt, scale=1.0, shift=0.0):
     """A [T, n] view into a larger buffer: base 0-7 elements off, row stride n + 0-9; the
-    view (on the device) and its values (on the host)."""
+    view (on the device) and its values (on the host).  With MAGS set, the values are
+    scaled by one of its factors, drawn per view."""
+    if MAGS is not None:
+        f = MAGS[int(g.integers(0, len(MAGS)))]
+        scale, shift = scale * f, shift * f
     off, pad = int(g.integers(0, 8)), int(g.integers(0, 10))
     buf = torch.from_numpy(g.standard_normal((T, n + off + pad)) * scale + shift).float().to(TD[dt])
     return buf.to(DEV)[:, off:off + n], buf[:, off:off + n].clone()
@@ -177,7 +187,9 @@ def test_cross_entropy_wide_vocab(gpu, seed, dt):
     check_loss(o["loss"].item(), r["loss"], tag + " loss")
     check_loss(o["z_loss"].item(), r["z_loss"], tag + " z_loss")
     assert o["n_valid"].item() == r["n_valid"] and o["status"].item() == r["n_bad"], tag
-    check(o["dlogits"].cpu(), r["dlogits"], dt, tag + " dlogits", single_rounding=True)
+    check(o["dlogits"].cpu(), r["dlogits"], dt, tag + " dlogits", single_rounding=True,
+          scale=xent_dz_terms(zh, t.numpy(), (t != IGN) & (t >= 0) & (t < V), r["lse"], zc,
+                                0.7, r["n_valid"]))
 
 
 @pytest.mark.parametrize("seed,dt", cases(8, 9))
@@ -193,8 +205,8 @@ def test_distillation_wide_vocab(gpu, seed, dt):
     tag = f"distill wide seed={seed} {dt} T={T} V={V}"
     assert o["n_valid"].item() == r["n_valid"], tag
     check_loss(o["loss"].item(), r["loss"], tag + " loss")
-    check_loss(o["kl"].item(), r["kl"], tag + " kl")
     keep = mask.numpy() != 0
+    check_loss(o["kl"].item(), r["kl"], tag + " kl", scale=kl_terms(zh, zt_h, keep))
     n = max(1, int(keep.sum()))
     check_softmax_diff(o["dlogits"].cpu(), r["dlogits"], softmax_sum(zh, zt_h, keep, 1.3 / n),
                        tag + " dlogits", rounded_out=dt == "bf16")
@@ -214,8 +226,8 @@ def test_distillation(gpu, seed, dt):
     tag = f"distill seed={seed} {dt} T={T} V={V}"
     assert o["n_valid"].item() == r["n_valid"], tag
     check_loss(o["loss"].item(), r["loss"], tag + " loss")
-    check_loss(o["kl"].item(), r["kl"], tag + " kl")
     keep = mask.numpy() != 0
+    check_loss(o["kl"].item(), r["kl"], tag + " kl", scale=kl_terms(zh, zth, keep))
     n = max(1, int(keep.sum()))
     check_softmax_diff(o["dlogits"].cpu(), r["dlogits"], softmax_sum(zh, zth, keep, 1.3 / n),
                        tag + " dlogits", rounded_out=dt == "bf16")
@@ -308,3 +320,13 @@ def test_adamw(gpu, seed):
         check_f32(dev["p"][i].cpu(), rp, tag + " p", scale=ap)
         check_f32(dev["m"][i].cpu(), rm, tag + " m", scale=am)
         check_f32(dev["v"][i].cpu(), rv, tag + " v")
+
+
+@pytest.mark.parametrize("seed,dt", cases(12, 21))
+def test_operands_scaled(gpu, seed, dt, monkeypatch):
+    # the same cases with every operand scaled independently by 0.01, 1, 10 or 100
+    # (logits to about +-600, norm weights to +-100): the bounds' magnitude terms
+    monkeypatch.setattr(sys.modules[__name__], "MAGS", (0.01, 1.0, 10.0, 100.0))
+    for fn in (test_rmsnorm, test_layernorm, test_swiglu, test_rope, test_cross_entropy,
+               test_distillation, test_mlp_activations):
+        fn(gpu, seed, dt)
