@@ -887,7 +887,6 @@ def cpu_baseline():
     """The fp64 oracle, as it stands, on a bounded sample of the same step: 4096 of the
     8192 tokens for every layer op and 2048 tokens for the lm head; times are scaled up
     linearly in tokens (every op is per-token) to the step's 8192 tokens."""
-    import numpy as np
     import torch
     import oracle
     from reduction_rmsnorm_fwd_amd import synth

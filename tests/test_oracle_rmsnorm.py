@@ -3,7 +3,6 @@ routine and central finite differences.  No GPU."""
 import math
 
 import numpy as np
-import pytest
 import torch
 
 import oracle
